@@ -1,0 +1,173 @@
+"""Plain fp64 CPU reference of the Mamba-2 selective state update (SSU).
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The GPU library never
+calls it, and it shares no code with the GPU library.
+
+The arithmetic lives in ``ssu_oracle.c`` (plain C, fp64, loops in the order
+sequence -> head -> row -> dstate). This module only compiles it with gcc, loads
+it with ctypes and widens operands: every fp16/bf16/fp32 value is exactly
+representable in fp64, so the widening loses nothing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "ssu_oracle.c")
+LIBRARY = os.path.join(HERE, "libssu_oracle.so")
+
+# Plain ISO C: no fused multiply-add contraction, no fast-math.
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle C source into a shared library and return its path."""
+    tmp = output + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, source, "-lm"], check=True)
+    os.replace(tmp, output)
+    return output
+
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _idx(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+def _p(a, typ):
+    return None if a is None else a.ctypes.data_as(typ)
+
+
+@dataclass
+class Result:
+    out: np.ndarray        # [rows, nheads, headdim] fp64; rows of inert sequences keep out_init
+    state: np.ndarray      # [nslots, nheads, headdim, dstate] fp64 after the call
+
+
+class Oracle:
+    """ctypes front end of one compiled oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.oracle_ssu_one_token.restype = _int
+        lib.oracle_ssu_one_token.argtypes = [
+            _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64,
+            _dp, _dp, _int, _dp, _dp, _dp, _dp, _dp, _dp, _int,
+            _ip, _ip, _i64, _int, _dp]
+        lib.oracle_ssu_packed_varlen.restype = _int
+        lib.oracle_ssu_packed_varlen.argtypes = [
+            _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+            _ip, _ip, _ip, _i64, _i64, _ip, _i64, _i64, _i64,
+            _dp, _dp, _int, _dp, _dp, _dp, _dp, _dp, _dp, _int,
+            _i64, _int, _dp]
+        self.lib = lib
+
+    @staticmethod
+    def _common(state, x, dt, A, B, C, D, z, dt_bias, out_init):
+        state = _f64(state)
+        if state.ndim != 4:
+            raise ValueError("state must be [nslots, nheads, headdim, dstate]")
+        x = _f64(x)
+        dt = _f64(dt)
+        rows = x.shape[0]
+        if dt.ndim == 3 and dt.shape[2] == 1:
+            dt = np.ascontiguousarray(dt[:, :, 0])
+        dt_per_dim = 1 if dt.ndim == 3 else 0
+        if out_init is None:
+            out = np.full(x.shape, np.nan, dtype=np.float64)
+        else:
+            out = _f64(out_init).copy()
+        return (state, x, dt, dt_per_dim, _f64(A), _f64(B), _f64(C), _f64(D),
+                _f64(z), _f64(dt_bias), out, rows)
+
+    def one_token(self, state, x, dt, A, B, C, *, D=None, z=None, dt_bias=None,
+                  dt_softplus=False, src=None, dst=None, pad_slot_id=-1,
+                  disable_state_update=False, out_init=None) -> Result:
+        """One token per sequence: row b of x/dt/B/C/z/out is sequence b."""
+        (state, x, dt, dt_per_dim, A, B, C, D, z, dt_bias, out,
+         batch) = self._common(state, x, dt, A, B, C, D, z, dt_bias, out_init)
+        nslots, H, P, N = state.shape
+        G = B.shape[1]
+        src, dst = _idx(src), _idx(dst)
+        state_out = np.empty_like(state)
+        rc = self.lib.oracle_ssu_one_token(
+            _p(state, _dp), _p(state_out, _dp), nslots, H, P, N, G, batch,
+            _p(x, _dp), _p(dt, _dp), dt_per_dim, _p(A, _dp), _p(B, _dp), _p(C, _dp),
+            _p(D, _dp), _p(z, _dp), _p(dt_bias, _dp), int(bool(dt_softplus)),
+            _p(src, _ip), _p(dst, _ip), int(pad_slot_id), int(bool(disable_state_update)),
+            _p(out, _dp))
+        if rc != 0:
+            raise ValueError("oracle_ssu_one_token rejected its arguments")
+        return Result(out, state_out)
+
+    def packed_varlen(self, state, x, dt, A, B, C, cu_seqlens, *, num_accepted=None,
+                      src_table=None, src_strides=None, dst_table=None, dst_strides=None,
+                      steps=None, D=None, z=None, dt_bias=None, dt_softplus=False,
+                      pad_slot_id=-1, disable_state_update=False, out_init=None) -> Result:
+        """Packed varlen form. A 2-D table [nseq, steps] takes strides (steps, 1)
+        unless strides are given; a flat table needs explicit strides and steps."""
+        (state, x, dt, dt_per_dim, A, B, C, D, z, dt_bias, out,
+         rows) = self._common(state, x, dt, A, B, C, D, z, dt_bias, out_init)
+        nslots, H, P, N = state.shape
+        G = B.shape[1]
+        cu = _idx(cu_seqlens)
+        nseq = cu.shape[0] - 1
+        na = _idx(num_accepted)
+
+        def table(t, strides):
+            if t is None:
+                return None, 0, 0, None
+            t = _idx(t)
+            if strides is None:
+                if t.ndim != 2:
+                    raise ValueError("a flat table needs explicit strides")
+                strides = (t.shape[1], 1)
+            width = t.shape[1] if t.ndim == 2 else None
+            return t.reshape(-1), int(strides[0]), int(strides[1]), width
+
+        st, sss, sst, sw = table(src_table, src_strides)
+        dtb, dss, dst_, dw = table(dst_table, dst_strides)
+        if steps is None:
+            steps = sw if sw is not None else (dw if dw is not None else 1)
+        state_out = np.empty_like(state)
+        rc = self.lib.oracle_ssu_packed_varlen(
+            _p(state, _dp), _p(state_out, _dp), nslots, H, P, N, G, rows, nseq,
+            _p(cu, _ip), _p(na, _ip), _p(st, _ip), sss, sst, _p(dtb, _ip), dss, dst_,
+            int(steps), _p(x, _dp), _p(dt, _dp), dt_per_dim, _p(A, _dp), _p(B, _dp),
+            _p(C, _dp), _p(D, _dp), _p(z, _dp), _p(dt_bias, _dp), int(bool(dt_softplus)),
+            int(pad_slot_id), int(bool(disable_state_update)), _p(out, _dp))
+        if rc != 0:
+            raise ValueError("oracle_ssu_packed_varlen rejected its arguments")
+        return Result(out, state_out)
+
+
+_DEFAULT: Oracle | None = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``ssu_oracle.c``; compiled on first use if absent."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            build()
+        _DEFAULT = Oracle(LIBRARY)
+    return _DEFAULT

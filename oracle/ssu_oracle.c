@@ -1,0 +1,209 @@
+/*
+ * ssu_oracle.c -- plain fp64 CPU reference of the Mamba-2 selective state update.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library; the GPU library never calls it and
+ * the two share no code. Loops run in the plain order sequence -> head -> row ->
+ * dstate, in fp64, with no blocking or reordering.
+ *
+ * What is computed, and where it comes from:
+ *
+ *  - The recurrence. The pages name the operands and their roles but do not write
+ *    the update; it is the Mamba-2 selective state space step (Dao & Gu,
+ *    "Transformers are SSMs", ICML 2024, the SSD recurrence
+ *    h_t = exp(dt_t * A) h_{t-1} + dt_t B_t x_t,  y_t = C_t . h_t + D x_t), with
+ *    the Mamba-2 block's output gate y * silu(z). Per (sequence, head h, row p):
+ *        v   = dt[h] (+ dt_bias[h]);  v = softplus(v) when requested
+ *        dA  = exp(A[h] * v)
+ *        s'  = s * dA + v * B[g, n] * x[h, p]            for every n < dstate
+ *        y   = sum_n s'[n] * C[g, n]  (+ D[h] * x[h, p])
+ *        y  *= z * sigmoid(z)                            when z is given
+ *    The output uses the post-update state; D enters before the gate; the bias is
+ *    added before the softplus and no clamp is applied.
+ *  - Operand roles, dtypes and per-head A/D/dt_bias: MATE docs, "Source code for
+ *    mate.mamba", module docstring (supported configuration) and the shape checks
+ *    of `selective_state_update`.
+ *  - Head-to-group map: heads form contiguous blocks of nheads/ngroups per group
+ *    (same page, the `head_ratio = heads // groups` specialisation key of the
+ *    prewarm entry, and the heads-divisible-by-groups check of the SSD entry).
+ *  - Slot vectors default to the identity (same page, `_slot_vector`); a missing
+ *    destination means the update is written back where it was read.
+ *  - Slot validity: a slot is used only when it differs from pad_slot_id and lies
+ *    in [0, nslots) -- the same mask the ring-tracker kernels of the vLLM
+ *    `ssu_dispatch` module apply before every load and store. An invalid read slot
+ *    makes the whole sequence inert (no state read or write, its `out` rows are
+ *    left as they are); an invalid destination only drops that state write.
+ *  - Packed form: MATE docs, `mate.mamba`, module docstring and
+ *    `_packed_selective_state_update`: rows are grouped by cu_seqlens, the
+ *    acceptance count picks the entry of the read table (entry k-1), each token
+ *    has its own destination entry, and the state chains token to token inside a
+ *    sequence without rounding in between.
+ *  - Table addressing: `_slot_table` docstring: entry = sequence * seq_stride +
+ *    position * step_stride.
+ *  - The dense [batch, steps, ...] form is the packed form with regular starts
+ *    (`selective_state_update` body), so it needs no function of its own here.
+ */
+#include "ssu_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* softplus(v) = log(1 + exp(v)), written so that neither branch overflows. */
+static double softplus(double v) {
+    if (v > 0.0) return v + log1p(exp(-v));
+    return log1p(exp(v));
+}
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+static int slot_valid(int64_t slot, int64_t pad_slot_id, int64_t nslots) {
+    return slot != pad_slot_id && slot >= 0 && slot < nslots;
+}
+
+typedef struct {
+    int64_t nslots, nheads, headdim, dstate, ngroups;
+    const double *x, *dt, *A, *B, *C, *D, *z, *dt_bias;
+    int dt_per_dim, dt_softplus;
+} problem;
+
+/*
+ * Advance one sequence's fp64 state `s` ([nheads, headdim, dstate]) by the token
+ * in packed row `row`, and write that row of `out`.
+ */
+static void step_token(const problem *pb, double *s, int64_t row, double *out) {
+    const int64_t H = pb->nheads, P = pb->headdim, N = pb->dstate;
+    const int64_t heads_per_group = H / pb->ngroups;
+    for (int64_t h = 0; h < H; ++h) {
+        const int64_t g = h / heads_per_group;
+        const double *Bg = pb->B + (row * pb->ngroups + g) * N;
+        const double *Cg = pb->C + (row * pb->ngroups + g) * N;
+        for (int64_t p = 0; p < P; ++p) {
+            const int64_t xi = (row * H + h) * P + p;
+            double v = pb->dt_per_dim ? pb->dt[xi] : pb->dt[row * H + h];
+            if (pb->dt_bias) v += pb->dt_bias[h];
+            if (pb->dt_softplus) v = softplus(v);
+            const double dA = exp(pb->A[h] * v);
+            const double xs = pb->x[xi];
+            double *sp = s + (h * P + p) * N;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                sp[n] = sp[n] * dA + v * Bg[n] * xs;
+                acc += sp[n] * Cg[n];
+            }
+            double y = acc;
+            if (pb->D) y += pb->D[h] * xs;
+            if (pb->z) {
+                const double zz = pb->z[xi];
+                y *= zz * sigmoid(zz);
+            }
+            out[xi] = y;
+        }
+    }
+}
+
+static int check_dims(const double *state_in, const double *state_out,
+                      const problem *pb) {
+    if (!state_in || !state_out || state_in == state_out) return -1;
+    if (pb->nslots <= 0 || pb->nheads <= 0 || pb->headdim <= 0 ||
+        pb->dstate <= 0 || pb->ngroups <= 0)
+        return -1;
+    if (pb->nheads % pb->ngroups != 0) return -1;
+    return 0;
+}
+
+int oracle_ssu_one_token(const double *state_in, double *state_out,
+                         int64_t nslots, int64_t nheads, int64_t headdim,
+                         int64_t dstate, int64_t ngroups, int64_t batch,
+                         const double *x, const double *dt, int dt_per_dim,
+                         const double *A, const double *B, const double *C,
+                         const double *D, const double *z,
+                         const double *dt_bias, int dt_softplus,
+                         const int64_t *src, const int64_t *dst,
+                         int64_t pad_slot_id, int disable_state_update,
+                         double *out) {
+    const problem pb = {nslots, nheads, headdim, dstate, ngroups,
+                        x,      dt,     A,       B,      C,
+                        D,      z,      dt_bias, dt_per_dim, dt_softplus};
+    if (check_dims(state_in, state_out, &pb) != 0 || batch < 0) return -1;
+    if (batch > 0 && (!x || !dt || !A || !B || !C || !out)) return -1;
+
+    const int64_t slot_elems = nheads * headdim * dstate;
+    memcpy(state_out, state_in, (size_t)(nslots * slot_elems) * sizeof(double));
+    double *s = (double *)malloc((size_t)slot_elems * sizeof(double));
+    if (!s) return -1;
+
+    for (int64_t b = 0; b < batch; ++b) {
+        const int64_t r = src ? src[b] : b;
+        const int64_t w = dst ? dst[b] : r;
+        if (!slot_valid(r, pad_slot_id, nslots)) continue;
+        memcpy(s, state_in + r * slot_elems, (size_t)slot_elems * sizeof(double));
+        step_token(&pb, s, b, out);
+        if (!disable_state_update && slot_valid(w, pad_slot_id, nslots))
+            memcpy(state_out + w * slot_elems, s, (size_t)slot_elems * sizeof(double));
+    }
+    free(s);
+    return 0;
+}
+
+int oracle_ssu_packed_varlen(
+    const double *state_in, double *state_out, int64_t nslots, int64_t nheads,
+    int64_t headdim, int64_t dstate, int64_t ngroups, int64_t rows,
+    int64_t nseq, const int64_t *cu_seqlens, const int64_t *num_accepted,
+    const int64_t *src_table, int64_t src_seq_stride, int64_t src_step_stride,
+    const int64_t *dst_table, int64_t dst_seq_stride, int64_t dst_step_stride,
+    int64_t steps, const double *x, const double *dt, int dt_per_dim,
+    const double *A, const double *B, const double *C, const double *D,
+    const double *z, const double *dt_bias, int dt_softplus,
+    int64_t pad_slot_id, int disable_state_update, double *out) {
+    const problem pb = {nslots, nheads, headdim, dstate, ngroups,
+                        x,      dt,     A,       B,      C,
+                        D,      z,      dt_bias, dt_per_dim, dt_softplus};
+    if (check_dims(state_in, state_out, &pb) != 0 || rows < 0 || nseq < 0)
+        return -1;
+    if (nseq > 0 && !cu_seqlens) return -1;
+    if (rows > 0 && (!x || !dt || !A || !B || !C || !out)) return -1;
+    /* An acceptance count indexes the read table, so it needs one. */
+    if (num_accepted && !src_table) return -1;
+    if ((src_table || dst_table) && steps <= 0) return -1;
+
+    const int64_t slot_elems = nheads * headdim * dstate;
+    memcpy(state_out, state_in, (size_t)(nslots * slot_elems) * sizeof(double));
+    double *s = (double *)malloc((size_t)slot_elems * sizeof(double));
+    if (!s) return -1;
+
+    for (int64_t b = 0; b < nseq; ++b) {
+        const int64_t begin = cu_seqlens[b], end = cu_seqlens[b + 1];
+        /* A row range outside [0, rows] or running backwards makes the sequence
+         * inert; an empty one has nothing to do. */
+        if (begin < 0 || end > rows || end <= begin) continue;
+
+        /* The read slot: entry k-1 of the sequence's read-table row. */
+        const int64_t k = num_accepted ? num_accepted[b] : 1;
+        int64_t r;
+        if (src_table) {
+            if (k < 1 || k > steps) continue;
+            r = src_table[b * src_seq_stride + (k - 1) * src_step_stride];
+        } else {
+            r = b;
+        }
+        if (!slot_valid(r, pad_slot_id, nslots)) continue;
+
+        memcpy(s, state_in + r * slot_elems, (size_t)slot_elems * sizeof(double));
+        for (int64_t t = 0; t < end - begin; ++t) {
+            step_token(&pb, s, begin + t, out);
+            if (disable_state_update) continue;
+            int64_t w;
+            if (dst_table)
+                w = t < steps ? dst_table[b * dst_seq_stride + t * dst_step_stride]
+                              : pad_slot_id;
+            else
+                w = r;
+            if (slot_valid(w, pad_slot_id, nslots))
+                memcpy(state_out + w * slot_elems, s,
+                       (size_t)slot_elems * sizeof(double));
+        }
+    }
+    free(s);
+    return 0;
+}

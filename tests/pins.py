@@ -1,0 +1,405 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself.
+
+Each `pin_*` function takes an `oracle.Oracle` and raises AssertionError when the
+oracle disagrees with the fact it checks. `test_oracle_pins.py` runs them on the
+real oracle; `test_oracle_mutants.py` runs them on builds of the oracle with a
+planted mistake and requires every such build to fail at least one pin.
+
+What pins the oracle (none of these re-types the oracle's loop):
+  - scalar cases worked by hand;
+  - softplus and sigmoid checked against numpy/scipy library routines;
+  - the matrix ("dual", semiseparable) form of the same linear recurrence from
+    the Mamba-2 SSD paper (Dao & Gu, ICML 2024), evaluated with numpy matmuls;
+  - the zero-decay closed form out_T = sum_{t<=T} dt_t (B_t . C_T) x_t;
+  - invariants: dt = 0 keeps the state, superposition, the gate factorises,
+    packed = sequential one-token steps, one-token = packed with one token per
+    sequence, pad / disable leave memory untouched, the head-to-group map;
+  - page examples stored under tests/golden/ (cu_seqlens with an empty sequence,
+    regular dense starts, flat-table addressing).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+from scipy.special import expit
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+RTOL = 1e-12
+
+
+def _close(a, b, rtol=RTOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= rtol * scale, f"{what}: max abs err {err:.3e} > {rtol:.1e} * {scale:.3e}"
+
+
+def _softplus(u):
+    return np.logaddexp(0.0, u)
+
+
+def _rand_problem(rng, *, rows, H, P, N, G, nslots, per_dim=False):
+    return dict(
+        state=rng.standard_normal((nslots, H, P, N)),
+        x=rng.standard_normal((rows, H, P)),
+        dt=rng.uniform(-3.0, 0.5, (rows, H, P) if per_dim else (rows, H)),
+        A=-np.exp(rng.uniform(0.0, 2.0, H)),
+        B=rng.standard_normal((rows, G, N)),
+        C=rng.standard_normal((rows, G, N)),
+        D=rng.standard_normal(H),
+        z=rng.standard_normal((rows, H, P)),
+        dt_bias=rng.uniform(-1.0, 1.0, H),
+    )
+
+
+# ---------------------------------------------------------------- hand-worked
+
+def pin_scalar_by_hand(orc):
+    """H = P = N = G = 1, one slot. s0 = 2, x = 3, dt = 0.5, B = 1, C = 2, D = 1.
+    A = 0: dA = 1, s' = 2 + 0.5*1*3 = 3.5, y = 3.5*2 + 1*3 = 10.
+    z = 0 gates to 0; z = 2 multiplies by 2*sigmoid(2)."""
+    one = np.ones((1, 1, 1))
+    kw = dict(x=3 * one, dt=np.array([[0.5]]), B=one, C=2 * one, D=np.array([1.0]))
+    r = orc.one_token(np.full((1, 1, 1, 1), 2.0), A=np.array([0.0]), dt_softplus=False, **kw)
+    assert r.state[0, 0, 0, 0] == 3.5, r.state
+    assert r.out[0, 0, 0] == 10.0, r.out
+    r = orc.one_token(np.full((1, 1, 1, 1), 2.0), A=np.array([0.0]), z=0 * one, **kw)
+    assert r.out[0, 0, 0] == 0.0, r.out
+    r = orc.one_token(np.full((1, 1, 1, 1), 2.0), A=np.array([0.0]), z=2 * one, **kw)
+    _close(r.out[0, 0, 0], 10.0 * 2.0 / (1.0 + math.exp(-2.0)), what="gate z=2")
+    # A = -1: dA = exp(-0.5); s' = 2 exp(-0.5) + 1.5; y = 2 s' + 3.
+    r = orc.one_token(np.full((1, 1, 1, 1), 2.0), A=np.array([-1.0]), **kw)
+    s1 = 2.0 * math.exp(-0.5) + 1.5
+    _close(r.state[0, 0, 0, 0], s1, what="decay state")
+    _close(r.out[0, 0, 0], 2.0 * s1 + 3.0, what="decay out")
+
+
+def pin_softplus_and_bias(orc):
+    """With A = 0, s0 = 0, x = B = 1, C = 1 and no D, y = softplus(dt + dt_bias):
+    the output reveals the effective step, which must be numpy's log(1 + e^u)
+    of the biased value (bias first, then softplus), or the raw biased value with
+    softplus off."""
+    u_dt = np.array([-30.0, -4.0, -0.5, 0.0, 0.3, 2.0, 19.0, 25.0, 40.0])
+    bias = np.array([0.25])
+    n = u_dt.size
+    one = np.ones((n, 1, 1))
+    for sp in (True, False):
+        r = orc.one_token(np.zeros((n, 1, 1, 1)), x=one, dt=u_dt[:, None], A=np.array([0.0]),
+                          B=one, C=one, dt_bias=bias, dt_softplus=sp)
+        want = _softplus(u_dt + bias[0]) if sp else u_dt + bias[0]
+        _close(r.out[:, 0, 0], want, rtol=1e-14, what=f"softplus={sp}")
+    # ln 2 at zero; dA = 2^A there.
+    r = orc.one_token(np.full((1, 1, 1, 1), 4.0), x=np.zeros((1, 1, 1)), dt=np.array([[0.0]]),
+                      A=np.array([-1.0]), B=np.ones((1, 1, 1)), C=np.ones((1, 1, 1)),
+                      dt_softplus=True)
+    _close(r.state[0, 0, 0, 0], 2.0, rtol=1e-15, what="2^A decay at softplus(0)")
+
+
+def pin_gate_factorises(orc):
+    """out(z) = out(no z) * z * sigmoid(z), with scipy's expit as sigmoid."""
+    rng = np.random.default_rng(11)
+    pb = _rand_problem(rng, rows=3, H=4, P=8, N=16, G=2, nslots=3)
+    z = pb.pop("z")
+    a = orc.one_token(dt_softplus=True, **pb)
+    b = orc.one_token(dt_softplus=True, z=z, **pb)
+    _close(b.out, a.out * z * expit(z), rtol=1e-13, what="gate")
+    assert np.array_equal(a.state, b.state)
+
+
+# ------------------------------------------------------------ independent forms
+
+def _ssd_matrix_form(h0, x, v, A, B, C, D):
+    """One head, L tokens: the semiseparable-matrix form of the recurrence.
+    h0 [P, N]; x [L, P]; v [L] effective steps; A, D scalars; B, C [L, N].
+    Returns y [L, P] and the states after every token [L, P, N]."""
+    L = x.shape[0]
+    S = np.cumsum(v)
+    seg = S[:, None] - S[None, :]                       # S_T - S_t
+    decay = np.where(np.tril(np.ones((L, L), dtype=bool)), np.exp(A * np.where(
+        np.tril(np.ones((L, L), dtype=bool)), seg, 0.0)), 0.0)
+    M = decay * (C @ B.T) * v[None, :]                   # [T, t]
+    y = M @ x + np.exp(A * S)[:, None] * (C @ h0.T) + D * x
+    states = np.exp(A * S)[:, None, None] * h0[None] + np.einsum(
+        "Tt,tp,tn->Tpn", decay * v[None, :], x, B)
+    return y, states
+
+
+def pin_ssd_matrix_form(orc):
+    """A packed sequence of L tokens, each writing its own slot, against the
+    matrix form of the same recurrence: every intermediate state and output."""
+    rng = np.random.default_rng(5)
+    L, H, P, N, G = 6, 4, 5, 7, 2
+    nslots = L + 1
+    pb = _rand_problem(rng, rows=L, H=H, P=P, N=N, G=G, nslots=nslots)
+    pb.pop("z")
+    table = np.array([[0, 1, 2, 3, 4, 5]])
+    dtab = np.array([[6, 1, 2, 3, 4, 5]])      # token t writes slot dtab[t]; token 0 -> slot 6
+    r = orc.packed_varlen(cu_seqlens=[0, L], src_table=table, dst_table=dtab,
+                          num_accepted=[1], dt_softplus=True, **pb)
+    v = _softplus(pb["dt"] + pb["dt_bias"][None, :])     # [L, H]
+    hpg = H // G
+    for h in range(H):
+        g = h // hpg
+        y, states = _ssd_matrix_form(pb["state"][0, h], pb["x"][:, h, :], v[:, h], pb["A"][h],
+                                     pb["B"][:, g, :], pb["C"][:, g, :], pb["D"][h])
+        _close(r.out[:, h, :], y, rtol=1e-11, what=f"y head {h}")
+        for t in range(L):
+            _close(r.state[dtab[0, t], h], states[t], rtol=1e-11, what=f"state t={t} h={h}")
+
+
+def pin_zero_decay_closed_form(orc):
+    """A = 0, D = 0, no gate, zero initial state:
+    out_T[p] = sum_{t<=T} dt_t (B_t . C_T) x_t[p], per head, with per-dim dt."""
+    rng = np.random.default_rng(7)
+    L, H, P, N, G = 5, 2, 3, 4, 1
+    pb = _rand_problem(rng, rows=L, H=H, P=P, N=N, G=G, nslots=1, per_dim=True)
+    r = orc.packed_varlen(np.zeros((1, H, P, N)), pb["x"], pb["dt"], np.zeros(H), pb["B"],
+                          pb["C"], cu_seqlens=[0, L], dt_softplus=False)
+    for h in range(H):
+        for T in range(L):
+            want = sum(pb["dt"][t, h] * (pb["B"][t, 0] @ pb["C"][T, 0]) * pb["x"][t, h]
+                       for t in range(T + 1))
+            _close(r.out[T, h], want, rtol=1e-12, what=f"T={T} h={h}")
+
+
+# ----------------------------------------------------------------- invariants
+
+def pin_zero_step_copies_state(orc):
+    """dt + dt_bias = 0 with softplus off: the state is unchanged bit for bit, so
+    src != dst copies the slot; out = C . s + D x (numpy dot)."""
+    rng = np.random.default_rng(3)
+    H, P, N, G, nslots, batch = 4, 6, 8, 2, 8, 3
+    pb = _rand_problem(rng, rows=batch, H=H, P=P, N=N, G=G, nslots=nslots)
+    pb["dt"] = -np.broadcast_to(pb["dt_bias"], (batch, H)).copy()
+    pb.pop("z")
+    src, dst = np.array([5, 0, 2]), np.array([1, 7, 3])
+    r = orc.one_token(src=src, dst=dst, dt_softplus=False, **pb)
+    for b in range(batch):
+        assert np.array_equal(r.state[dst[b]], pb["state"][src[b]]), b
+        for h in range(H):
+            g = h // (H // G)
+            want = pb["state"][src[b], h] @ pb["C"][b, g] + pb["D"][h] * pb["x"][b, h]
+            _close(r.out[b, h], want, what=f"b={b} h={h}")
+    untouched = [s for s in range(nslots) if s not in set(dst.tolist())]
+    assert np.array_equal(r.state[untouched], pb["state"][untouched])
+
+
+def pin_superposition(orc):
+    """Without a gate the step is linear in (state, x) jointly."""
+    rng = np.random.default_rng(9)
+    a = _rand_problem(rng, rows=2, H=3, P=4, N=5, G=1, nslots=2)
+    b = _rand_problem(rng, rows=2, H=3, P=4, N=5, G=1, nslots=2)
+    for k in ("dt", "A", "B", "C", "D", "dt_bias"):
+        b[k] = a[k]
+    a.pop("z"), b.pop("z")
+    ra = orc.one_token(dt_softplus=True, **a)
+    rb = orc.one_token(dt_softplus=True, **b)
+    s = dict(a, state=a["state"] + 2.5 * b["state"], x=a["x"] + 2.5 * b["x"])
+    rs = orc.one_token(dt_softplus=True, **s)
+    _close(rs.out, ra.out + 2.5 * rb.out, rtol=1e-12, what="out")
+    _close(rs.state, ra.state + 2.5 * rb.state, rtol=1e-12, what="state")
+
+
+def pin_packed_equals_sequential(orc):
+    """A packed sequence of L tokens equals L one-token calls, call t reading the
+    slot call t-1 wrote (or the read slot), bit for bit on an fp64 cache."""
+    rng = np.random.default_rng(13)
+    H, P, N, G, L = 4, 3, 8, 2, 4
+    nslots = 10
+    pb = _rand_problem(rng, rows=L, H=H, P=P, N=N, G=G, nslots=nslots)
+    table = np.array([[4, 9, 2, 7]])
+    r = orc.packed_varlen(cu_seqlens=[0, L], src_table=table, dst_table=table,
+                          num_accepted=[3], dt_softplus=True, **pb)
+    state = pb["state"].copy()
+    read = table[0, 2]
+    outs = []
+    for t in range(L):
+        step = {k: (v[t:t + 1] if k in ("x", "dt", "B", "C", "z") else v)
+                for k, v in pb.items() if k != "state"}
+        rt = orc.one_token(state, src=[read], dst=[table[0, t]], dt_softplus=True, **step)
+        state = rt.state
+        outs.append(rt.out[0])
+        read = table[0, t]
+    assert np.array_equal(r.state, state)
+    assert np.array_equal(r.out, np.stack(outs))
+
+
+def pin_one_token_equals_packed(orc):
+    """One token per sequence through the packed form (cu = arange, 1-wide tables)
+    equals the one-token form bit for bit; so does the dense [batch, steps] layout
+    with regular starts against per-sequence packed calls."""
+    rng = np.random.default_rng(17)
+    H, P, N, G, batch, nslots = 4, 5, 6, 2, 5, 9
+    pb = _rand_problem(rng, rows=batch, H=H, P=P, N=N, G=G, nslots=nslots)
+    src = np.array([3, 8, -1, 0, 6])
+    dst = np.array([1, 8, 4, 2, -1])
+    a = orc.one_token(src=src, dst=dst, dt_softplus=True, **pb)
+    b = orc.packed_varlen(cu_seqlens=np.arange(batch + 1), src_table=src[:, None],
+                          dst_table=dst[:, None], dt_softplus=True, **pb)
+    assert np.array_equal(a.state, b.state)
+    assert np.array_equal(a.out, b.out, equal_nan=True)
+
+
+def pin_pad_and_disable(orc):
+    """A pad or out-of-range read slot leaves its out rows and every slot alone; a
+    pad destination drops only the write; disabling the update changes no slot
+    and no output."""
+    rng = np.random.default_rng(19)
+    H, P, N, G, nslots = 2, 4, 4, 1, 6
+    pb = _rand_problem(rng, rows=5, H=H, P=P, N=N, G=G, nslots=nslots)
+    src = np.array([-1, 6, 2, -7, 4])          # pad, out of range, ok, out of range, ok
+    dst = np.array([0, 1, -1, 3, 5])           # .., .., pad dst, .., ok
+    r = orc.one_token(src=src, dst=dst, dt_softplus=True, **pb)
+    for b in (0, 1, 3):
+        assert np.all(np.isnan(r.out[b])), b
+    assert np.all(np.isfinite(r.out[[2, 4]]))
+    changed = [s for s in range(nslots) if not np.array_equal(r.state[s], pb["state"][s])]
+    assert changed == [5], changed
+    d = orc.one_token(src=src, dst=dst, dt_softplus=True, disable_state_update=True, **pb)
+    assert np.array_equal(d.state, pb["state"])
+    assert np.array_equal(d.out, r.out, equal_nan=True)
+    # A non-default pad id: 2 is now pad, -1 merely out of range.
+    q = orc.one_token(src=src, dst=dst, dt_softplus=True, pad_slot_id=2, **pb)
+    assert np.all(np.isnan(q.out[2])) and np.all(np.isfinite(q.out[4]))
+
+
+def pin_group_map(orc):
+    """Heads form contiguous blocks of H/G per group: each head of a G-group call
+    equals a single-head call fed its group's B/C. G = H with B/C replicated per
+    head equals G = 1."""
+    rng = np.random.default_rng(23)
+    H, P, N, G, batch = 6, 3, 5, 3, 2
+    pb = _rand_problem(rng, rows=batch, H=H, P=P, N=N, G=G, nslots=batch)
+    full = orc.one_token(dt_softplus=True, **pb)
+    for h in range(H):
+        g = h // (H // G)
+        single = orc.one_token(pb["state"][:, h:h + 1], pb["x"][:, h:h + 1], pb["dt"][:, h:h + 1],
+                               pb["A"][h:h + 1], pb["B"][:, g:g + 1], pb["C"][:, g:g + 1],
+                               D=pb["D"][h:h + 1], z=pb["z"][:, h:h + 1],
+                               dt_bias=pb["dt_bias"][h:h + 1], dt_softplus=True)
+        assert np.array_equal(full.out[:, h:h + 1], single.out), h
+        assert np.array_equal(full.state[:, h:h + 1], single.state), h
+    one = dict(pb, B=pb["B"][:, :1], C=pb["C"][:, :1])
+    rep = dict(pb, B=np.repeat(one["B"], H, axis=1), C=np.repeat(one["C"], H, axis=1))
+    a = orc.one_token(dt_softplus=True, **one)
+    b = orc.one_token(dt_softplus=True, **rep)
+    assert np.array_equal(a.out, b.out) and np.array_equal(a.state, b.state)
+
+
+def pin_accepted_count_selects_entry(orc):
+    """With a zero effective step, out = C . s_read + D x names the slot read: it
+    must be the table entry k-1; k outside [1, steps] makes the sequence inert."""
+    rng = np.random.default_rng(29)
+    H, P, N, G, nseq, steps, nslots = 2, 3, 4, 1, 4, 3, 12
+    lengths = [1, 2, 3, 2]
+    rows = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    pb = _rand_problem(rng, rows=rows, H=H, P=P, N=N, G=G, nslots=nslots)
+    pb["dt"] = -np.broadcast_to(pb["dt_bias"], (rows, H)).copy()
+    pb.pop("z")
+    table = np.arange(nseq * steps).reshape(nseq, steps)
+    k = np.array([2, 3, 0, 4])          # two valid, then 0 and steps + 1 (inert)
+    r = orc.packed_varlen(cu_seqlens=cu, num_accepted=k, src_table=table, dst_table=table,
+                          dt_softplus=False, **pb)
+    for b in range(2):
+        s = pb["state"][table[b, k[b] - 1]]
+        for t in range(lengths[b]):
+            row = cu[b] + t
+            want = s @ pb["C"][row, 0] + pb["D"][:, None] * pb["x"][row]
+            _close(r.out[row], want, what=f"b={b} t={t}")
+            assert np.array_equal(r.state[table[b, t]], s)
+    for b in (2, 3):
+        assert np.all(np.isnan(r.out[cu[b]:cu[b + 1]]))
+        for t in range(steps):
+            assert np.array_equal(r.state[table[b, t]], pb["state"][table[b, t]])
+
+
+def pin_missing_destination_writes_back(orc):
+    """Without a destination the last token's state lands in the read slot."""
+    rng = np.random.default_rng(31)
+    H, P, N, G = 2, 2, 3, 1
+    pb = _rand_problem(rng, rows=3, H=H, P=P, N=N, G=G, nslots=4)
+    table = np.array([[2, 0, 3]])
+    a = orc.packed_varlen(cu_seqlens=[0, 3], src_table=table, num_accepted=[2],
+                          dt_softplus=True, **pb)
+    b = orc.packed_varlen(cu_seqlens=[0, 3], src_table=table, num_accepted=[2],
+                          dst_table=np.array([[-1, -1, 0]]), dt_softplus=True, **pb)
+    assert np.array_equal(a.state[0], b.state[0])
+    assert np.array_equal(a.out, b.out)
+    for s in (1, 2, 3):
+        assert np.array_equal(a.state[s], pb["state"][s])
+
+
+# ------------------------------------------------------------- page examples
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def pin_page_examples(orc):
+    g = _golden("page_examples.json")
+    rng = np.random.default_rng(37)
+    H, P, N = 2, 2, 3
+
+    # Query starts [0, 0, 2]: sequence 0 is empty, sequence 1 owns rows 0 and 1.
+    ex = g["empty_sequence_starts"]
+    cu = np.array(ex["cu_seqlens"])
+    rows = int(cu[-1])
+    pb = _rand_problem(rng, rows=rows, H=H, P=P, N=N, G=1, nslots=2)
+    tab = np.array([[0, 0], [1, 1]])
+    r = orc.packed_varlen(cu_seqlens=cu, src_table=tab, dst_table=tab, dt_softplus=True, **pb)
+    for b in ex["empty_sequences"]:
+        assert np.array_equal(r.state[tab[b, 0]], pb["state"][tab[b, 0]])
+    assert list(range(int(cu[1]), int(cu[2]))) == ex["rows_of_sequence_1"]
+    seq = orc.packed_varlen(cu_seqlens=[0, rows], src_table=tab[1:], dst_table=tab[1:],
+                            dt_softplus=True, **pb)
+    assert np.array_equal(r.out, seq.out) and np.array_equal(r.state, seq.state)
+
+    # Dense [batch, steps] layout: starts 0, steps, 2 steps, ... batch * steps.
+    ex = g["dense_regular_starts"]
+    batch, steps = ex["batch"], ex["steps"]
+    starts = np.arange(0, (batch + 1) * steps, steps)
+    assert starts.tolist() == ex["cu_seqlens"]
+    pb = _rand_problem(rng, rows=batch * steps, H=H, P=P, N=N, G=1, nslots=batch * steps)
+    tab = np.arange(batch * steps).reshape(batch, steps)
+    dense = orc.packed_varlen(cu_seqlens=starts, src_table=tab, dst_table=tab,
+                              dt_softplus=True, **pb)
+    for b in range(batch):
+        sl = slice(b * steps, (b + 1) * steps)
+        one = dict(pb, x=pb["x"][sl], dt=pb["dt"][sl], B=pb["B"][sl], C=pb["C"][sl],
+                   z=pb["z"][sl])
+        rb = orc.packed_varlen(cu_seqlens=[0, steps], src_table=tab[b:b + 1],
+                               dst_table=tab[b:b + 1], dt_softplus=True, **one)
+        assert np.array_equal(dense.out[sl], rb.out)
+        for t in range(steps):
+            assert np.array_equal(dense.state[tab[b, t]], rb.state[tab[b, t]])
+
+    # Flat [rows] table, strides (1, 1): position t of sequence b is entry b + t.
+    for ex in g["flat_table_addressing"]["cases"]:
+        flat = np.array(ex["table"])
+        lengths = ex["lengths"]
+        cu = np.concatenate([[0], np.cumsum(lengths)])
+        nslots = int(flat.max()) + 1
+        pb = _rand_problem(rng, rows=int(cu[-1]), H=H, P=P, N=N, G=1, nslots=nslots)
+        r = orc.packed_varlen(cu_seqlens=cu, src_table=flat, src_strides=(1, 1),
+                              dst_table=flat, dst_strides=(1, 1), steps=ex["steps"],
+                              dt_softplus=True, **pb)
+        tab = np.full((len(lengths), ex["steps"]), -1)
+        for b, ents in enumerate(ex["entries_written"]):
+            for t, e in enumerate(ents):
+                tab[b, t] = flat[e]
+        r2 = orc.packed_varlen(cu_seqlens=cu, src_table=tab, dst_table=tab,
+                               dt_softplus=True, **pb)
+        assert np.array_equal(r.out, r2.out) and np.array_equal(r.state, r2.state)
+        written = sorted({int(flat[e]) for ents in ex["entries_written"] for e in ents})
+        changed = [s for s in range(nslots) if not np.array_equal(r.state[s], pb["state"][s])]
+        assert changed == written, (changed, written)
+
+
+ALL = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

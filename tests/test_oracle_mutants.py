@@ -1,0 +1,81 @@
+"""Plant plausible mistakes in copies of the oracle source and require the pins
+to catch each one. The mistakes are made in temporary copies on the CPU; the
+oracle in the tree is never modified. Every mutant stays in bounds (no planted
+mistake changes which memory is touched beyond the buffers' extents)."""
+import os
+import shutil
+
+import pytest
+
+import oracle
+import pins
+
+# (name, original text, planted text); the original must occur exactly once.
+MUTANTS = [
+    ("drop_dt_in_input", "sp[n] * dA + v * Bg[n] * xs", "sp[n] * dA + Bg[n] * xs"),
+    ("drop_x_in_input", "sp[n] * dA + v * Bg[n] * xs", "sp[n] * dA + v * Bg[n]"),
+    ("drop_decay", "sp[n] * dA + v * Bg[n] * xs", "sp[n] + v * Bg[n] * xs"),
+    ("decay_sign", "exp(pb->A[h] * v)", "exp(-pb->A[h] * v)"),
+    ("decay_uses_raw_dt", "exp(pb->A[h] * v)", "exp(pb->A[h] * (pb->dt_per_dim ? pb->dt[xi] : pb->dt[row * H + h]))"),
+    ("C_swapped_for_B", "acc += sp[n] * Cg[n];", "acc += sp[n] * Bg[n];"),
+    ("output_from_old_state",
+     "sp[n] = sp[n] * dA + v * Bg[n] * xs;\n                acc += sp[n] * Cg[n];",
+     "acc += sp[n] * Cg[n];\n                sp[n] = sp[n] * dA + v * Bg[n] * xs;"),
+    ("group_modulo", "const int64_t g = h / heads_per_group;", "const int64_t g = h % pb->ngroups;"),
+    ("D_without_x", "y += pb->D[h] * xs;", "y += pb->D[h];"),
+    ("gate_without_z", "y *= zz * sigmoid(zz);", "y *= sigmoid(zz);"),
+    ("gate_sign", "y *= zz * sigmoid(zz);", "y *= zz * sigmoid(-zz);"),
+    ("D_after_gate",
+     "if (pb->D) y += pb->D[h] * xs;\n            if (pb->z) {\n                const double zz = pb->z[xi];\n                y *= zz * sigmoid(zz);\n            }",
+     "if (pb->z) {\n                const double zz = pb->z[xi];\n                y *= zz * sigmoid(zz);\n            }\n            if (pb->D) y += pb->D[h] * xs;"),
+    ("softplus_branch", "if (v > 0.0) return v + log1p(exp(-v));", "if (v > 0.0) return log1p(exp(-v));"),
+    ("bias_after_softplus",
+     "if (pb->dt_bias) v += pb->dt_bias[h];\n            if (pb->dt_softplus) v = softplus(v);",
+     "if (pb->dt_softplus) v = softplus(v);\n            if (pb->dt_bias) v += pb->dt_bias[h];"),
+    ("bias_ignored", "if (pb->dt_bias) v += pb->dt_bias[h];", ""),
+    ("dt_head_index", "pb->dt[row * H + h]", "pb->dt[h]"),
+    ("accepted_entry_k", "(k - 1) * src_step_stride", "(k - 1 + (k < steps)) * src_step_stride"),
+    ("accepted_ignored", "r = src_table[b * src_seq_stride + (k - 1) * src_step_stride];",
+     "r = src_table[b * src_seq_stride];"),
+    ("pad_read_not_skipped", "if (!slot_valid(r, pad_slot_id, nslots)) continue;\n        memcpy(s, state_in + r * slot_elems, (size_t)slot_elems * sizeof(double));\n        step_token(&pb, s, b, out);",
+     "memcpy(s, state_in + (slot_valid(r, pad_slot_id, nslots) ? r : 0) * slot_elems, (size_t)slot_elems * sizeof(double));\n        step_token(&pb, s, b, out);"),
+    ("disable_ignored_one_token", "if (!disable_state_update && slot_valid(w, pad_slot_id, nslots))",
+     "if (slot_valid(w, pad_slot_id, nslots))"),
+    ("dst_ignored_one_token", "const int64_t w = dst ? dst[b] : r;", "const int64_t w = r;"),
+    ("packed_writes_read_slot", "w = t < steps ? dst_table[b * dst_seq_stride + t * dst_step_stride]\n                              : pad_slot_id;",
+     "w = r;"),
+    ("packed_state_not_chained",
+     "step_token(&pb, s, begin + t, out);",
+     "memcpy(s, state_in + r * slot_elems, (size_t)slot_elems * sizeof(double));\n            step_token(&pb, s, begin + t, out);"),
+    ("valid_upper_bound", "slot >= 0 && slot < nslots", "slot >= 0 && slot <= nslots - 2"),
+    ("pad_id_ignored", "return slot != pad_slot_id && slot >= 0", "return slot >= 0"),
+]
+
+
+@pytest.fixture(scope="module")
+def workdir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+def _build_mutant(workdir, name, old, new):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"{name}: anchor occurs {src.count(old)} times"
+    d = workdir / name
+    d.mkdir()
+    shutil.copy(os.path.join(oracle.HERE, "ssu_oracle.h"), d / "ssu_oracle.h")
+    (d / "ssu_oracle.c").write_text(src.replace(old, new))
+    lib = str(d / f"libssu_oracle_{name}.so")
+    oracle.build(str(d / "ssu_oracle.c"), lib)
+    return oracle.Oracle(lib)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(workdir, name, old, new):
+    mutant = _build_mutant(workdir, name, old, new)
+    caught = []
+    for pin in pins.ALL:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name!r}"
