@@ -1,0 +1,238 @@
+"""Mamba-2 selective state update (SSU) decode step on AMD Instinct MI355X.
+
+Python binding of the C ABI in include/ssu.h. It checks tensor shapes, dtypes,
+devices and contiguity, then hands raw device pointers and torch's current HIP
+stream to the library; every step of the update runs in the library's gfx950
+kernel. There is no fallback: without the built library every call raises.
+
+    ssu_one_token(state, x, dt, A, B, C, out=None, *, D, z, dt_bias, dt_softplus,
+                  state_batch_indices, dst_state_batch_indices, pad_slot_id,
+                  disable_state_update)
+    ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens, out=None, *,
+                      num_accepted_tokens, state_batch_indices,
+                      dst_state_batch_indices, ...)
+
+Operand shapes follow the MATE documentation page "Source code for mate.mamba"
+(`selective_state_update`): state [slots, heads, dim, dstate]; x, z, out
+[rows, heads, dim]; dt [rows, heads], [rows, heads, 1] or [rows, heads, dim]
+in fp32; B, C [rows, groups, dstate] in x's dtype; A, D, dt_bias fp32 [heads].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import _abi
+
+__all__ = ["ssu_one_token", "ssu_packed_varlen", "library_path", "library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBRARY = os.path.join(_HERE, "_lib", "libssu_amd.so")
+_lib = None
+_lock = threading.Lock()
+
+_STATE_DTYPES = {torch.float32: _abi.SSU_F32, torch.float16: _abi.SSU_F16,
+                 torch.bfloat16: _abi.SSU_BF16}
+_IO_DTYPES = _STATE_DTYPES
+_INDEX_DTYPES = {torch.int32: _abi.SSU_I32, torch.int64: _abi.SSU_I64}
+
+
+def library_path() -> str:
+    return _LIBRARY
+
+
+def library() -> ctypes.CDLL:
+    """The loaded HIP library (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                _lib = _abi.load(_LIBRARY)
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_device(device, **tensors):
+    if device.type != "cuda":
+        raise ValueError(f"state must be on a GPU, got {device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, state is on {device}")
+
+
+def _contig(name, t):
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _per_head(name, t, heads):
+    if t is None:
+        return None
+    if t.dtype != torch.float32:
+        raise NotImplementedError(f"{name} must be fp32, got {t.dtype}")
+    if t.dim() != 1 or t.shape[0] != heads:
+        raise NotImplementedError(
+            f"{name} must hold one value per head ([{heads}]), got {tuple(t.shape)}")
+    _contig(name, t)
+    return t
+
+
+def _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus, pad_slot_id,
+              disable_state_update, heads_per_block):
+    if state.dim() != 4:
+        raise ValueError(f"state must be [slots, heads, dim, dstate], got {tuple(state.shape)}")
+    if state.dtype not in _STATE_DTYPES:
+        raise NotImplementedError(f"state dtype {state.dtype} is not supported")
+    slots, heads, dim, dstate = state.shape
+    if x.dim() != 3 or x.shape[1:] != (heads, dim):
+        raise ValueError(f"x must be [rows, {heads}, {dim}], got {tuple(x.shape)}")
+    rows = x.shape[0]
+    if x.dtype not in _IO_DTYPES:
+        raise NotImplementedError(f"x dtype {x.dtype} is not supported")
+    if dt.dtype != torch.float32:
+        raise NotImplementedError(f"dt must be fp32, got {dt.dtype}")
+    if dt.shape == (rows, heads) or dt.shape == (rows, heads, 1):
+        dt_per_dim = 0
+    elif dt.shape == (rows, heads, dim):
+        dt_per_dim = 1
+    else:
+        raise ValueError(f"dt must be [rows, heads], [rows, heads, 1] or [rows, heads, dim]; "
+                         f"got {tuple(dt.shape)}")
+    if B.dim() != 3 or B.shape[0] != rows or B.shape[2] != dstate or C.shape != B.shape:
+        raise ValueError(f"B/C must be [rows, groups, {dstate}]; got B={tuple(B.shape)}, "
+                         f"C={tuple(C.shape)}")
+    if B.dtype != x.dtype or C.dtype != x.dtype:
+        raise ValueError("B and C must share the x dtype")
+    groups = B.shape[1]
+    if groups < 1 or heads % groups:
+        raise ValueError(f"heads ({heads}) must be a multiple of groups ({groups})")
+    if z is not None and (z.shape != x.shape or z.dtype != x.dtype):
+        raise ValueError("z must match x in shape and dtype")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError(f"out must be {x.dtype} {tuple(x.shape)}, got {out.dtype} {tuple(out.shape)}")
+    A = _per_head("A", A, heads)
+    D = _per_head("D", D, heads)
+    dt_bias = _per_head("dt_bias", dt_bias, heads)
+    _check_device(state.device, x=x, dt=dt, A=A, B=B, C=C, out=out, D=D, z=z, dt_bias=dt_bias)
+    for name, t in (("state", state), ("x", x), ("dt", dt), ("B", B), ("C", C), ("z", z),
+                    ("out", out)):
+        _contig(name, t)
+    op = _abi.Operands(
+        state=_ptr(state), state_dtype=_STATE_DTYPES[state.dtype], nslots=slots, nheads=heads,
+        headdim=dim, dstate=dstate, ngroups=groups,
+        x=_ptr(x), B=_ptr(B), C=_ptr(C), z=_ptr(z), out=_ptr(out), io_dtype=_IO_DTYPES[x.dtype],
+        dt=_ptr(dt), dt_per_dim=dt_per_dim, A=_ptr(A), D=_ptr(D), dt_bias=_ptr(dt_bias),
+        dt_softplus=int(bool(dt_softplus)), pad_slot_id=int(pad_slot_id),
+        disable_state_update=int(bool(disable_state_update)),
+        heads_per_block=int(heads_per_block))
+    return op, out, rows
+
+
+def _index(name, t, device):
+    if t is None:
+        return None, 0
+    if t.dtype not in _INDEX_DTYPES:
+        raise ValueError(f"{name} must be int32 or int64, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, state is on {device}")
+    _contig(name, t)
+    return t, _INDEX_DTYPES[t.dtype]
+
+
+def _stream(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _raise(lib, rc, entry):
+    msg = lib.ssu_last_error().decode(errors="replace")
+    if rc == _abi.SSU_ERR_INVALID_ARGUMENT:
+        raise ValueError(f"{entry}: {msg}")
+    if rc == _abi.SSU_ERR_UNSUPPORTED:
+        raise NotImplementedError(f"{entry}: {msg}")
+    raise RuntimeError(f"{entry}: {msg} (status {rc})")
+
+
+def ssu_one_token(state, x, dt, A, B, C, out=None, *, D=None, z=None, dt_bias=None,
+                  dt_softplus=False, state_batch_indices=None, dst_state_batch_indices=None,
+                  pad_slot_id=-1, disable_state_update=False, heads_per_block=0, stream=None):
+    """One decode token per sequence (row b is sequence b). Updates `state` in place
+    at the destination slots and returns `out` [batch, heads, dim]."""
+    lib = library()
+    op, out, batch = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
+                               pad_slot_id, disable_state_update, heads_per_block)
+    src, src_dt = _index("state_batch_indices", state_batch_indices, state.device)
+    dst, dst_dt = _index("dst_state_batch_indices", dst_state_batch_indices, state.device)
+    for name, t in (("state_batch_indices", src), ("dst_state_batch_indices", dst)):
+        if t is not None and (t.dim() != 1 or t.shape[0] != batch):
+            raise ValueError(f"{name} must be [{batch}], got {tuple(t.shape)}")
+    args = _abi.OneTokenArgs(struct_size=ctypes.sizeof(_abi.OneTokenArgs), op=op, batch=batch,
+                             src_slots=_ptr(src), src_dtype=src_dt,
+                             dst_slots=_ptr(dst), dst_dtype=dst_dt)
+    rc = lib.ssu_one_token(ctypes.byref(args), _stream(state.device, stream))
+    if rc != _abi.SSU_OK:
+        _raise(lib, rc, "ssu_one_token")
+    return out
+
+
+def _table(name, t, device, nseq):
+    """(tensor, dtype code, seq stride, step stride, width) of a slot table."""
+    t, code = _index(name, t, device)
+    if t is None:
+        return None, 0, 0, 0, None
+    if t.dim() == 2:
+        if t.shape[0] != nseq:
+            raise ValueError(f"{name} must have one row per sequence ({nseq}), got {t.shape[0]}")
+        return t, code, t.stride(0), t.stride(1), t.shape[1]
+    if t.dim() == 1:
+        # Flat per-row form: sequence b's position t is entry b + t.
+        return t, code, 1, 1, t.shape[0] - nseq + 1
+    raise ValueError(f"{name} must be [sequences, steps] or flat [rows], got {tuple(t.shape)}")
+
+
+def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens, out=None, *, num_accepted_tokens=None,
+                      state_batch_indices=None, dst_state_batch_indices=None, D=None, z=None,
+                      dt_bias=None, dt_softplus=False, pad_slot_id=-1,
+                      disable_state_update=False, steps=None, heads_per_block=0, stream=None):
+    """Packed variable-length multi-token update. Sequence b owns rows
+    [cu_seqlens[b], cu_seqlens[b+1]). Returns `out` [rows, heads, dim]."""
+    lib = library()
+    op, out, rows = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
+                              pad_slot_id, disable_state_update, heads_per_block)
+    cu, meta = _index("cu_seqlens", cu_seqlens, state.device)
+    if cu is None or cu.dim() != 1 or cu.shape[0] < 1:
+        raise ValueError("cu_seqlens must be a 1-D [sequences + 1] tensor")
+    nseq = cu.shape[0] - 1
+    na, na_dt = _index("num_accepted_tokens", num_accepted_tokens, state.device)
+    if na is not None:
+        if na.dim() != 1 or na.shape[0] != nseq:
+            raise ValueError(f"num_accepted_tokens must be [{nseq}], got {tuple(na.shape)}")
+        if na.dtype != cu.dtype:
+            raise ValueError("cu_seqlens and num_accepted_tokens must share a dtype")
+    src, src_dt, sss, sst, sw = _table("state_batch_indices", state_batch_indices,
+                                       state.device, nseq)
+    dst, dst_dt, dss, dst_st, dw = _table("dst_state_batch_indices", dst_state_batch_indices,
+                                          state.device, nseq)
+    if steps is None:
+        widths = [w for w in (sw, dw) if w is not None]
+        if len(set(widths)) > 1:
+            raise ValueError(f"read and write tables have different widths {widths}; pass steps")
+        steps = widths[0] if widths else 1
+    args = _abi.PackedArgs(
+        struct_size=ctypes.sizeof(_abi.PackedArgs), op=op, rows=rows, nseq=nseq,
+        cu_seqlens=_ptr(cu), num_accepted=_ptr(na), meta_dtype=meta,
+        src_table=_ptr(src), src_dtype=src_dt, src_seq_stride=sss, src_step_stride=sst,
+        dst_table=_ptr(dst), dst_dtype=dst_dt, dst_seq_stride=dss, dst_step_stride=dst_st,
+        steps=int(steps))
+    rc = lib.ssu_packed_varlen(ctypes.byref(args), _stream(state.device, stream))
+    if rc != _abi.SSU_OK:
+        _raise(lib, rc, "ssu_packed_varlen")
+    return out

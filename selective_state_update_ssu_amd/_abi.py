@@ -1,0 +1,67 @@
+"""ctypes mirror of include/ssu.h. Field order and types must match the header;
+the library checks `struct_size` on every call, so a stale mirror fails loudly."""
+import ctypes
+import os
+
+from ctypes import c_int32, c_int64, c_uint32, c_void_p, c_char_p
+
+SSU_F32, SSU_F16, SSU_BF16 = 0, 1, 2
+SSU_I32, SSU_I64 = 0, 1
+SSU_OK, SSU_ERR_INVALID_ARGUMENT, SSU_ERR_UNSUPPORTED, SSU_ERR_LAUNCH = 0, 1, 2, 3
+ABI_VERSION = 1
+
+EXPORTS = ("ssu_one_token", "ssu_packed_varlen", "ssu_last_error", "ssu_version")
+
+
+class Operands(ctypes.Structure):
+    _fields_ = [
+        ("state", c_void_p), ("state_dtype", c_int32),
+        ("nslots", c_int64), ("nheads", c_int64), ("headdim", c_int64),
+        ("dstate", c_int64), ("ngroups", c_int64),
+        ("x", c_void_p), ("B", c_void_p), ("C", c_void_p), ("z", c_void_p),
+        ("out", c_void_p), ("io_dtype", c_int32),
+        ("dt", c_void_p), ("dt_per_dim", c_int32),
+        ("A", c_void_p), ("D", c_void_p), ("dt_bias", c_void_p), ("dt_softplus", c_int32),
+        ("pad_slot_id", c_int64), ("disable_state_update", c_int32),
+        ("heads_per_block", c_int32),
+    ]
+
+
+class OneTokenArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_uint32), ("op", Operands), ("batch", c_int64),
+        ("src_slots", c_void_p), ("src_dtype", c_int32),
+        ("dst_slots", c_void_p), ("dst_dtype", c_int32),
+    ]
+
+
+class PackedArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_uint32), ("op", Operands), ("rows", c_int64), ("nseq", c_int64),
+        ("cu_seqlens", c_void_p), ("num_accepted", c_void_p), ("meta_dtype", c_int32),
+        ("src_table", c_void_p), ("src_dtype", c_int32),
+        ("src_seq_stride", c_int64), ("src_step_stride", c_int64),
+        ("dst_table", c_void_p), ("dst_dtype", c_int32),
+        ("dst_seq_stride", c_int64), ("dst_step_stride", c_int64),
+        ("steps", c_int64),
+    ]
+
+
+def load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: the SSU entry points run only on the HIP library. "
+            "Build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(or selective_state_update_ssu_amd/build.py).")
+    lib = ctypes.CDLL(path)
+    lib.ssu_one_token.restype = c_int32
+    lib.ssu_one_token.argtypes = [ctypes.POINTER(OneTokenArgs), c_void_p]
+    lib.ssu_packed_varlen.restype = c_int32
+    lib.ssu_packed_varlen.argtypes = [ctypes.POINTER(PackedArgs), c_void_p]
+    lib.ssu_last_error.restype = c_char_p
+    lib.ssu_last_error.argtypes = []
+    lib.ssu_version.restype = c_int32
+    lib.ssu_version.argtypes = []
+    if lib.ssu_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} reports ABI {lib.ssu_version()}, expected {ABI_VERSION}")
+    return lib

@@ -1,0 +1,197 @@
+"""The C ABI on the host: the library loads, exports what include/ssu.h declares,
+agrees with the ctypes mirror on struct layout, and rejects every invalid call
+before touching the GPU. No call here reaches a kernel launch: each one either
+fails validation or has no work, so these run on machines without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from selective_state_update_ssu_amd import _abi
+import selective_state_update_ssu_amd as ssu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssu.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssu.library_path()):
+        from selective_state_update_ssu_amd import build
+        build.build()
+    return ssu.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssu_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert names == sorted(_abi.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", ssu.library_path()],
+                        capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", nm, re.M))
+    assert set(names) <= exported
+
+
+def test_version(lib):
+    assert lib.ssu_version() == _abi.ABI_VERSION
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """Offsets and sizes of every field, as the C compiler lays them out."""
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssu.h"', "int main(void){"]
+    checks = []
+    for cname, cls in (("ssu_operands", _abi.Operands), ("ssu_one_token_args", _abi.OneTokenArgs),
+                       ("ssu_packed_args", _abi.PackedArgs)):
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        checks.append((cname, ctypes.sizeof(cls)))
+        for fname, _ in cls._fields_:
+            lines.append(f'printf("{cname}.{fname} %zu\\n", offsetof({cname}, {fname}));')
+            checks.append((f"{cname}.{fname}", getattr(cls, fname).offset))
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", f"-I{os.path.dirname(HEADER)}", str(src), "-o", str(exe)],
+                   check=True)
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True,
+                                                         text=True, check=True).stdout.split("\n") if l)
+    for key, want in checks:
+        assert int(got[key]) == want, (key, got[key], want)
+
+
+# Fake, never-dereferenced device addresses, 256-byte aligned and far apart.
+def addr(i):
+    return 0x7F0000000000 + i * (1 << 32)
+
+
+def good_operands(**kw):
+    op = _abi.Operands(
+        state=addr(1), state_dtype=_abi.SSU_F32, nslots=8, nheads=8, headdim=64, dstate=128,
+        ngroups=2, x=addr(2), B=addr(3), C=addr(4), z=addr(5), out=addr(6),
+        io_dtype=_abi.SSU_BF16, dt=addr(7), dt_per_dim=0, A=addr(8), D=addr(9),
+        dt_bias=addr(10), dt_softplus=1, pad_slot_id=-1, disable_state_update=0,
+        heads_per_block=0)
+    for k, v in kw.items():
+        setattr(op, k, v)
+    return op
+
+
+def one_token(lib, batch=4, **kw):
+    a = _abi.OneTokenArgs(struct_size=ctypes.sizeof(_abi.OneTokenArgs), op=good_operands(),
+                          batch=batch, src_slots=addr(11), src_dtype=_abi.SSU_I32,
+                          dst_slots=None, dst_dtype=0)
+    for k, v in kw.items():
+        if hasattr(a.op, k) and k not in ("struct_size",):
+            setattr(a.op, k, v)
+        else:
+            setattr(a, k, v)
+    rc = lib.ssu_one_token(ctypes.byref(a), None)
+    return rc, lib.ssu_last_error().decode()
+
+
+def packed(lib, **kw):
+    a = _abi.PackedArgs(struct_size=ctypes.sizeof(_abi.PackedArgs), op=good_operands(),
+                        rows=10, nseq=4, cu_seqlens=addr(12), num_accepted=addr(13),
+                        meta_dtype=_abi.SSU_I32, src_table=addr(14), src_dtype=_abi.SSU_I32,
+                        src_seq_stride=4, src_step_stride=1, dst_table=addr(15),
+                        dst_dtype=_abi.SSU_I32, dst_seq_stride=4, dst_step_stride=1, steps=4)
+    for k, v in kw.items():
+        if hasattr(a.op, k):
+            setattr(a.op, k, v)
+        else:
+            setattr(a, k, v)
+    rc = lib.ssu_packed_varlen(ctypes.byref(a), None)
+    return rc, lib.ssu_last_error().decode()
+
+
+INV, UNS = _abi.SSU_ERR_INVALID_ARGUMENT, _abi.SSU_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ngroups=0), INV, "positive"),
+    (dict(ngroups=3), INV, "multiple of ngroups"),
+    (dict(nslots=0), INV, "positive"),
+    (dict(dstate=48), UNS, "dstate 48"),
+    (dict(state_dtype=7), INV, "state_dtype"),
+    (dict(io_dtype=-1), INV, "io_dtype"),
+    (dict(dt_per_dim=2), INV, "dt_per_dim"),
+    (dict(heads_per_block=3), INV, "heads_per_block"),
+    (dict(heads_per_block=8), INV, "heads_per_block"),
+    (dict(nheads=12, ngroups=4, heads_per_block=2), INV, "divide"),
+    (dict(dstate=256, heads_per_block=4), UNS, "exceeds"),
+    (dict(state=0), INV, "state must not be NULL"),
+    (dict(x=0), INV, "x must not be NULL"),
+    (dict(A=0), INV, "A must not be NULL"),
+    (dict(out=0), INV, "out must not be NULL"),
+    (dict(state=addr(1) + 8), UNS, "16-byte aligned"),
+    (dict(x=addr(2) + 1), INV, "aligned"),
+    (dict(out=addr(2) + 64), INV, "out overlaps x"),
+    (dict(out=addr(1) + 4096), INV, "out overlaps state"),
+    (dict(batch=-1), INV, "batch"),
+    (dict(src_dtype=5), INV, "src_dtype"),
+    (dict(struct_size=8), INV, "struct_size"),
+])
+def test_one_token_rejects(lib, kw, code, needle):
+    rc, msg = one_token(lib, **kw)
+    assert rc == code, (rc, msg)
+    assert needle in msg, msg
+
+
+def test_one_token_empty_batch_is_ok(lib):
+    rc, msg = one_token(lib, batch=0)
+    assert rc == _abi.SSU_OK and msg == ""
+
+
+def test_null_args(lib):
+    assert lib.ssu_one_token(None, None) == INV
+    assert lib.ssu_packed_varlen(None, None) == INV
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(src_table=None), INV, "src_table is required"),
+    (dict(cu_seqlens=None), INV, "cu_seqlens must not be NULL"),
+    (dict(meta_dtype=3), INV, "meta_dtype"),
+    (dict(steps=0), INV, "steps"),
+    (dict(src_seq_stride=-1), INV, "strides"),
+    (dict(dst_step_stride=-2), INV, "strides"),
+    (dict(rows=-1), INV, "rows"),
+    (dict(dst_dtype=9), INV, "dst_dtype"),
+    (dict(dstate=100), UNS, "dstate 100"),
+    (dict(struct_size=4), INV, "struct_size"),
+])
+def test_packed_rejects(lib, kw, code, needle):
+    rc, msg = packed(lib, **kw)
+    assert rc == code, (rc, msg)
+    assert needle in msg, msg
+
+
+def test_packed_without_work_is_ok(lib):
+    assert packed(lib, nseq=0)[0] == _abi.SSU_OK
+    assert packed(lib, rows=0)[0] == _abi.SSU_OK
+
+
+def test_binding_refuses_host_tensors():
+    """No CPU fallback: host tensors are rejected before any launch."""
+    import torch
+    from selective_state_update_ssu_amd import workloads as wl
+    w = wl.tiny("cpu")
+    with pytest.raises(ValueError, match="GPU"):
+        ssu.ssu_one_token(w.state, w.x, w.dt, w.A, w.B, w.C, D=w.D, dt_bias=w.dt_bias)
+
+
+def test_product_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "selective_state_update_ssu_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), os.path.join(dirpath, f)

@@ -1,0 +1,256 @@
+"""GPU path against the fp64 oracle, through the C ABI (via the binding).
+
+Small shapes (spanning several workgroups and a ragged row block) are compared
+in full; the named decode workloads run at their real sizes, in the launch
+configuration the benchmark times, with exact placement checked over the whole
+call and a sample of sequences compared against the oracle."""
+import itertools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import harness as hz
+from selective_state_update_ssu_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def compare_full(name, w, out, after, before, ref):
+    hz.check_placement(name, w, out, after, before)
+    e_out = hz.check_out_rows(name + " out", out, np.arange(w.rows), ref.out)
+    e_st = hz.check_slots(name + " state", after, before, list(range(w.state.shape[0])), ref.state)
+    return e_out, e_st
+
+
+# ----------------------------------------------------------- named workloads
+
+def _sample(w, untouched, k=6):
+    n = w.rows if w.mode == "one_token" else w.cu_seqlens.shape[0] - 1
+    picks = [0, n - 1, n // 2, n // 3]
+    if w.mode == "one_token":
+        inert = [b for b in range(n) if untouched[b]]
+    else:
+        cu = hz.i64(w.cu_seqlens)
+        inert = [b for b in range(n) if cu[b + 1] > cu[b] and untouched[cu[b]]]
+    picks += inert[:2]
+    rng = np.random.default_rng(0)
+    picks += rng.choice(n, size=min(k, n), replace=False).tolist()
+    return sorted(set(int(p) for p in picks))
+
+
+@pytest.mark.parametrize("name", list(wl.NAMED))
+def test_named_workload(name):
+    _say(f"[parity] named workload {name}")
+    w = wl.NAMED[name](DEV)
+    out, after, before = hz.gpu_run(w)
+    written, untouched = hz.check_placement(name, w, out, after, before)
+    seqs = _sample(w, untouched)
+    rows, out_ref, slots, state_ref = hz.oracle_sample(w, seqs, before)
+    e_out = hz.check_out_rows(name + " out", out, rows, out_ref)
+    e_st = hz.check_slots(name + " state", after, before, slots, state_ref)
+    _say(f"[parity] {name}: {len(written)} slots written, {int(untouched.sum())} rows inert, "
+         f"sampled {len(seqs)} sequences, worst out {e_out:.3g}, worst state {e_st:.3g}")
+
+
+@pytest.mark.parametrize("hpb", [2, 4])
+def test_heads_per_block_bit_identical(hpb):
+    """The launch shape changes nothing in the arithmetic of an element."""
+    w = wl.nemotron_h(DEV)
+    o1, s1, _ = hz.gpu_run(w, heads_per_block=1)
+    o2, s2, _ = hz.gpu_run(w, heads_per_block=hpb)
+    assert torch.equal(hz.bits(o1), hz.bits(o2))
+    assert torch.equal(hz.bits(s1), hz.bits(s2))
+
+
+# ---------------------------------------------------------------- small grid
+
+def _small_cases():
+    cases = []
+    for st, io in itertools.product(["f32", "f16", "bf16"], ["f32", "f16", "bf16"]):
+        cases.append(dict(state_dtype=st, io=io, N=128, P=64, H=8, G=2))
+    for N in (16, 32, 64, 256):
+        for st in ("f32", "bf16"):
+            cases.append(dict(state_dtype=st, io="bf16", N=N, P=64, H=4, G=1))
+    for P in (80, 40, 128, 1):
+        cases.append(dict(state_dtype="f32", io="bf16", N=64, P=P, H=4, G=2))
+    cases.append(dict(state_dtype="f16", io="f16", N=16, P=72, H=6, G=3))
+    # launch shapes, optional operands and index dtypes
+    cases.append(dict(state_dtype="f32", io="bf16", N=128, P=64, H=8, G=1, hpb=4))
+    cases.append(dict(state_dtype="bf16", io="f16", N=128, P=64, H=8, G=2, hpb=2))
+    cases.append(dict(state_dtype="f32", io="f16", N=256, P=64, H=4, G=1, hpb=2))
+    cases.append(dict(state_dtype="f32", io="bf16", N=64, P=64, H=4, G=1, with_z=False,
+                      with_D=False, with_bias=False))
+    cases.append(dict(state_dtype="f32", io="bf16", N=64, P=64, H=4, G=1, dt_per_dim=True))
+    cases.append(dict(state_dtype="f32", io="bf16", N=64, P=64, H=4, G=1, softplus=False))
+    cases.append(dict(state_dtype="f16", io="bf16", N=32, P=64, H=4, G=4, index_dtype="i64",
+                      pad_fraction=0.3, dst_mode="distinct"))
+    cases.append(dict(state_dtype="f32", io="f32", N=16, P=64, H=8, G=1, dst_mode="none"))
+    cases.append(dict(state_dtype="f32", io="bf16", N=128, P=64, H=4, G=1, identity=True))
+    cases.append(dict(state_dtype="f32", io="bf16", N=128, P=64, H=4, G=1, disable=True,
+                      pad_fraction=0.2))
+    return cases
+
+
+def _case_id(c):
+    return "-".join(f"{k}{v}" for k, v in c.items())
+
+
+def _one_token_case(c, seed):
+    c = dict(c)
+    batch = c.pop("batch", 7)
+    hpb = c.pop("hpb", 0)
+    disable = c.pop("disable", False)
+    softplus = c.pop("softplus", True)
+    nslots = c.pop("nslots", 2 * batch + 3)
+    w = wl.one_token("small", seed, batch=batch, nslots=nslots, device=DEV, **c)
+    w.dt_softplus = softplus
+    w.disable_state_update = disable
+    return w, hpb
+
+
+@pytest.mark.parametrize("case", _small_cases(), ids=_case_id)
+def test_one_token_small(case):
+    w, hpb = _one_token_case(case, seed=101)
+    out, after, before = hz.gpu_run(w, heads_per_block=hpb)
+    ref = hz.oracle_full(w)
+    compare_full(_case_id(case), w, out, after, before, ref)
+
+
+@pytest.mark.parametrize("case", [
+    dict(state_dtype="f32", io="bf16", N=128, P=64, H=8, G=2),
+    dict(state_dtype="bf16", io="f16", N=64, P=80, H=4, G=1),
+    dict(state_dtype="f16", io="f32", N=16, P=64, H=4, G=2, hpb=2),
+    dict(state_dtype="f32", io="bf16", N=256, P=64, H=4, G=1, meta_dtype="i64", index_dtype="i64"),
+    dict(state_dtype="f32", io="bf16", N=128, P=64, H=4, G=1, accepted=False),
+    dict(state_dtype="f32", io="bf16", N=64, P=64, H=4, G=1, with_z=False, dt_per_dim=True),
+    dict(state_dtype="f32", io="bf16", N=128, P=64, H=4, G=1, disable=True),
+], ids=_case_id)
+def test_packed_small(case):
+    c = dict(case)
+    hpb = c.pop("hpb", 0)
+    disable = c.pop("disable", False)
+    lengths = [1, 4, 0, 2, 3, 1, 0, 4, 2]          # includes empty sequences
+    w = wl.packed("small", 202, nseq=len(lengths), max_len=4, nslots=48, device=DEV,
+                  lengths=lengths, pad_fraction=0.12, **c)
+    w.disable_state_update = disable
+    out, after, before = hz.gpu_run(w, heads_per_block=hpb)
+    ref = hz.oracle_full(w)
+    compare_full(_case_id(case), w, out, after, before, ref)
+
+
+# ------------------------------------------------------------- packed edges
+
+def _packed_base(seed=303, **kw):
+    lengths = [3, 1, 2, 4]
+    return wl.packed("edge", seed, nseq=4, max_len=4, H=4, P=64, N=64, G=1, nslots=24,
+                     device=DEV, lengths=lengths, **kw)
+
+
+def test_packed_write_back_without_destination_table():
+    w = _packed_base()
+    w.dst_table = None
+    out, after, before = hz.gpu_run(w)
+    compare_full("no-dst", w, out, after, before, hz.oracle_full(w))
+
+
+def test_packed_identity_read_without_tables():
+    w = _packed_base(accepted=False)
+    w.src_table = None
+    w.dst_table = None
+    out, after, before = hz.gpu_run(w)
+    compare_full("no-tables", w, out, after, before, hz.oracle_full(w))
+
+
+def test_packed_steps_narrower_than_sequences():
+    """Positions at or beyond the table width are not written; counts beyond it
+    make the sequence inert."""
+    w = _packed_base()
+    w.src_table = w.src_table[:, :2].contiguous()
+    w.dst_table = w.src_table
+    w.num_accepted = torch.tensor([1, 1, 2, 3], dtype=w.cu_seqlens.dtype, device=DEV)
+    out, after, before = hz.gpu_run(w)
+    compare_full("narrow", w, out, after, before, hz.oracle_full(w))
+
+
+def test_packed_flat_tables():
+    """A flat per-row table addresses entry b + t (strides 1, 1)."""
+    lengths = [1, 1, 1, 1, 1]
+    w = wl.packed("flat", 404, nseq=5, max_len=1, H=4, P=64, N=32, G=1, nslots=16,
+                  device=DEV, lengths=lengths, accepted=False)
+    flat = torch.tensor([7, 3, 12, -1, 5], dtype=torch.int32, device=DEV)
+    w.src_table = flat
+    w.dst_table = flat
+    w.meta["steps"] = 1
+    w.meta["table_strides"] = (1, 1)
+    out, after, before = hz.gpu_run(w)
+    compare_full("flat", w, out, after, before, hz.oracle_full(w))
+
+
+def test_packed_bad_row_ranges_are_inert():
+    w = _packed_base()
+    cu = w.cu_seqlens.clone()
+    cu[2] = cu[3] + 1           # sequence 1 runs backwards, sequence 2 starts late
+    cu[4] = w.rows + 5          # sequence 3 runs past the rows
+    w.cu_seqlens = cu
+    out, after, before = hz.gpu_run(w)
+    compare_full("bad-ranges", w, out, after, before, hz.oracle_full(w))
+
+
+def test_packed_bad_counts_and_slots_are_inert():
+    w = _packed_base()
+    w.num_accepted = torch.tensor([0, 5, -3, 2], dtype=w.cu_seqlens.dtype, device=DEV)
+    t = w.src_table.clone()
+    t[3, 1] = 10_000            # out-of-range read slot for sequence 3
+    t[0, 2] = -1                # pad destination at position 2 of sequence 0
+    w.src_table = t
+    w.dst_table = t
+    out, after, before = hz.gpu_run(w)
+    compare_full("bad-counts", w, out, after, before, hz.oracle_full(w))
+
+
+# ------------------------------------------------------------ exact copies
+
+@pytest.mark.parametrize("state_dtype", ["f32", "f16", "bf16"])
+def test_zero_step_copies_slot_bit_exact(state_dtype):
+    """dt + dt_bias = 0 with softplus off: the destination slot is a bit-exact
+    copy of the source slot, in every storage dtype."""
+    w = wl.one_token("copy", 505, batch=6, H=4, P=64, N=128, G=1, nslots=16, device=DEV,
+                     state_dtype=state_dtype, io="bf16", dst_mode="distinct")
+    w.dt_softplus = False
+    w.dt = -w.dt_bias.expand(w.rows, -1).contiguous()
+    out, after, before = hz.gpu_run(w)
+    for b in range(w.rows):
+        s, d = int(w.src[b]), int(w.dst[b])
+        assert torch.equal(hz.bits(after[d]), hz.bits(before[s])), b
+    compare_full("copy", w, out, after, before, hz.oracle_full(w))
+
+
+# ------------------------------------------------------------- empty calls
+
+def test_empty_calls_launch_nothing():
+    import selective_state_update_ssu_amd as ssu
+    w = wl.one_token("empty", 606, batch=0, H=4, P=64, N=64, G=1, nslots=4, device=DEV)
+    out = ssu.ssu_one_token(w.state, w.x, w.dt, w.A, w.B, w.C, D=w.D, z=w.z,
+                            dt_bias=w.dt_bias, state_batch_indices=w.src)
+    assert out.shape[0] == 0
+    p = _packed_base()
+    cu = torch.zeros(3, dtype=torch.int32, device=DEV)
+    x = p.x[:0]
+    ssu.ssu_packed_varlen(p.state, x, p.dt[:0], p.A, p.B[:0], p.C[:0], cu, D=p.D,
+                          z=p.z[:0], dt_bias=p.dt_bias)
+    torch.cuda.synchronize()
