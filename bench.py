@@ -38,8 +38,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--mode", choices=["full", "kernel", "copy"], default="full")
+    ap.add_argument("--mode", choices=["full", "kernel", "copy", "summarize"], default="full")
+    ap.add_argument("--prof-dir", help="summarize: directory holding the rocprofv3 passes")
+    ap.add_argument("--prof-cmd", default="", help="summarize: the command lines that made them")
     ap.add_argument("--heads-per-block", type=int, default=0)
+    ap.add_argument("--loads-per-lane", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
@@ -48,7 +51,7 @@ def parse():
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "selective_state_update_ssu_amd", "csrc", "*")))
+    files = sorted(glob.glob(os.path.join(ROOT, "selective_state_update_ssu_amd", "csrc", "ssu_*")))
     files.append(os.path.join(ROOT, "include", "ssu.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -117,14 +120,17 @@ def accounting(w):
     row_bytes = H * P * iosz * (2 + (w.z is not None)) + 2 * G * N * iosz + 4 * H * dt_cols
     state_read = live_seqs * slot_head
     state_write = writes * slot_head
+    out_bytes = live_rows * H * P * iosz
     total = state_read + state_write + live_rows * row_bytes + index_bytes + 3 * 4 * H
+    write = state_write + out_bytes
     return dict(live_rows=live_rows, live_seqs=live_seqs, state_writes=writes,
-                state_read_bytes=state_read, state_write_bytes=state_write, bytes=total)
+                state_read_bytes=state_read, state_write_bytes=state_write,
+                read_bytes=total - write, write_bytes=write, bytes=total)
 
 
 # ---------------------------------------------------------------------- timing
 
-def make_call(w, hpb):
+def make_call(w, hpb, lpl=0, order=0):
     import torch
     import selective_state_update_ssu_amd as ssu
 
@@ -132,7 +138,7 @@ def make_call(w, hpb):
     out = torch.empty_like(w.x)
     common = dict(D=w.D, z=w.z, dt_bias=w.dt_bias, dt_softplus=w.dt_softplus,
                   pad_slot_id=w.pad_slot_id, disable_state_update=w.disable_state_update,
-                  heads_per_block=hpb)
+                  heads_per_block=hpb, loads_per_lane=lpl, tile_order=order)
     if w.mode == "one_token":
         return lambda: ssu.ssu_one_token(state, w.x, w.dt, w.A, w.B, w.C, out,
                                          state_batch_indices=w.src,
@@ -163,15 +169,39 @@ def time_calls(call, steps, warmup):
     return (t1 - t0) * 1e3 / steps, start.elapsed_time(end) / steps
 
 
-def copy_bandwidth(steps=50, nbytes=2 << 30):
-    """A plain device copy of `nbytes` (torch's copy kernel): GB/s counting the
-    bytes read plus the bytes written."""
+def stream_library():
+    import ctypes
+    from selective_state_update_ssu_amd import build
+    lib = ctypes.CDLL(build.STREAM_LIBRARY)
+    lib.ssu_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_void_p]
+    lib.ssu_stream_write.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.ssu_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    return lib
+
+
+def ceilings(steps=30, nbytes=2 << 30, kinds=("copy", "read", "write")):
+    """HBM GB/s of plain streaming kernels over `nbytes` buffers: a copy (bytes
+    read plus bytes written), a read-only and a write-only pass."""
     import torch
 
-    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    lib = stream_library()
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
-    wall, ev = time_calls(lambda: b.copy_(a), steps, 5)
-    return 2 * nbytes / (ev * 1e-3) / 1e9, ev
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    calls = {
+        "copy": (lambda: lib.ssu_stream_copy(b.data_ptr(), a.data_ptr(), nbytes, s), 2 * nbytes),
+        "read": (lambda: lib.ssu_stream_read(a.data_ptr(), nbytes, sink.data_ptr(), s), nbytes),
+        "write": (lambda: lib.ssu_stream_write(b.data_ptr(), nbytes, s), nbytes),
+    }
+    out = {}
+    for k in kinds:
+        call, moved = calls[k]
+        _, ev = time_calls(call, steps, 3)
+        out[k] = moved / (ev * 1e-3) / 1e9
+    return out
 
 
 def traffic_for(workload, kernel_ms):
@@ -230,6 +260,95 @@ def torch_index(idx):
     return torch.as_tensor(idx, dtype=torch.long)
 
 
+# ------------------------------------------------------------ profile summary
+
+def _csv_rows(pattern):
+    import csv
+    rows = []
+    for f in sorted(glob.glob(pattern, recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize(prof_dir, workload, cmd):
+    """Summarise rocprofv3 output under prof_dir: kt/ (kernel trace + stats),
+    pmc_FETCH_SIZE/ and pmc_WRITE_SIZE/ (SSU kernel), cal_FETCH_SIZE/ and
+    cal_WRITE_SIZE/ (the streaming copy of 2 GiB each way). Writes the summary
+    to profiles/ and records the calibrated traffic in profiles/traffic.json."""
+    import statistics
+    from selective_state_update_ssu_amd import workloads as wl
+
+    stats = [r for r in _csv_rows(os.path.join(prof_dir, "kt", "**", "*kernel_stats.csv"))
+             if "ssu_update_kernel" in r["Name"]]
+    if len(stats) != 1:
+        raise SystemExit(f"expected one SSU kernel in the stats, found {len(stats)}")
+    kname, avg_ns = stats[0]["Name"], float(stats[0]["AverageNs"])
+
+    def counter(sub, name, kernel_pred):
+        vals = [float(r["Counter_Value"]) for r in
+                _csv_rows(os.path.join(prof_dir, sub, "**", "*counter_collection.csv"))
+                if r["Counter_Name"] == name and kernel_pred(r["Kernel_Name"])]
+        return statistics.median(vals), len(vals)
+
+    is_ssu = lambda n: "ssu_update_kernel" in n
+    is_copy = lambda n: "copy_kernel" in n
+    fetch_kib, nf = counter("pmc_FETCH_SIZE", "FETCH_SIZE", is_ssu)
+    write_kib, nw = counter("pmc_WRITE_SIZE", "WRITE_SIZE", is_ssu)
+    cal_fetch, _ = counter("cal_FETCH_SIZE", "FETCH_SIZE", is_copy)
+    cal_write, _ = counter("cal_WRITE_SIZE", "WRITE_SIZE", is_copy)
+    copy_bytes = 2 << 30
+    f_fetch = copy_bytes / (cal_fetch * 1024)
+    f_write = copy_bytes / (cal_write * 1024)
+    read_b = fetch_kib * 1024 * f_fetch
+    write_b = write_kib * 1024 * f_write
+    w = wl.NAMED[workload]("cpu")
+    acc = accounting(w)
+    traffic = read_b + write_b
+    algo_read, algo_write = acc["read_bytes"], acc["write_bytes"]
+    gbps = acc["bytes"] / (avg_ns * 1e-9) / 1e9
+    short = kname.replace("_ZN3ssu17ssu_update_kernelI", "ssu_update_kernel<").split("EEEv")[0]
+    md = f"""# {short} on {workload}
+
+Kernel: `{kname}`
+
+Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):
+```
+{cmd.strip()}
+```
+
+| quantity | value |
+|---|---|
+| average kernel duration (kernel trace, {stats[0]['Calls']} calls) | {avg_ns / 1e3:.1f} us |
+| algorithmic bytes per launch | {acc['bytes'] / 1e6:.2f} MB (read {algo_read / 1e6:.2f}, write {algo_write / 1e6:.2f}) |
+| algorithmic bandwidth at that duration | {gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.3f} of 8 TB/s) |
+| FETCH_SIZE per dispatch (median of {nf}) | {fetch_kib:.1f} KiB |
+| WRITE_SIZE per dispatch (median of {nw}) | {write_kib:.1f} KiB |
+| copy calibration, 2 GiB each way: FETCH_SIZE / WRITE_SIZE | {cal_fetch:.1f} / {cal_write:.1f} KiB |
+| scale factors (true bytes / counter bytes) | fetch {f_fetch:.4f}, write {f_write:.4f} |
+| calibrated HBM traffic per launch | {traffic / 1e6:.2f} MB (read {read_b / 1e6:.2f}, write {write_b / 1e6:.2f}) |
+| traffic / algorithmic bytes | {traffic / acc['bytes']:.4f} |
+"""
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    out_md = os.path.join(ROOT, "profiles", f"ssu_update_kernel_{workload}.md")
+    with open(out_md, "w") as f:
+        f.write(md)
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        rec = {"kernel_source_sha256": kernel_source_hash(), "workloads": {}}
+    rec["workloads"][workload] = {
+        "kernel": kname, "avg_ns": avg_ns, "fetch_kib": fetch_kib, "write_kib": write_kib,
+        "fetch_scale": f_fetch, "write_scale": f_write, "hbm_bytes_per_launch": traffic,
+        "algorithmic_bytes": acc["bytes"]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(md)
+
+
 # ---------------------------------------------------------------------- main
 
 def describe(w):
@@ -243,13 +362,13 @@ def describe(w):
     return d
 
 
-def run_workload(name, steps, warmup, hpb):
+def run_workload(name, steps, warmup, hpb, lpl=0):
     import torch
     from selective_state_update_ssu_amd import workloads as wl
 
     w = wl.NAMED[name]("cuda")
     acc = accounting(w)
-    wall, ev = time_calls(make_call(w, hpb), steps, warmup)
+    wall, ev = time_calls(make_call(w, hpb, lpl), steps, warmup)
     rec = dict(config=describe(w), ms_per_step=wall, kernel_us=ev * 1e3,
                tokens_per_s=acc["live_rows"] / (wall * 1e-3),
                hbm_gbps=acc["bytes"] / (ev * 1e-3) / 1e9, **acc)
@@ -261,6 +380,9 @@ def run_workload(name, steps, warmup, hpb):
 
 def main():
     args = parse()
+    if args.mode == "summarize":
+        summarize(args.prof_dir, args.workload, args.prof_cmd)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
@@ -276,11 +398,12 @@ def main():
     torch.cuda.set_device(0)
 
     if args.mode == "copy":
-        gbps, ms = copy_bandwidth()
-        print(json.dumps({"copy_gbps": gbps, "copy_ms": ms, "bytes_each_way": 2 << 30}))
+        print(json.dumps({"ceilings_gbps": ceilings(steps=args.steps, kinds=("copy",)),
+                          "bytes_each_way": 2 << 30}))
         return
 
-    head = run_workload(args.workload, args.steps, args.warmup, args.heads_per_block)
+    head = run_workload(args.workload, args.steps, args.warmup, args.heads_per_block,
+                        args.loads_per_lane)
     print(f"[bench] {args.workload}: {head['kernel_us']:.1f} us/launch, "
           f"{head['hbm_gbps']:.0f} GB/s, {head['tokens_per_s'] / 1e6:.3f} M tokens/s",
           file=sys.stderr, flush=True)
@@ -294,12 +417,13 @@ def main():
             if name == args.workload:
                 continue
             rec = run_workload(name, max(20, args.steps // 2), max(5, args.warmup // 2),
-                               args.heads_per_block)
+                               args.heads_per_block, args.loads_per_lane)
             extra[name] = {k: rec[k] for k in ("tokens_per_s", "hbm_gbps", "frac_of_peak",
                                                "kernel_us", "ms_per_step", "bytes", "live_rows")}
             print(f"[bench] {name}: {rec['kernel_us']:.1f} us/launch, {rec['hbm_gbps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
-    copy_gbps, _ = copy_bandwidth()
+    ceil = ceilings()
+    copy_gbps = ceil["copy"]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     kernel_ms = head["kernel_us"] * 1e-3
@@ -321,6 +445,7 @@ def main():
         "frac_of_peak": head["frac_of_peak"],
         "copy_gbps": copy_gbps,
         "frac_of_copy": head["hbm_gbps"] / copy_gbps,
+        "stream_ceilings_gbps": ceil,
         "roofline": {
             "bound": "hbm",
             "achieved": head["hbm_gbps"],

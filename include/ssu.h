@@ -118,7 +118,12 @@ typedef struct ssu_operands {
 
     int32_t heads_per_block;  /* launch shape: heads of one group per workgroup,
                                  0 = library default, else 1, 2 or 4 dividing
-                                 nheads / ngroups */
+                                 nheads / ngroups (at most 2 for dstate 256
+                                 and for ssu_packed_varlen) */
+    int32_t loads_per_lane;   /* launch shape: 16-byte state loads each lane keeps in
+                                 flight, 0 = library default, else 2 or 4 */
+    int32_t tile_order;       /* launch shape: 0 = library default, 1 = each XCD takes
+                                 a contiguous range of tiles, 2 = hardware order */
 } ssu_operands;
 
 /*

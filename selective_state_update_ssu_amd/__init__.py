@@ -84,7 +84,7 @@ def _per_head(name, t, heads):
 
 
 def _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus, pad_slot_id,
-              disable_state_update, heads_per_block):
+              disable_state_update, heads_per_block, loads_per_lane, tile_order):
     if state.dim() != 4:
         raise ValueError(f"state must be [slots, heads, dim, dstate], got {tuple(state.shape)}")
     if state.dtype not in _STATE_DTYPES:
@@ -132,7 +132,8 @@ def _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus, pad_slot_i
         dt=_ptr(dt), dt_per_dim=dt_per_dim, A=_ptr(A), D=_ptr(D), dt_bias=_ptr(dt_bias),
         dt_softplus=int(bool(dt_softplus)), pad_slot_id=int(pad_slot_id),
         disable_state_update=int(bool(disable_state_update)),
-        heads_per_block=int(heads_per_block))
+        heads_per_block=int(heads_per_block), loads_per_lane=int(loads_per_lane),
+        tile_order=int(tile_order))
     return op, out, rows
 
 
@@ -163,12 +164,16 @@ def _raise(lib, rc, entry):
 
 def ssu_one_token(state, x, dt, A, B, C, out=None, *, D=None, z=None, dt_bias=None,
                   dt_softplus=False, state_batch_indices=None, dst_state_batch_indices=None,
-                  pad_slot_id=-1, disable_state_update=False, heads_per_block=0, stream=None):
+                  pad_slot_id=-1, disable_state_update=False, heads_per_block=0,
+                  loads_per_lane=0, tile_order=0, stream=None):
     """One decode token per sequence (row b is sequence b). Updates `state` in place
-    at the destination slots and returns `out` [batch, heads, dim]."""
+    at the destination slots and returns `out` [batch, heads, dim].
+    heads_per_block / loads_per_lane / tile_order pick the launch shape (0: the
+    library default)."""
     lib = library()
     op, out, batch = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
-                               pad_slot_id, disable_state_update, heads_per_block)
+                               pad_slot_id, disable_state_update, heads_per_block,
+                               loads_per_lane, tile_order)
     src, src_dt = _index("state_batch_indices", state_batch_indices, state.device)
     dst, dst_dt = _index("dst_state_batch_indices", dst_state_batch_indices, state.device)
     for name, t in (("state_batch_indices", src), ("dst_state_batch_indices", dst)):
@@ -201,12 +206,14 @@ def _table(name, t, device, nseq):
 def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens, out=None, *, num_accepted_tokens=None,
                       state_batch_indices=None, dst_state_batch_indices=None, D=None, z=None,
                       dt_bias=None, dt_softplus=False, pad_slot_id=-1,
-                      disable_state_update=False, steps=None, heads_per_block=0, stream=None):
+                      disable_state_update=False, steps=None, heads_per_block=0,
+                      loads_per_lane=0, tile_order=0, stream=None):
     """Packed variable-length multi-token update. Sequence b owns rows
     [cu_seqlens[b], cu_seqlens[b+1]). Returns `out` [rows, heads, dim]."""
     lib = library()
     op, out, rows = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
-                              pad_slot_id, disable_state_update, heads_per_block)
+                              pad_slot_id, disable_state_update, heads_per_block,
+                              loads_per_lane, tile_order)
     cu, meta = _index("cu_seqlens", cu_seqlens, state.device)
     if cu is None or cu.dim() != 1 or cu.shape[0] < 1:
         raise ValueError("cu_seqlens must be a 1-D [sequences + 1] tensor")

@@ -18,6 +18,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIBRARY = os.path.join(LIB_DIR, "libssu_amd.so")
+# Streaming reference kernels used by the benchmark only (bandwidth ceilings and
+# counter calibration); not part of the SSU library.
+STREAM_LIBRARY = os.path.join(LIB_DIR, "libssu_stream.so")
+STREAM_SOURCES = ["stream_ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -57,15 +61,17 @@ def build(verbose: bool = False) -> str:
         msg = _run([HIPCC, *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         return obj, msg
 
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        results = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 1)) as ex:
+        results = list(ex.map(compile_one, SOURCES + STREAM_SOURCES))
     for obj, msg in results:
         if msg and verbose:
             print(msg, file=sys.stderr)
-    tmp = LIBRARY + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-          *[o for o, _ in results]])
-    os.replace(tmp, LIBRARY)
+    objs = dict(zip(SOURCES + STREAM_SOURCES, (o for o, _ in results)))
+    for lib, srcs in ((LIBRARY, SOURCES), (STREAM_LIBRARY, STREAM_SOURCES)):
+        tmp = lib + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+              *[objs[s] for s in srcs]])
+        os.replace(tmp, lib)
     return LIBRARY
 
 

@@ -57,7 +57,7 @@ bool overlaps(const Range& a, const Range& b) {
 }
 
 // Checks shared by both entry points. `rows` rows of x/out/B/C/z/dt are used.
-int check_operands(const ssu_operands& op, int64_t rows, bool work) {
+int check_operands(const ssu_operands& op, int64_t rows, bool work, bool packed) {
     if (!is_dtype(op.state_dtype))
         return fail(SSU_ERR_INVALID_ARGUMENT, "state_dtype %d is not an ssu_dtype", op.state_dtype);
     if (!is_dtype(op.io_dtype))
@@ -80,13 +80,19 @@ int check_operands(const ssu_operands& op, int64_t rows, bool work) {
     if (hpb > 1 && hpg % hpb != 0)
         return fail(SSU_ERR_INVALID_ARGUMENT,
                     "heads_per_block (%d) must divide nheads / ngroups (%lld)", hpb, (long long)hpg);
+    if (op.tile_order < 0 || op.tile_order > 2)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "tile_order must be 0, 1 or 2, got %d", op.tile_order);
+    if (op.loads_per_lane != 0 && op.loads_per_lane != 2 && op.loads_per_lane != 4)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "loads_per_lane must be 0, 2 or 4, got %d",
+                    op.loads_per_lane);
     const int64_t N = op.dstate;
     if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256)
         return fail(SSU_ERR_UNSUPPORTED, "dstate %lld is not built (16, 32, 64, 128, 256 are)",
                     (long long)N);
-    if (hpb > ssu::max_heads_per_block(static_cast<int>(N)))
-        return fail(SSU_ERR_UNSUPPORTED, "heads_per_block %d exceeds %d for dstate %lld", hpb,
-                    ssu::max_heads_per_block(static_cast<int>(N)), (long long)N);
+    const int hmax = ssu::max_heads_per_block(static_cast<int>(N), packed);
+    if (hpb > hmax)
+        return fail(SSU_ERR_UNSUPPORTED, "heads_per_block %d exceeds %d for dstate %lld%s", hpb,
+                    hmax, (long long)N, packed ? " (packed)" : "");
     const size_t ssz = dtype_size(op.state_dtype), iosz = dtype_size(op.io_dtype);
     if (op.nheads > INT32_MAX || op.headdim > INT32_MAX ||
         static_cast<uint64_t>(op.headdim) * N * ssz > 0x7fffffffull)
@@ -131,12 +137,34 @@ int check_operands(const ssu_operands& op, int64_t rows, bool work) {
     return SSU_OK;
 }
 
-int default_heads_per_block(const ssu_operands& op) {
-    (void)op;
-    return 1;
+// Default launch shape. Measured on MI355X at the named decode shapes (dstate
+// 128, headdim 64): a read+write one-token call streams best in small tiles
+// (2 loads per lane, 2 heads per workgroup with an fp32 state, 1 with a 16-bit
+// one); a read-only call and the packed call, which writes several states per
+// state read, in larger ones (4 loads per lane, 2 heads per workgroup). One-token
+// calls gain from each XCD walking a contiguous range of tiles; packed calls do
+// not (their per-sequence work varies with the token count).
+struct Shape {
+    int heads_per_block, loads_per_lane, xcd_order;
+};
+
+Shape default_shape(const ssu_operands& op, bool packed) {
+    const bool read_only = op.disable_state_update != 0;
+    Shape s;
+    if (packed)
+        s = {2, 4, 0};
+    else if (read_only)
+        s = {2, 4, 1};
+    else
+        s = {op.state_dtype == SSU_F32 ? 2 : 1, 2, 1};
+    const int64_t hpg = op.nheads / op.ngroups;
+    const int hmax = ssu::max_heads_per_block(static_cast<int>(op.dstate), packed);
+    while (s.heads_per_block > 1 && (hpg % s.heads_per_block != 0 || s.heads_per_block > hmax))
+        s.heads_per_block /= 2;
+    return s;
 }
 
-void fill_common(ssu::KernelParams& k, const ssu_operands& op) {
+void fill_common(ssu::KernelParams& k, const ssu_operands& op, bool packed) {
     k.state = op.state;
     k.x = op.x;
     k.B = op.B;
@@ -153,9 +181,11 @@ void fill_common(ssu::KernelParams& k, const ssu_operands& op) {
     k.headdim = static_cast<int32_t>(op.headdim);
     k.ngroups = static_cast<int32_t>(op.ngroups);
     k.heads_per_group = static_cast<int32_t>(op.nheads / op.ngroups);
-    k.heads_per_block = op.heads_per_block ? op.heads_per_block : default_heads_per_block(op);
+    const Shape dflt = default_shape(op, packed);
+    k.heads_per_block = op.heads_per_block ? op.heads_per_block : dflt.heads_per_block;
+    k.loads_per_lane = op.loads_per_lane ? op.loads_per_lane : dflt.loads_per_lane;
+    k.xcd_order = op.tile_order ? op.tile_order == 1 : dflt.xcd_order;
     k.head_blocks = k.nheads / k.heads_per_block;
-    k.row_blocks = static_cast<int32_t>((op.headdim + ssu::kRowsPerBlock - 1) / ssu::kRowsPerBlock);
     k.dt_per_dim = op.dt_per_dim;
     k.dt_softplus = op.dt_softplus ? 1 : 0;
     k.disable_state_update = op.disable_state_update ? 1 : 0;
@@ -163,28 +193,25 @@ void fill_common(ssu::KernelParams& k, const ssu_operands& op) {
 
 int launch(const ssu::KernelParams& k, const ssu_operands& op, int64_t nseq, void* stream,
            const char* entry) {
-    const uint64_t blocks = static_cast<uint64_t>(nseq) * k.head_blocks * k.row_blocks;
-    if (blocks > 0x7fffffffull)
-        return fail(SSU_ERR_UNSUPPORTED, "%s: %llu workgroups exceed the grid limit", entry,
-                    (unsigned long long)blocks);
-    const dim3 grid(static_cast<unsigned>(blocks));
-    const dim3 block(static_cast<unsigned>(ssu::kHeadThreads * k.heads_per_block));
     const auto s = static_cast<hipStream_t>(stream);
     const int io = op.io_dtype, N = static_cast<int>(op.dstate);
-    if (log_enabled())
-        std::fprintf(stderr,
-                     "[ssu] %s: state=%s io=%s dstate=%d heads_per_block=%d grid=%u block=%u "
-                     "lds=%d B\n",
-                     entry, dtype_name(op.state_dtype), dtype_name(io), N, k.heads_per_block,
-                     grid.x, block.x,
-                     static_cast<int>(sizeof(float) * 2 *
-                                      (2 * N + 5 * k.heads_per_block * ssu::kRowsPerBlock)));
+    ssu::LaunchShape shape;
     hipError_t e;
     switch (op.state_dtype) {
-        case SSU_F32: e = ssu::launch_state_f32(k, io, N, grid, block, s); break;
-        case SSU_F16: e = ssu::launch_state_f16(k, io, N, grid, block, s); break;
-        default: e = ssu::launch_state_bf16(k, io, N, grid, block, s); break;
+        case SSU_F32: e = ssu::launch_state_f32(k, io, N, nseq, s, &shape); break;
+        case SSU_F16: e = ssu::launch_state_f16(k, io, N, nseq, s, &shape); break;
+        default: e = ssu::launch_state_bf16(k, io, N, nseq, s, &shape); break;
     }
+    if (log_enabled())
+        std::fprintf(stderr,
+                     "[ssu] %s: state=%s io=%s dstate=%d heads_per_block=%d loads_per_lane=%d "
+                     "xcd_order=%d rows_per_block=%u grid=%u block=%u lds=%u B -> %s\n",
+                     entry, dtype_name(op.state_dtype), dtype_name(io), N, k.heads_per_block,
+                     k.loads_per_lane, k.xcd_order,
+                     shape.rows_per_block, shape.grid, shape.block, shape.lds_bytes,
+                     hipGetErrorString(e));
+    if (e == hipErrorInvalidConfiguration)
+        return fail(SSU_ERR_UNSUPPORTED, "%s: the launch needs more than 2^31-1 workgroups", entry);
     if (e != hipSuccess)
         return fail(SSU_ERR_LAUNCH, "%s: launch failed: %s", entry, hipGetErrorString(e));
     return ok();
@@ -206,11 +233,11 @@ int ssu_one_token(const ssu_one_token_args* a, void* stream) {
     if (a->dst_slots && !is_index(a->dst_dtype))
         return fail(SSU_ERR_INVALID_ARGUMENT, "dst_dtype %d is not an ssu_index_dtype", a->dst_dtype);
     const ssu_operands& op = a->op;
-    if (int rc = check_operands(op, a->batch, a->batch > 0)) return rc;
+    if (int rc = check_operands(op, a->batch, a->batch > 0, false)) return rc;
     if (a->batch == 0) return ok();
 
     ssu::KernelParams k{};
-    fill_common(k, op);
+    fill_common(k, op, false);
     k.src = a->src_slots;
     k.dst = a->dst_slots;
     k.src_i64 = a->src_dtype == SSU_I64;
@@ -247,11 +274,11 @@ int ssu_packed_varlen(const ssu_packed_args* a, void* stream) {
         return fail(SSU_ERR_INVALID_ARGUMENT, "table strides must be >= 0");
     const ssu_operands& op = a->op;
     const bool work = a->nseq > 0 && a->rows > 0;
-    if (int rc = check_operands(op, a->rows, work)) return rc;
+    if (int rc = check_operands(op, a->rows, work, true)) return rc;
     if (!work) return ok();
 
     ssu::KernelParams k{};
-    fill_common(k, op);
+    fill_common(k, op, true);
     k.src = a->src_table;
     k.dst = a->dst_table;
     k.cu = a->cu_seqlens;

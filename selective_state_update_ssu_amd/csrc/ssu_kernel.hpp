@@ -1,29 +1,29 @@
 // ssu_kernel.hpp -- the selective state update kernel for gfx950 (CDNA4, wave64).
 //
-// One workgroup owns a (sequence, block of heads of one group, block of 64 rows)
+// One workgroup owns a (sequence, block of heads of one group, block of rows)
 // tile. Each head of the block gets a 256-thread head group (four wave64s). The
 // head's rows are spread so that one vector-memory instruction of a wave covers
 // RPI whole consecutive dstate rows -- 64 lanes x (16 or 8) bytes, one contiguous
-// 1 KiB (or 512 B) run of the slot -- and each lane owns the same VEC consecutive
-// dstate elements of RL different rows for the whole call. The state therefore
-// crosses HBM exactly once in each direction: read once per sequence, kept in fp32
-// registers across all tokens of a packed sequence, written once per token.
+// run of the slot -- and each lane owns the same VEC consecutive dstate elements
+// of RL different rows for the whole call. The state therefore crosses HBM
+// exactly once in each direction: read once per sequence, kept in fp32 registers
+// across all tokens of a packed sequence, written once per token.
 //
-// Per token, the operands that are shared along a row (B and C of the group, N
-// values each) or along dstate (x, z, dt of the head, one per row) are staged once
-// in LDS, widened to fp32 and with dt -> v -> dA evaluated there, then read by
-// every lane that needs them; B and C are shared by all heads of the workgroup.
-// The dot product over dstate is a lane-local FMA chain followed by a cross-lane
-// reduction over the LPR lanes of a row (DPP quad/mirror moves inside 16-lane
-// rows, one permute across rows when LPR > 16). The per-row epilogue (D * x,
-// SiLU gate, rounding, store of `out`) runs on one lane per row after the partial
-// sums meet in LDS.
+// The per-token operands shared along a row (B and C of the group, N values
+// each) or along dstate (x, z, dt of the head, one per row) are staged in LDS
+// once per workgroup, already widened to fp32 and turned into the per-row
+// factors the update needs (v*x, exp(A*v), D*x, z*sigmoid(z)); B and C serve all
+// heads of the workgroup. A packed sequence stages up to kStageTokens tokens at a
+// time, so its token loop runs without a barrier or a global load: one barrier
+// per chunk of tokens. The dot product over dstate is a lane-local FMA chain plus
+// a cross-lane sum over the LPR lanes of a row (DPP quad/mirror moves inside
+// 16-lane rows, one permute across rows when LPR > 16); the first lane of each
+// row then finishes that row (skip term, gate, rounding) and stores it.
 //
 // Memory ordering: gfx9 counts loads and stores in one vmcnt queue, so every load
-// the next step waits for is issued before anything it must not wait for. The
-// token-0 operands are requested before the state, and token t+1's operands
-// before token t's state stores. Workgroup barriers fence LDS only, so the state
-// loads stay in flight across them. Stage buffers alternate between tokens.
+// the next step waits for is issued before anything it must not wait for: the
+// staged operands are requested before the state. Workgroup barriers fence LDS
+// only, so the state loads stay in flight across them.
 //
 // Semantics follow include/ssu.h.
 #pragma once
@@ -149,33 +149,64 @@ __device__ __forceinline__ bool slot_ok(int64_t s, const KernelParams& p) {
     return s != p.pad_slot_id && s >= 0 && s < p.nslots;
 }
 
-// Number of LDS floats a launch needs (double-buffered stage).
-__host__ __device__ constexpr int lds_floats(int dstate, int heads_per_block) {
-    return 2 * (2 * dstate + 5 * heads_per_block * kRowsPerBlock);
+// Tokens of a packed sequence staged in LDS at a time.
+constexpr int kStageTokens = 8;
+
+// LDS floats one staged token takes: B and C of the group, then four per-row
+// factors for every row of every head of the workgroup.
+__host__ __device__ constexpr int token_floats(int dstate, int heads_per_block, int rows) {
+    return 2 * dstate + 4 * heads_per_block * rows;
+}
+
+// LDS bytes of a launch: `tokens` staged tokens, their destination ids, and one
+// row sum per row of the workgroup (each wave's rows, for its coalesced store).
+__host__ __device__ constexpr unsigned lds_bytes(int dstate, int heads_per_block, int rows,
+                                                 int tokens) {
+    return tokens * (4u * token_floats(dstate, heads_per_block, rows) + 8u) +
+           4u * heads_per_block * rows;
+}
+
+// Order this wave's earlier LDS writes before its later LDS reads (other lanes).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Lane geometry of one (state dtype, dstate, load depth) instance.
+template <typename ST, int N, int LOADS>
+struct Geometry {
+    static constexpr int kMaxVec = 16 / static_cast<int>(sizeof(ST));
+    static constexpr int VEC = kMaxVec < N / 4 ? kMaxVec : N / 4;  // elements per lane-load
+    static constexpr int LPR = N / VEC;                            // lanes per dstate row
+    static constexpr int RPI = 64 / LPR;                           // rows per wave instruction
+    static constexpr int RL = LOADS < LPR / 4 ? LOADS : LPR / 4;  // loads per lane
+    static constexpr int RB = 4 * RPI * RL;                        // rows per head group
+    static_assert(RL >= 1 && RB <= kHeadThreads, "geometry");
+};
+
+// Tile of workgroup `id` out of `n` when each XCD should walk a contiguous range
+// of tiles: workgroup id lands on XCD id % kXcds, and the XCDs that receive one
+// extra workgroup come first. A bijection of [0, n).
+__device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t n) {
+    const int64_t xcd = id % kXcds, k = id / kXcds;
+    const int64_t per = (n + kXcds - 1) / kXcds;
+    int64_t tall = n % kXcds;
+    if (tall == 0) tall = kXcds;
+    return xcd < tall ? xcd * per + k : tall * per + (xcd - tall) * (per - 1) + k;
 }
 
 // ------------------------------------------------------------------ kernel
 
-template <typename ST, typename IT, int N, bool PACKED>
-__global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N)) void ssu_update_kernel(
+template <typename ST, typename IT, int N, int LOADS, bool PACKED>
+__global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void ssu_update_kernel(
     const KernelParams p) {
     // Lane geometry.
-    constexpr int kMaxVec = 16 / static_cast<int>(sizeof(ST));
-    constexpr int VEC = kMaxVec < N / 4 ? kMaxVec : N / 4;    // elements per lane-load
+    typedef Geometry<ST, N, LOADS> Geo;
+    constexpr int VEC = Geo::VEC, LPR = Geo::LPR, RPI = Geo::RPI, RL = Geo::RL, RB = Geo::RB;
     constexpr int W = VEC / Pack<ST>::kPerWord;               // 32-bit words per lane-load
-    constexpr int LPR = N / VEC;                              // lanes per dstate row
-    constexpr int RPI = 64 / LPR;                             // rows per wave instruction
-    constexpr int RL = LPR / 4;                               // row-loads per lane
-    constexpr int RB = kRowsPerBlock;
-    static_assert(4 * RPI * RL == RB, "a head group covers one row block");
+    constexpr int T = PACKED ? kStageTokens : 1;              // tokens staged at a time
     typedef typename Words<W>::type words_t;
-
-    extern __shared__ float lds[];
-    const int hpb = p.heads_per_block;
-    float* const sB = lds;                   // [2][N]
-    float* const sC = sB + 2 * N;            // [2][N]
-    float* const sRow = sC + 2 * N;          // [2][5][hpb][RB]: xv, dA, x, z, y
-    enum { kXV = 0, kDA = 1, kX = 2, kZ = 3, kY = 4 };
 
     const int tid = threadIdx.x;
     // Head within the workgroup and wave within the head group are wave-uniform;
@@ -186,17 +217,30 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N)) void ssu_upda
     const int lane = ht % 64;
     const int rg = lane / LPR;               // row within one wave instruction
     const int n0 = (lane % LPR) * VEC;       // first dstate element of this lane
+    const bool row_leader = (lane % LPR) == 0;
 
     int64_t wg = blockIdx.x;
+    if (p.xcd_order) wg = xcd_tile(wg, gridDim.x);
     const int rb = static_cast<int>(wg % p.row_blocks);
     wg /= p.row_blocks;
     const int hblk = static_cast<int>(wg % p.head_blocks);
     const int64_t seq = wg / p.head_blocks;
+    const int hpb = p.heads_per_block;
     const int h = hblk * hpb + lh;
     const int g = (hblk * hpb) / p.heads_per_group;
     const int H = p.nheads, P = p.headdim;
-    auto row_slot = [&](int buf, int which, int pl) -> float& {
-        return sRow[((buf * 5 + which) * hpb + lh) * RB + pl];
+
+    // LDS: per staged token tt, B[N] C[N] then factors [4][hpb][RB]; after all
+    // tokens, their destination ids.
+    extern __shared__ float lds[];
+    const int tok = token_floats(N, hpb, RB);
+    int64_t* const sW = reinterpret_cast<int64_t*>(lds + T * tok);
+    // This wave's row sums, indexed by row within the wave's RPI * RL rows.
+    constexpr int WROWS = RPI * RL;
+    float* const sY = reinterpret_cast<float*>(sW + T) + (lh * 4 + wave) * WROWS;
+    enum { kXV = 0, kDA = 1, kDX = 2, kGZ = 3 };  // v*x, exp(A*v), D*x, z*sigmoid(z)
+    auto factor = [&](int tt, int which, int pl) -> float& {
+        return lds[tt * tok + 2 * N + (which * hpb + lh) * RB + pl];
     };
 
     // ---- slot resolution (uniform across the workgroup)
@@ -226,81 +270,109 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N)) void ssu_upda
     const float a_h = p.A[h];
     const float d_h = p.D ? p.D[h] : 0.f;
     const float bias_h = p.dt_bias ? p.dt_bias[h] : 0.f;
+    const bool gated = p.z != nullptr;
 
-    // ---- per-token operand staging: raw loads into registers, widened and written
-    // to LDS only when the next step needs them. Threads that stage nothing load a
-    // valid dummy address instead of branching.
-    const int prow = rb * RB + ht;            // row this thread stages (ht < RB)
-    const bool stages_row = ht < RB && prow < P;
-    const bool stages_bc = tid < N;
+    // ---- operand staging: raw loads into registers, factors into LDS once the
+    // loads land. A chunk of nt tokens is spread over the workgroup: row factors
+    // over (token, row) pairs of each head group, B/C over (token, n) pairs of the
+    // whole workgroup, destination ids over the first nt threads. Elements past
+    // the chunk or past headdim load a valid dummy address instead of branching.
+    constexpr int ROW_PASSES = (T * RB + kHeadThreads - 1) / kHeadThreads;
+    constexpr int BC_PASSES = (T * N + kHeadThreads - 1) / kHeadThreads;
+    const int nthreads = kHeadThreads * hpb;
     typedef typename Bits<IT>::type bits_t;
     const bits_t* const xp = static_cast<const bits_t*>(p.x);
-    const bits_t* const zp = static_cast<const bits_t*>(p.z ? p.z : p.x);  // no gate: unused
+    const bits_t* const zp = static_cast<const bits_t*>(gated ? p.z : p.x);  // ungated: unused
     const bits_t* const Bp = static_cast<const bits_t*>(p.B);
     const bits_t* const Cp = static_cast<const bits_t*>(p.C);
-    struct Stage {
-        bits_t x, z, b, c;
+    struct RowStage {
+        bits_t x, z;
         float dt;
-        int64_t w;                             // raw destination id (validated at use)
     };
-    auto stage_load = [&](int64_t t) -> Stage {
-        Stage s;
-        const int64_t row = begin + t;
-        const int64_t xi = stages_row ? (row * H + h) * P + prow : 0;
-        s.x = xp[xi];
-        s.z = zp[xi];
-        s.dt = p.dt[p.dt_per_dim ? xi : (stages_row ? row * H + h : 0)];
-        const int64_t bi = stages_bc ? (row * p.ngroups + g) * N + tid : 0;
-        s.b = Bp[bi];
-        s.c = Cp[bi];
+    RowStage rs[ROW_PASSES];
+    bits_t bs[BC_PASSES], cs[BC_PASSES];
+    int64_t dw = 0;
+    // Raw destination slot of token t (validated where it is used).
+    auto dest_load = [&](int64_t t) -> int64_t {
         if constexpr (PACKED) {
             if (p.dst)
-                s.w = t < p.steps ? load_index(p.dst, p.dst_i64,
-                                               seq * p.dst_seq_stride + t * p.dst_step_stride)
-                                  : p.pad_slot_id;
-            else
-                s.w = (t == len - 1) ? r : p.pad_slot_id;
+                return t < p.steps
+                           ? load_index(p.dst, p.dst_i64, seq * p.dst_seq_stride + t * p.dst_step_stride)
+                           : p.pad_slot_id;
+            return t == len - 1 ? r : p.pad_slot_id;
         } else {
-            s.w = p.dst ? load_index(p.dst, p.dst_i64, seq) : r;
+            return p.dst ? load_index(p.dst, p.dst_i64, seq) : r;
         }
-        return s;
     };
-    auto stage_store = [&](const Stage& s, int buf) {
-        if (ht < RB) {
-            float xv = 0.f, dA = 0.f, x = 0.f, z = 0.f;
-            if (stages_row) {
-                x = widen_io<IT>(s.x);
-                z = widen_io<IT>(s.z);
-                float v = s.dt + bias_h;
-                if (p.dt_softplus) v = softplus_f32(v);
-                dA = expf(a_h * v);
-                xv = v * x;
+    auto load_chunk = [&](int64_t t0, int64_t nt) {
+#pragma unroll
+        for (int q = 0; q < ROW_PASSES; ++q) {
+            const int idx = ht + q * kHeadThreads, k = idx / RB, pl = idx % RB;
+            const bool live = k < nt && rb * RB + pl < P;
+            const int64_t row = begin + t0 + k;
+            const int64_t xi = live ? (row * H + h) * P + rb * RB + pl : 0;
+            rs[q].x = xp[xi];
+            rs[q].z = zp[xi];
+            rs[q].dt = p.dt[p.dt_per_dim ? xi : (live ? row * H + h : 0)];
+        }
+#pragma unroll
+        for (int q = 0; q < BC_PASSES; ++q) {
+            const int idx = tid + q * nthreads, k = idx / N, n = idx % N;
+            const int64_t bi = k < nt ? ((begin + t0 + k) * p.ngroups + g) * N + n : 0;
+            bs[q] = Bp[bi];
+            cs[q] = Cp[bi];
+        }
+        if (tid < nt) dw = dest_load(t0 + tid);
+    };
+    auto store_chunk = [&](int64_t nt) {
+#pragma unroll
+        for (int q = 0; q < ROW_PASSES; ++q) {
+            const int idx = ht + q * kHeadThreads, k = idx / RB, pl = idx % RB;
+            if (k < nt) {
+                float xv = 0.f, dA = 0.f, dx = 0.f, gz = 1.f;
+                if (rb * RB + pl < P) {
+                    const float x = widen_io<IT>(rs[q].x);
+                    float v = rs[q].dt + bias_h;
+                    if (p.dt_softplus) v = softplus_f32(v);
+                    dA = expf(a_h * v);
+                    xv = v * x;
+                    dx = d_h * x;
+                    if (gated) gz = silu_f32(widen_io<IT>(rs[q].z));
+                }
+                factor(k, kXV, pl) = xv;
+                factor(k, kDA, pl) = dA;
+                factor(k, kDX, pl) = dx;
+                factor(k, kGZ, pl) = gz;
             }
-            row_slot(buf, kXV, ht) = xv;
-            row_slot(buf, kDA, ht) = dA;
-            row_slot(buf, kX, ht) = x;
-            row_slot(buf, kZ, ht) = z;
         }
-        if (stages_bc) {
-            sB[buf * N + tid] = widen_io<IT>(s.b);
-            sC[buf * N + tid] = widen_io<IT>(s.c);
+#pragma unroll
+        for (int q = 0; q < BC_PASSES; ++q) {
+            const int idx = tid + q * nthreads, k = idx / N, n = idx % N;
+            if (k < nt) {
+                lds[k * tok + n] = widen_io<IT>(bs[q]);
+                lds[k * tok + N + n] = widen_io<IT>(cs[q]);
+            }
         }
+        if (tid < nt) sW[tid] = dw;
     };
 
-    // Token 0's operands are requested before the state, so waiting for them does
-    // not wait for the state.
-    Stage stage = stage_load(0);
+    // The first chunk's operands are requested before the state, so waiting for
+    // them does not wait for the state.
+    const int64_t first = len < T ? len : T;
+    load_chunk(0, first);
 
     // ---- state gather: RL row-loads per lane, all in flight at once. Rows past
     // headdim (a ragged last block) read the last row instead and are never stored.
     const size_t slot_bytes = static_cast<size_t>(H) * P * N * sizeof(ST);
     const size_t head_bytes = static_cast<size_t>(P) * N * sizeof(ST);
     const bool full_block = rb * RB + RB <= P;
+    int prow_of[RL];
     unsigned off[RL];
 #pragma unroll
     for (int i = 0; i < RL; ++i) {
-        const int pr = rb * RB + wave * (RPI * RL) + i * RPI + rg;
-        off[i] = (static_cast<unsigned>(pr < P ? pr : P - 1) * N + n0) * sizeof(ST);
+        prow_of[i] = rb * RB + wave * (RPI * RL) + i * RPI + rg;
+        const int pr = prow_of[i] < P ? prow_of[i] : P - 1;
+        off[i] = (static_cast<unsigned>(pr) * N + n0) * sizeof(ST);
     }
     words_t raw[RL];
     {
@@ -310,34 +382,43 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N)) void ssu_upda
             raw[i] = __builtin_nontemporal_load(reinterpret_cast<const words_t*>(tile + off[i]));
     }
 
-    float s[RL][VEC];
-    auto token = [&](int64_t t, bool first) {
-        const int buf = static_cast<int>(t & 1);
-        stage_store(stage, buf);
-        const int64_t w = uniform64(stage.w);
-        lds_barrier();
-        if constexpr (PACKED) {
-            if (t + 1 < len) stage = stage_load(t + 1);
-        }
-        if (first) {
-#pragma unroll
-            for (int i = 0; i < RL; ++i)
-#pragma unroll
-                for (int k = 0; k < W; ++k)
-                    Pack<ST>::widen(raw[i][k], &s[i][k * Pack<ST>::kPerWord]);
-        }
+    store_chunk(first);
+    lds_barrier();
 
+    float s[RL][VEC];
+#pragma unroll
+    for (int i = 0; i < RL; ++i)
+#pragma unroll
+        for (int k = 0; k < W; ++k) Pack<ST>::widen(raw[i][k], &s[i][k * Pack<ST>::kPerWord]);
+
+    char* const head_base = static_cast<char*>(p.state) + h * head_bytes;
+    for (int64_t t = 0; t < len; ++t) {
+        int tt = 0;
+        if constexpr (PACKED) {
+            tt = static_cast<int>(t % T);
+            if (t > 0 && tt == 0) {
+                // Next chunk: every wave is done with the previous one first.
+                lds_barrier();
+                const int64_t nt = len - t < T ? len - t : T;
+                load_chunk(t, nt);
+                store_chunk(nt);
+                lds_barrier();
+            }
+        }
+        const float* const sB = lds + tt * tok;
+        const float* const sC = sB + N;
         float bv[VEC], cv[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            bv[e] = sB[buf * N + n0 + e];
-            cv[e] = sC[buf * N + n0 + e];
+            bv[e] = sB[n0 + e];
+            cv[e] = sC[n0 + e];
         }
+        const int64_t out_row = ((begin + t) * H + h) * P;
 #pragma unroll
         for (int i = 0; i < RL; ++i) {
-            const int pl = wave * (RPI * RL) + i * RPI + rg;
-            const float dA = row_slot(buf, kDA, pl);
-            const float xv = row_slot(buf, kXV, pl);
+            const int pl = prow_of[i] - rb * RB;
+            const float dA = factor(tt, kDA, pl);
+            const float xv = factor(tt, kXV, pl);
             float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -345,71 +426,88 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N)) void ssu_upda
                 acc = fmaf(s[i][e], cv[e], acc);
             }
             acc = group_sum<LPR>(acc);
-            if ((lane % LPR) == 0) row_slot(buf, kY, pl) = acc;
+            if (row_leader) sY[i * RPI + rg] = acc;
         }
+        // The wave's rows are contiguous: lane k finishes row k (skip term, gate,
+        // rounding) so that `out` leaves in one coalesced store.
+        wave_lds_sync();
+        {
+            const int wrow0 = wave * WROWS;
+            const int prow_k = rb * RB + wrow0 + lane;
+            if (lane < WROWS && prow_k < P) {
+                const float y = (sY[lane] + factor(tt, kDX, wrow0 + lane)) *
+                                factor(tt, kGZ, wrow0 + lane);
+                store_io<IT>(p.out, out_row + prow_k, y);
+            }
+        }
+        wave_lds_sync();  // the next token's row sums reuse sY
 
         // ---- state scatter for this token
+        const int64_t w = uniform64(sW[tt]);
         if (!p.disable_state_update && slot_ok(w, p)) {
-            char* tile = static_cast<char*>(p.state) + w * slot_bytes + h * head_bytes;
+            char* tile = head_base + w * slot_bytes;
 #pragma unroll
             for (int i = 0; i < RL; ++i) {
                 words_t o;
 #pragma unroll
                 for (int k = 0; k < W; ++k) o[k] = Pack<ST>::narrow(&s[i][k * Pack<ST>::kPerWord]);
-                const int pr = rb * RB + wave * (RPI * RL) + i * RPI + rg;
-                if (full_block || pr < P)
+                if (full_block || prow_of[i] < P)
                     __builtin_nontemporal_store(o, reinterpret_cast<words_t*>(tile + off[i]));
             }
         }
-        lds_barrier();
-
-        // ---- epilogue: one lane per row
-        if (stages_row) {
-            float y = row_slot(buf, kY, ht) + d_h * row_slot(buf, kX, ht);
-            if (p.z) y *= silu_f32(row_slot(buf, kZ, ht));
-            store_io<IT>(p.out, ((begin + t) * H + h) * P + prow, y);
-        }
-    };
-
-    token(0, true);
-    if constexpr (PACKED) {
-        for (int64_t t = 1; t < len; ++t) token(t, false);
     }
 }
 
 // ---------------------------------------------------------------- launchers
 
-template <typename ST, typename IT, int N>
-hipError_t launch_instance(const KernelParams& p, dim3 grid, dim3 block, hipStream_t stream) {
-    const size_t lds = sizeof(float) * lds_floats(N, p.heads_per_block);
+template <typename ST, typename IT, int N, int LOADS>
+hipError_t launch_instance(KernelParams p, int64_t nseq, hipStream_t stream, LaunchShape* shape) {
+    constexpr int RB = Geometry<ST, N, LOADS>::RB;
+    p.row_blocks = (p.headdim + RB - 1) / RB;
+    const uint64_t blocks = static_cast<uint64_t>(nseq) * p.head_blocks * p.row_blocks;
+    if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    const dim3 block(static_cast<unsigned>(kHeadThreads * p.heads_per_block));
+    const unsigned lds = lds_bytes(N, p.heads_per_block, RB, p.packed ? kStageTokens : 1);
+    if (shape) *shape = LaunchShape{grid.x, block.x, lds, static_cast<unsigned>(RB)};
     if (p.packed)
-        hipLaunchKernelGGL((ssu_update_kernel<ST, IT, N, true>), grid, block, lds, stream, p);
+        hipLaunchKernelGGL((ssu_update_kernel<ST, IT, N, LOADS, true>), grid, block, lds, stream, p);
     else
-        hipLaunchKernelGGL((ssu_update_kernel<ST, IT, N, false>), grid, block, lds, stream, p);
+        hipLaunchKernelGGL((ssu_update_kernel<ST, IT, N, LOADS, false>), grid, block, lds, stream, p);
     return hipGetLastError();
 }
 
+template <typename ST, typename IT, int N>
+hipError_t launch_depth(const KernelParams& p, int64_t nseq, hipStream_t stream,
+                        LaunchShape* shape) {
+    switch (p.loads_per_lane) {
+        case 2: return launch_instance<ST, IT, N, 2>(p, nseq, stream, shape);
+        case 4: return launch_instance<ST, IT, N, 4>(p, nseq, stream, shape);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename ST, typename IT>
-hipError_t launch_dstate(const KernelParams& p, int dstate, dim3 grid, dim3 block,
-                         hipStream_t stream) {
+hipError_t launch_dstate(const KernelParams& p, int dstate, int64_t nseq, hipStream_t stream,
+                         LaunchShape* shape) {
     switch (dstate) {
-        case 16: return launch_instance<ST, IT, 16>(p, grid, block, stream);
-        case 32: return launch_instance<ST, IT, 32>(p, grid, block, stream);
-        case 64: return launch_instance<ST, IT, 64>(p, grid, block, stream);
-        case 128: return launch_instance<ST, IT, 128>(p, grid, block, stream);
-        case 256: return launch_instance<ST, IT, 256>(p, grid, block, stream);
+        case 16: return launch_depth<ST, IT, 16>(p, nseq, stream, shape);
+        case 32: return launch_depth<ST, IT, 32>(p, nseq, stream, shape);
+        case 64: return launch_depth<ST, IT, 64>(p, nseq, stream, shape);
+        case 128: return launch_depth<ST, IT, 128>(p, nseq, stream, shape);
+        case 256: return launch_depth<ST, IT, 256>(p, nseq, stream, shape);
         default: return hipErrorInvalidValue;
     }
 }
 
 // io dtype codes follow ssu_dtype: 0 fp32, 1 fp16, 2 bf16.
 template <typename ST>
-hipError_t launch_state(const KernelParams& p, int io_dtype, int dstate, dim3 grid, dim3 block,
-                        hipStream_t stream) {
+hipError_t launch_state(const KernelParams& p, int io_dtype, int dstate, int64_t nseq,
+                        hipStream_t stream, LaunchShape* shape) {
     switch (io_dtype) {
-        case 0: return launch_dstate<ST, float>(p, dstate, grid, block, stream);
-        case 1: return launch_dstate<ST, _Float16>(p, dstate, grid, block, stream);
-        case 2: return launch_dstate<ST, __bf16>(p, dstate, grid, block, stream);
+        case 0: return launch_dstate<ST, float>(p, dstate, nseq, stream, shape);
+        case 1: return launch_dstate<ST, _Float16>(p, dstate, nseq, stream, shape);
+        case 2: return launch_dstate<ST, __bf16>(p, dstate, nseq, stream, shape);
         default: return hipErrorInvalidValue;
     }
 }

@@ -3,9 +3,9 @@
 
 namespace ssu {
 
-hipError_t launch_state_f32(const KernelParams& p, int io_dtype, int dstate, dim3 grid,
-                           dim3 block, hipStream_t stream) {
-    return launch_state<float>(p, io_dtype, dstate, grid, block, stream);
+hipError_t launch_state_f32(KernelParams p, int io_dtype, int dstate, int64_t nseq,
+                           hipStream_t stream, LaunchShape* shape) {
+    return launch_state<float>(p, io_dtype, dstate, nseq, stream, shape);
 }
 
 }  // namespace ssu

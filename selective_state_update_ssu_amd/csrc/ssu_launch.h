@@ -7,17 +7,19 @@
 
 namespace ssu {
 
-// Rows of one head covered by one 256-thread head group of a workgroup.
-constexpr int kRowsPerBlock = 64;
-// Threads per head group (four wave64s).
+// Threads per head group (four wave64s): one head of one row block.
 constexpr int kHeadThreads = 256;
+// Depths of 16-byte state loads a lane may keep in flight; each is compiled. A
+// lane gets fewer when a head's dstate rows are too short to give it that many.
+constexpr int kLoadDepths[] = {2, 4};
 // Largest number of heads one workgroup may cover.
 constexpr int kMaxHeadsPerBlock = 4;
 
-// Heads per workgroup a dstate allows: dstate 256 keeps 64 state values per lane,
-// so its workgroups stop at 512 threads to leave the compiler 256 VGPRs.
-__host__ __device__ constexpr int max_heads_per_block(int dstate) {
-    return dstate >= 256 ? 2 : kMaxHeadsPerBlock;
+// Heads per workgroup an instance allows. Large states per lane (dstate 256) and
+// the packed kernel (state plus a chunk of staged tokens) stop at 512 threads, to
+// leave the compiler 256 VGPRs instead of spilling.
+__host__ __device__ constexpr int max_heads_per_block(int dstate, bool packed) {
+    return (dstate >= 256 || packed) ? 2 : kMaxHeadsPerBlock;
 }
 
 // Everything a launch needs, by value. Sizes are validated on the host.
@@ -47,8 +49,10 @@ struct KernelParams {
 
     int32_t nheads, headdim, ngroups, heads_per_group;
     int32_t heads_per_block;  // heads per workgroup (same group)
+    int32_t loads_per_lane;   // one of kLoadDepths
+    int32_t xcd_order;        // nonzero: each XCD walks a contiguous range of tiles
     int32_t head_blocks;      // nheads / heads_per_block
-    int32_t row_blocks;       // ceil(headdim / kRowsPerBlock)
+    int32_t row_blocks;       // ceil(headdim / rows per block), set by the launcher
 
     int32_t src_i64, dst_i64, meta_i64;
     int32_t packed;
@@ -57,13 +61,23 @@ struct KernelParams {
     int32_t disable_state_update;
 };
 
-// One launcher per state dtype; each dispatches on (io dtype, dstate).
-// Returns hipErrorInvalidValue for an (io, dstate) pair it was not built for.
-hipError_t launch_state_f32(const KernelParams& p, int io_dtype, int dstate,
-                            dim3 grid, dim3 block, hipStream_t stream);
-hipError_t launch_state_f16(const KernelParams& p, int io_dtype, int dstate,
-                            dim3 grid, dim3 block, hipStream_t stream);
-hipError_t launch_state_bf16(const KernelParams& p, int io_dtype, int dstate,
-                             dim3 grid, dim3 block, hipStream_t stream);
+// Compute dies (XCDs) the hardware deals consecutive workgroups to, round robin.
+constexpr int kXcds = 8;
+
+// Launch shape chosen by a launcher (reported for logging).
+struct LaunchShape {
+    unsigned grid = 0, block = 0, lds_bytes = 0, rows_per_block = 0;
+};
+
+// One launcher per state dtype; each dispatches on (io dtype, dstate), derives
+// the row block and grid of that kernel instance, and launches `nseq` sequences'
+// worth of workgroups. Returns hipErrorInvalidValue for an (io, dstate) pair it
+// was not built for and hipErrorInvalidConfiguration for a grid too large.
+hipError_t launch_state_f32(KernelParams p, int io_dtype, int dstate, int64_t nseq,
+                            hipStream_t stream, LaunchShape* shape);
+hipError_t launch_state_f16(KernelParams p, int io_dtype, int dstate, int64_t nseq,
+                            hipStream_t stream, LaunchShape* shape);
+hipError_t launch_state_bf16(KernelParams p, int io_dtype, int dstate, int64_t nseq,
+                             hipStream_t stream, LaunchShape* shape);
 
 }  // namespace ssu

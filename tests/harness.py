@@ -38,14 +38,15 @@ def bits(t):
 
 # ------------------------------------------------------------------ GPU side
 
-def gpu_run(w: Workload, heads_per_block=0):
+def gpu_run(w: Workload, heads_per_block=0, loads_per_lane=0, tile_order=0):
     """Run the workload on its device. Returns (out, state_after, state_before);
     the workload's own state tensor is left untouched."""
     state = w.state.clone()
     out = w.out_sentinel()
     common = dict(D=w.D, z=w.z, dt_bias=w.dt_bias, dt_softplus=w.dt_softplus,
                   pad_slot_id=w.pad_slot_id, disable_state_update=w.disable_state_update,
-                  heads_per_block=heads_per_block)
+                  heads_per_block=heads_per_block, loads_per_lane=loads_per_lane,
+                  tile_order=tile_order)
     if w.mode == "one_token":
         ssu.ssu_one_token(state, w.x, w.dt, w.A, w.B, w.C, out,
                           state_batch_indices=w.src, dst_state_batch_indices=w.dst, **common)

@@ -79,7 +79,7 @@ def good_operands(**kw):
         ngroups=2, x=addr(2), B=addr(3), C=addr(4), z=addr(5), out=addr(6),
         io_dtype=_abi.SSU_BF16, dt=addr(7), dt_per_dim=0, A=addr(8), D=addr(9),
         dt_bias=addr(10), dt_softplus=1, pad_slot_id=-1, disable_state_update=0,
-        heads_per_block=0)
+        heads_per_block=0, loads_per_lane=0, tile_order=0)
     for k, v in kw.items():
         setattr(op, k, v)
     return op
@@ -126,6 +126,9 @@ INV, UNS = _abi.SSU_ERR_INVALID_ARGUMENT, _abi.SSU_ERR_UNSUPPORTED
     (dict(dt_per_dim=2), INV, "dt_per_dim"),
     (dict(heads_per_block=3), INV, "heads_per_block"),
     (dict(heads_per_block=8), INV, "heads_per_block"),
+    (dict(loads_per_lane=3), INV, "loads_per_lane"),
+    (dict(loads_per_lane=8), INV, "loads_per_lane"),
+    (dict(tile_order=3), INV, "tile_order"),
     (dict(nheads=12, ngroups=4, heads_per_block=2), INV, "divide"),
     (dict(dstate=256, heads_per_block=4), UNS, "exceeds"),
     (dict(state=0), INV, "state must not be NULL"),
@@ -166,6 +169,7 @@ def test_null_args(lib):
     (dict(rows=-1), INV, "rows"),
     (dict(dst_dtype=9), INV, "dst_dtype"),
     (dict(dstate=100), UNS, "dstate 100"),
+    (dict(heads_per_block=4), UNS, "exceeds"),
     (dict(struct_size=4), INV, "struct_size"),
 ])
 def test_packed_rejects(lib, kw, code, needle):
