@@ -143,6 +143,15 @@ def make_call(w, hpb, lpl=0, order=0):
         return lambda: ssu.ssu_one_token(state, w.x, w.dt, w.A, w.B, w.C, out,
                                          state_batch_indices=w.src,
                                          dst_state_batch_indices=w.dst, **common)
+    if w.meta.get("dense"):
+        nseq = w.cu_seqlens.shape[0] - 1
+        d4 = lambda t: None if t is None else t.view(nseq, -1, *t.shape[1:])
+        x4, dt4, B4, C4, out4 = d4(w.x), d4(w.dt), d4(w.B), d4(w.C), d4(out)
+        common["z"] = d4(w.z)
+        return lambda: ssu.ssu_packed_varlen(state, x4, dt4, w.A, B4, C4, None, out4,
+                                             num_accepted_tokens=w.num_accepted,
+                                             state_batch_indices=w.src_table,
+                                             dst_state_batch_indices=w.dst_table, **common)
     return lambda: ssu.ssu_packed_varlen(state, w.x, w.dt, w.A, w.B, w.C, w.cu_seqlens, out,
                                          num_accepted_tokens=w.num_accepted,
                                          state_batch_indices=w.src_table,
@@ -413,7 +422,8 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for name in ("tiny", "bf16_state", "nemotron_h", "nemotron_h_readonly", "packed_mtp"):
+        for name in ("tiny", "bf16_state", "nemotron_h", "nemotron_h_readonly", "packed_mtp",
+                     "dense_mtp"):
             if name == args.workload:
                 continue
             rec = run_workload(name, max(20, args.steps // 2), max(5, args.warmup // 2),

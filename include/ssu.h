@@ -145,7 +145,11 @@ typedef struct ssu_one_token_args {
 /*
  * ssu_packed_varlen: packed variable-length multi-token decode.
  * Sequence b owns rows [cu_seqlens[b], cu_seqlens[b+1]); an empty range does
- * nothing, a range outside [0, rows] or running backwards is inert. The state
+ * nothing, a range outside [0, rows] or running backwards is inert. With
+ * cu_seqlens NULL and seq_len > 0 the sequences are regular: sequence b owns rows
+ * [b * seq_len, (b + 1) * seq_len) and rows must equal nseq * seq_len -- the dense
+ * [batch, steps, heads, dim] layout, which the MATE page runs as packed varlen
+ * with regular starts (`selective_state_update`, `_dense_seq_starts`). The state
  * chains from token to token of a sequence in fp32 registers, without rounding to
  * the storage dtype in between.
  *   read slot   k = num_accepted[b] (NULL: 1); the slot is
@@ -167,7 +171,8 @@ typedef struct ssu_packed_args {
     ssu_operands op;
     int64_t rows;             /* packed rows (= cu_seqlens[nseq] for valid data), >= 0 */
     int64_t nseq;             /* sequences, >= 0; 0 launches nothing */
-    const void *cu_seqlens;   /* [nseq + 1], required when nseq > 0 */
+    const void *cu_seqlens;   /* [nseq + 1]; or NULL with seq_len > 0 */
+    int64_t seq_len;          /* rows per sequence when cu_seqlens is NULL, else 0 */
     const void *num_accepted; /* [nseq] or NULL */
     int32_t meta_dtype;       /* ssu_index_dtype of cu_seqlens and num_accepted */
     const void *src_table;    /* or NULL */

@@ -72,15 +72,22 @@ def _contig(name, t):
 
 
 def _per_head(name, t, heads):
+    """One fp32 value per head. Besides a [heads] vector this accepts the tied
+    views callers pass for a per-head parameter: [heads, dim, dstate] with both
+    inner strides 0, and [heads, 1] (MATE page, `_per_head`)."""
     if t is None:
         return None
     if t.dtype != torch.float32:
         raise NotImplementedError(f"{name} must be fp32, got {t.dtype}")
+    if t.dim() == 3 and t.shape[0] == heads and t.stride(1) == 0 and t.stride(2) == 0:
+        t = t[:, 0, 0]
+    elif t.dim() == 2 and t.shape == (heads, 1):
+        t = t[:, 0]
     if t.dim() != 1 or t.shape[0] != heads:
         raise NotImplementedError(
-            f"{name} must hold one value per head ([{heads}]), got {tuple(t.shape)}")
-    _contig(name, t)
-    return t
+            f"{name} must hold one value per head ([{heads}] or a tied view), got "
+            f"{tuple(t.shape)} with strides {tuple(t.stride())}")
+    return t.contiguous()
 
 
 def _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus, pad_slot_id,
@@ -203,26 +210,81 @@ def _table(name, t, device, nseq):
     raise ValueError(f"{name} must be [sequences, steps] or flat [rows], got {tuple(t.shape)}")
 
 
-def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens, out=None, *, num_accepted_tokens=None,
-                      state_batch_indices=None, dst_state_batch_indices=None, D=None, z=None,
-                      dt_bias=None, dt_softplus=False, pad_slot_id=-1,
-                      disable_state_update=False, steps=None, heads_per_block=0,
-                      loads_per_lane=0, tile_order=0, stream=None):
-    """Packed variable-length multi-token update. Sequence b owns rows
-    [cu_seqlens[b], cu_seqlens[b+1]). Returns `out` [rows, heads, dim]."""
+def _flatten_dense(name, t, lead, min_dim=4):
+    """[batch, steps, ...] -> [batch * steps, ...] (a view for contiguous input)."""
+    if t is None:
+        return None
+    if t.dim() < min_dim or tuple(t.shape[:2]) != lead:
+        raise ValueError(f"a dense x [{lead[0]}, {lead[1]}, heads, dim] needs {name} in the "
+                         f"same layout, got {tuple(t.shape)}")
+    return t.reshape(lead[0] * lead[1], *t.shape[2:])
+
+
+def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens=None, out=None, *,
+                      num_accepted_tokens=None, state_batch_indices=None,
+                      dst_state_batch_indices=None, D=None, z=None, dt_bias=None,
+                      dt_softplus=False, pad_slot_id=-1, disable_state_update=False,
+                      steps=None, heads_per_block=0, loads_per_lane=0, tile_order=0,
+                      stream=None):
+    """Packed variable-length multi-token update. Returns `out`.
+
+    x is the packed [rows, heads, dim] form, sequence b owning rows
+    [cu_seqlens[b], cu_seqlens[b+1]); or the dense [batch, steps, heads, dim]
+    form (every operand 4-D), which runs as `batch` regular sequences of `steps`
+    rows with no starts tensor. Without cu_seqlens a packed x must have one row
+    per sequence."""
     lib = library()
+    dense_out = None
+    dense_shape = None
+    seq_len = 0
+    if x.dim() == 4:
+        dense_shape = tuple(x.shape)
+        batch, dsteps = x.shape[:2]
+        rows = batch * dsteps
+        if out is not None:
+            if not out.is_contiguous() or out.shape != x.shape:
+                raise ValueError("a dense out must be contiguous and shaped like x")
+            dense_out = out
+            out = out.view(rows, *out.shape[2:])
+        lead = (batch, dsteps)
+        dt = _flatten_dense("dt", dt, lead, min_dim=3)
+        B, C = _flatten_dense("B", B, lead), _flatten_dense("C", C, lead)
+        z = _flatten_dense("z", z, lead)
+        x = x.reshape(rows, *x.shape[2:])
+        if cu_seqlens is None:
+            seq_len = max(dsteps, 1)
     op, out, rows = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
                               pad_slot_id, disable_state_update, heads_per_block,
                               loads_per_lane, tile_order)
     cu, meta = _index("cu_seqlens", cu_seqlens, state.device)
-    if cu is None or cu.dim() != 1 or cu.shape[0] < 1:
-        raise ValueError("cu_seqlens must be a 1-D [sequences + 1] tensor")
-    nseq = cu.shape[0] - 1
     na, na_dt = _index("num_accepted_tokens", num_accepted_tokens, state.device)
+    if cu is not None:
+        if cu.dim() != 1 or cu.shape[0] < 1:
+            raise ValueError("cu_seqlens must be a 1-D [sequences + 1] tensor")
+        nseq = cu.shape[0] - 1
+    elif dense_shape is not None:
+        nseq = dense_shape[0]
+    else:
+        # One row per sequence; count sequences from the per-sequence metadata.
+        if na is not None:
+            nseq = na.shape[0]
+        elif state_batch_indices is not None:
+            nseq = state_batch_indices.shape[0]
+        elif dst_state_batch_indices is not None:
+            nseq = dst_state_batch_indices.shape[0]
+        else:
+            raise ValueError("a packed call needs cu_seqlens, a dense x, or per-sequence "
+                             "metadata (slot tables or num_accepted_tokens)")
+        if nseq != rows:
+            raise ValueError(f"without cu_seqlens, {rows} rows cannot be split across "
+                             f"{nseq} sequences")
+        seq_len = 1
+    if na is not None and cu is None:
+        meta = na_dt
     if na is not None:
         if na.dim() != 1 or na.shape[0] != nseq:
             raise ValueError(f"num_accepted_tokens must be [{nseq}], got {tuple(na.shape)}")
-        if na.dtype != cu.dtype:
+        if cu is not None and na.dtype != cu.dtype:
             raise ValueError("cu_seqlens and num_accepted_tokens must share a dtype")
     src, src_dt, sss, sst, sw = _table("state_batch_indices", state_batch_indices,
                                        state.device, nseq)
@@ -235,11 +297,13 @@ def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens, out=None, *, num_accept
         steps = widths[0] if widths else 1
     args = _abi.PackedArgs(
         struct_size=ctypes.sizeof(_abi.PackedArgs), op=op, rows=rows, nseq=nseq,
-        cu_seqlens=_ptr(cu), num_accepted=_ptr(na), meta_dtype=meta,
+        cu_seqlens=_ptr(cu), seq_len=seq_len, num_accepted=_ptr(na), meta_dtype=meta,
         src_table=_ptr(src), src_dtype=src_dt, src_seq_stride=sss, src_step_stride=sst,
         dst_table=_ptr(dst), dst_dtype=dst_dt, dst_seq_stride=dss, dst_step_stride=dst_st,
         steps=int(steps))
     rc = lib.ssu_packed_varlen(ctypes.byref(args), _stream(state.device, stream))
     if rc != _abi.SSU_OK:
         _raise(lib, rc, "ssu_packed_varlen")
-    return out
+    if dense_out is not None:
+        return dense_out
+    return out.view(dense_shape) if dense_shape is not None else out

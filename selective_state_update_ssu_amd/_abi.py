@@ -38,7 +38,8 @@ class OneTokenArgs(ctypes.Structure):
 class PackedArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", c_uint32), ("op", Operands), ("rows", c_int64), ("nseq", c_int64),
-        ("cu_seqlens", c_void_p), ("num_accepted", c_void_p), ("meta_dtype", c_int32),
+        ("cu_seqlens", c_void_p), ("seq_len", c_int64),
+        ("num_accepted", c_void_p), ("meta_dtype", c_int32),
         ("src_table", c_void_p), ("src_dtype", c_int32),
         ("src_seq_stride", c_int64), ("src_step_stride", c_int64),
         ("dst_table", c_void_p), ("dst_dtype", c_int32),

@@ -256,8 +256,12 @@ int ssu_packed_varlen(const ssu_packed_args* a, void* stream) {
                     a->struct_size, sizeof(ssu_packed_args));
     if (a->rows < 0 || a->nseq < 0)
         return fail(SSU_ERR_INVALID_ARGUMENT, "rows and nseq must be >= 0");
-    if (a->nseq > 0 && !a->cu_seqlens)
-        return fail(SSU_ERR_INVALID_ARGUMENT, "cu_seqlens must not be NULL when nseq > 0");
+    if (a->seq_len < 0) return fail(SSU_ERR_INVALID_ARGUMENT, "seq_len must be >= 0");
+    if (a->cu_seqlens && a->seq_len)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "pass either cu_seqlens or seq_len, not both");
+    if (a->nseq > 0 && !a->cu_seqlens && !a->seq_len)
+        return fail(SSU_ERR_INVALID_ARGUMENT,
+                    "cu_seqlens must not be NULL when nseq > 0 (or give seq_len)");
     if ((a->cu_seqlens || a->num_accepted) && !is_index(a->meta_dtype))
         return fail(SSU_ERR_INVALID_ARGUMENT, "meta_dtype %d is not an ssu_index_dtype", a->meta_dtype);
     if (a->num_accepted && !a->src_table)
@@ -276,12 +280,16 @@ int ssu_packed_varlen(const ssu_packed_args* a, void* stream) {
     const bool work = a->nseq > 0 && a->rows > 0;
     if (int rc = check_operands(op, a->rows, work, true)) return rc;
     if (!work) return ok();
+    if (!a->cu_seqlens && a->nseq * a->seq_len != a->rows)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "rows (%lld) must equal nseq * seq_len (%lld * %lld)",
+                    (long long)a->rows, (long long)a->nseq, (long long)a->seq_len);
 
     ssu::KernelParams k{};
     fill_common(k, op, true);
     k.src = a->src_table;
     k.dst = a->dst_table;
     k.cu = a->cu_seqlens;
+    k.seq_len = a->seq_len;
     k.na = a->num_accepted;
     k.src_seq_stride = a->src_seq_stride;
     k.src_step_stride = a->src_step_stride;

@@ -246,10 +246,15 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
     // ---- slot resolution (uniform across the workgroup)
     int64_t begin, len, r;
     if constexpr (PACKED) {
-        const int64_t b0 = load_index(p.cu, p.meta_i64, seq);
-        const int64_t b1 = load_index(p.cu, p.meta_i64, seq + 1);
-        begin = uniform64(b0);
-        len = uniform64(b1 - b0);
+        if (p.cu) {
+            const int64_t b0 = load_index(p.cu, p.meta_i64, seq);
+            const int64_t b1 = load_index(p.cu, p.meta_i64, seq + 1);
+            begin = uniform64(b0);
+            len = uniform64(b1 - b0);
+        } else {
+            begin = seq * p.seq_len;
+            len = p.seq_len;
+        }
         if (begin < 0 || begin + len > p.rows || len <= 0) return;
         if (p.src) {
             const int64_t k = uniform64(p.na ? load_index(p.na, p.meta_i64, seq) : 1);

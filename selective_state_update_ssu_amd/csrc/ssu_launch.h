@@ -38,11 +38,12 @@ struct KernelParams {
     // Slot resolution.
     const void* src;    // one-token: [batch] vector; packed: table; may be null
     const void* dst;    // may be null
-    const void* cu;     // packed only
+    const void* cu;     // packed only; null: regular sequences of seq_len rows
     const void* na;     // packed only, may be null
     int64_t src_seq_stride, src_step_stride;
     int64_t dst_seq_stride, dst_step_stride;
     int64_t steps;
+    int64_t seq_len;
     int64_t nslots;
     int64_t pad_slot_id;
     int64_t rows;

@@ -27,6 +27,8 @@ Named workloads (one GPU each, at their real decode shapes):
               a [256, 4] table of distinct slots serves as both the read and the
               write table; the acceptance count ~ U{1..len} picks the read entry;
               5 % of sequences have an all-pad table row.
+  dense_mtp   the Mamba2-2.7B shape in the dense [256, 2, ...] layout (one draft
+              token per sequence), slot table [256, 2] of 1024 slots, 5 % pads.
 """
 from __future__ import annotations
 
@@ -177,11 +179,14 @@ def one_token(name, seed, *, batch, H, P, N, G, nslots, device, state_dtype="f32
 
 def packed(name, seed, *, nseq, max_len, H, P, N, G, nslots, device, state_dtype="f32",
            io="bf16", with_z=True, pad_fraction=0.0, meta_dtype="i32",
-           index_dtype="i32", lengths=None, accepted=True, **kw) -> Workload:
+           index_dtype="i32", lengths=None, accepted=True, dense=False, **kw) -> Workload:
     """A packed MTP batch: lengths ~ U{1..max_len} (or given), a [nseq, max_len]
     table of distinct slots used as both read and write table, acceptance counts
     ~ U{1..len}, and round(pad_fraction * nseq) sequences whose table row is all
-    pad (-1)."""
+    pad (-1). dense=True: every sequence has max_len rows and the call is meant to
+    be made in the dense [nseq, max_len, ...] layout (meta["dense"])."""
+    if dense:
+        lengths = [max_len] * nseq
     if lengths is None:
         lengths = torch.randint(1, max_len + 1, (nseq,),
                                 generator=_generator(seed, "lengths", "cpu"))
@@ -209,7 +214,7 @@ def packed(name, seed, *, nseq, max_len, H, P, N, G, nslots, device, state_dtype
     return Workload(name=name, mode="packed", state=state, cu_seqlens=cu.to(mdt).to(device),
                     num_accepted=num_acc, src_table=table, dst_table=table,
                     meta=dict(seed=seed, state_dtype=state_dtype, io=io,
-                              lengths=lengths.tolist()), **ops)
+                              lengths=lengths.tolist(), dense=dense), **ops)
 
 
 # The five named decode workloads. `seed` defaults to the workload's ordinal.
@@ -241,6 +246,14 @@ def nemotron_h(device, seed=3, disable_state_update=False):
     return w
 
 
+def dense_mtp(device, seed=5):
+    """Mamba2-2.7B-shaped MTP decode in the dense [batch, steps] layout: 256
+    sequences of 2 tokens (one draft), no starts tensor."""
+    return packed("dense_mtp", seed, nseq=256, max_len=2, H=80, P=64, N=128, G=1,
+                  nslots=1024, device=device, state_dtype="f32", io="bf16",
+                  with_z=True, pad_fraction=0.05, dense=True)
+
+
 def packed_mtp(device, seed=4):
     return packed("packed_mtp", seed, nseq=256, max_len=4, H=80, P=64, N=128, G=1,
                   nslots=2048, device=device, state_dtype="f32", io="bf16",
@@ -254,4 +267,5 @@ NAMED = {
     "nemotron_h": nemotron_h,
     "nemotron_h_readonly": lambda device, seed=3: nemotron_h(device, seed, True),
     "packed_mtp": packed_mtp,
+    "dense_mtp": dense_mtp,
 }

@@ -50,6 +50,16 @@ def gpu_run(w: Workload, heads_per_block=0, loads_per_lane=0, tile_order=0):
     if w.mode == "one_token":
         ssu.ssu_one_token(state, w.x, w.dt, w.A, w.B, w.C, out,
                           state_batch_indices=w.src, dst_state_batch_indices=w.dst, **common)
+    elif w.meta.get("dense"):
+        # The dense [batch, steps, ...] layout: every operand 4-D, no starts tensor.
+        nseq = w.cu_seqlens.shape[0] - 1
+        d4 = lambda t: None if t is None else t.view(nseq, -1, *t.shape[1:])
+        ret = ssu.ssu_packed_varlen(state, d4(w.x), d4(w.dt), w.A, d4(w.B), d4(w.C), None,
+                                    d4(out), num_accepted_tokens=w.num_accepted,
+                                    state_batch_indices=w.src_table,
+                                    dst_state_batch_indices=w.dst_table,
+                                    **dict(common, z=d4(w.z)))
+        assert ret.data_ptr() == out.data_ptr() and ret.dim() == 4
     else:
         ssu.ssu_packed_varlen(state, w.x, w.dt, w.A, w.B, w.C, w.cu_seqlens, out,
                               num_accepted_tokens=w.num_accepted,

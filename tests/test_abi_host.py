@@ -162,6 +162,9 @@ def test_null_args(lib):
 @pytest.mark.parametrize("kw,code,needle", [
     (dict(src_table=None), INV, "src_table is required"),
     (dict(cu_seqlens=None), INV, "cu_seqlens must not be NULL"),
+    (dict(seq_len=2), INV, "either cu_seqlens or seq_len"),
+    (dict(cu_seqlens=None, seq_len=3), INV, "nseq * seq_len"),
+    (dict(seq_len=-1), INV, "seq_len"),
     (dict(meta_dtype=3), INV, "meta_dtype"),
     (dict(steps=0), INV, "steps"),
     (dict(src_seq_stride=-1), INV, "strides"),

@@ -259,3 +259,52 @@ def test_empty_calls_launch_nothing():
     ssu.ssu_packed_varlen(p.state, x, p.dt[:0], p.A, p.B[:0], p.C[:0], cu, D=p.D,
                           z=p.z[:0], dt_bias=p.dt_bias)
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ dense layout
+
+@pytest.mark.parametrize("case", [
+    dict(state_dtype="f32", io="bf16", N=128, P=64, H=8, G=2),
+    dict(state_dtype="bf16", io="f16", N=64, P=80, H=4, G=1, accepted=False),
+], ids=_case_id)
+def test_dense_layout(case):
+    """[batch, steps, heads, dim] operands run as regular sequences (no starts
+    tensor): equal to the oracle given the regular starts, and bit-identical to
+    the packed call with an explicit cu_seqlens."""
+    w = wl.packed("dense", 707, nseq=6, max_len=3, nslots=24, device=DEV, dense=True,
+                  pad_fraction=0.2, **case)
+    out, after, before = hz.gpu_run(w)
+    compare_full("dense", w, out, after, before, hz.oracle_full(w))
+    w.meta["dense"] = False
+    out2, after2, _ = hz.gpu_run(w)
+    assert torch.equal(hz.bits(out), hz.bits(out2))
+    assert torch.equal(hz.bits(after), hz.bits(after2))
+
+
+def test_packed_one_row_per_sequence_without_starts():
+    """Without cu_seqlens a packed x holds one row per sequence."""
+    import selective_state_update_ssu_amd as ssu
+    w = wl.packed("onerow", 808, nseq=7, max_len=2, H=4, P=64, N=64, G=1, nslots=16,
+                  device=DEV, lengths=[1] * 7, pad_fraction=0.15)
+    ref = hz.oracle_full(w)
+    state = w.state.clone()
+    out = w.out_sentinel()
+    ssu.ssu_packed_varlen(state, w.x, w.dt, w.A, w.B, w.C, None, out, D=w.D, z=w.z,
+                          dt_bias=w.dt_bias, dt_softplus=True,
+                          num_accepted_tokens=w.num_accepted, state_batch_indices=w.src_table,
+                          dst_state_batch_indices=w.dst_table)
+    torch.cuda.synchronize()
+    compare_full("onerow", w, out, state, w.state, ref)
+
+
+def test_tied_parameter_views_bit_identical():
+    """Per-head A/D/dt_bias given as tied stride-0 [heads, dim, dstate] views or
+    [heads, 1] columns give the same bits as [heads] vectors."""
+    w = wl.one_token("tied", 909, batch=5, H=4, P=64, N=128, G=1, nslots=12, device=DEV)
+    o1, s1, _ = hz.gpu_run(w)
+    H, P, N = 4, 64, 128
+    w.A = w.A[:, None, None].expand(H, P, N)
+    w.dt_bias = w.dt_bias[:, None, None].expand(H, P, N)
+    w.D = w.D[:, None].contiguous()
+    o2, s2, _ = hz.gpu_run(w)
+    assert torch.equal(hz.bits(o1), hz.bits(o2)) and torch.equal(hz.bits(s1), hz.bits(s2))
