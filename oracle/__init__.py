@@ -79,6 +79,12 @@ class Oracle:
             _ip, _ip, _ip, _i64, _i64, _ip, _i64, _i64, _i64,
             _dp, _dp, _int, _dp, _dp, _dp, _dp, _dp, _dp, _int,
             _i64, _int, _dp]
+        for f in (lib.oracle_ring_update, lib.oracle_ring_commit):
+            f.restype = _int
+        lib.oracle_ring_update.argtypes = [_ip, _ip, _ip, _i64, _ip, _i64, _i64, _int, _i64,
+                                           _i64, _i64]
+        lib.oracle_ring_commit.argtypes = [_ip, _ip, _ip, _i64, _ip, _i64, _i64, _ip, _ip,
+                                           _i64, _i64, _i64]
         self.lib = lib
 
     @staticmethod
@@ -158,6 +164,65 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_ssu_packed_varlen rejected its arguments")
         return Result(out, state_out)
+
+
+@dataclass
+class Rings:
+    ring_start: np.ndarray
+    prev_num_accepted: np.ndarray
+    prev_query_len: np.ndarray
+
+
+def _rings(ring_start, prev_num_accepted, prev_query_len):
+    return Rings(*(_idx(a).copy() for a in (ring_start, prev_num_accepted, prev_query_len)))
+
+
+def _ring_slots(slots, slot_stride):
+    s = _idx(slots).reshape(-1)
+    if slot_stride is None:
+        slot_stride = 1
+    n = (s.shape[0] - 1) // slot_stride + 1 if s.shape[0] else 0
+    return s, int(slot_stride), n
+
+
+def _ring_update(self, ring_start, prev_num_accepted, prev_query_len, slots, *,
+                 logical_window=None, ring_buffer_len=None, pad_slot_id=-1,
+                 slot_stride=None, n=None) -> Rings:
+    """Reset (logical_window None) or advance the trackers of the named slots.
+    Returns updated copies; num_states is the shortest tracker's length."""
+    r = _rings(ring_start, prev_num_accepted, prev_query_len)
+    s, stride, n_all = _ring_slots(slots, slot_stride)
+    n = n_all if n is None else n
+    num_states = min(a.shape[0] for a in (r.ring_start, r.prev_num_accepted, r.prev_query_len))
+    reset = logical_window is None
+    rc = self.lib.oracle_ring_update(
+        _p(r.ring_start, _ip), _p(r.prev_num_accepted, _ip), _p(r.prev_query_len, _ip),
+        num_states, _p(s, _ip), stride, n, int(reset), 0 if reset else int(logical_window),
+        1 if reset else int(ring_buffer_len), int(pad_slot_id))
+    if rc != 0:
+        raise ValueError("oracle_ring_update rejected its arguments")
+    return r
+
+
+def _ring_commit(self, ring_start, prev_num_accepted, prev_query_len, slots, num_accepted,
+                 query_start_loc, *, logical_window, ring_buffer_len, pad_slot_id=-1,
+                 slot_stride=None, n=None) -> Rings:
+    r = _rings(ring_start, prev_num_accepted, prev_query_len)
+    s, stride, n_all = _ring_slots(slots, slot_stride)
+    n = n_all if n is None else n
+    num_states = min(a.shape[0] for a in (r.ring_start, r.prev_num_accepted, r.prev_query_len))
+    na, qsl = _idx(num_accepted), _idx(query_start_loc)
+    rc = self.lib.oracle_ring_commit(
+        _p(r.ring_start, _ip), _p(r.prev_num_accepted, _ip), _p(r.prev_query_len, _ip),
+        num_states, _p(s, _ip), stride, n, _p(na, _ip), _p(qsl, _ip), int(logical_window),
+        int(ring_buffer_len), int(pad_slot_id))
+    if rc != 0:
+        raise ValueError("oracle_ring_commit rejected its arguments")
+    return r
+
+
+Oracle.ring_update = _ring_update
+Oracle.ring_commit = _ring_commit
 
 
 _DEFAULT: Oracle | None = None

@@ -42,6 +42,10 @@
  *    position * step_stride.
  *  - The dense [batch, steps, ...] form is the packed form with regular starts
  *    (`selective_state_update` body), so it needs no function of its own here.
+ *  - ReplaySSM ring trackers: the update / reset and the delayed commit of the
+ *    vLLM `ssu_dispatch` module source (the two tracker kernels and their
+ *    wrappers `update_replayssm_ring_trackers` and
+ *    `commit_replayssm_ring_trackers`), restated per slot below.
  */
 #include "ssu_oracle.h"
 
@@ -205,5 +209,83 @@ int oracle_ssu_packed_varlen(
         }
     }
     free(s);
+    return 0;
+}
+
+/*
+ * ReplaySSM ring trackers. Per named slot s:
+ *  reset:   ring_start = prev_num_accepted = prev_query_len = 0.
+ *  advance: one more token was decoded since the checkpoint. If that makes the
+ *           count exceed the logical window, the ring start moves past the
+ *           tokens counted so far (mod the ring length) and the count restarts
+ *           at 1; otherwise the count grows by one. prev_query_len is left alone.
+ *  commit:  the previous speculative window (prev_query_len tokens, 0 = none)
+ *           is settled with the count accepted from it. When a window exists and
+ *           the tokens counted since the checkpoint plus that window would exceed
+ *           the logical window, the ring start moves past the counted tokens and
+ *           the count becomes the accepted number; otherwise the accepted number
+ *           is added to the count. With no window the count becomes 0. Then the
+ *           current window's length is recorded.
+ */
+static int ring_args_ok(const int64_t *a, const int64_t *b, const int64_t *c,
+                        int64_t num_states, const int64_t *slots, int64_t n) {
+    if (n < 0 || num_states < 0) return 0;
+    if (n > 0 && (!slots || !a || !b || !c)) return 0;
+    return 1;
+}
+
+int oracle_ring_update(int64_t *ring_start, int64_t *prev_num_accepted,
+                       int64_t *prev_query_len, int64_t num_states,
+                       const int64_t *slots, int64_t slot_stride, int64_t n,
+                       int reset, int64_t logical_window,
+                       int64_t ring_buffer_len, int64_t pad_slot_id) {
+    if (!ring_args_ok(ring_start, prev_num_accepted, prev_query_len, num_states, slots, n))
+        return -1;
+    if (!reset && ring_buffer_len < 1) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t s = slots[i * slot_stride];
+        if (!slot_valid(s, pad_slot_id, num_states)) continue;
+        if (reset) {
+            ring_start[s] = 0;
+            prev_num_accepted[s] = 0;
+            prev_query_len[s] = 0;
+            continue;
+        }
+        const int64_t counted = prev_num_accepted[s];
+        if (counted + 1 > logical_window) {
+            ring_start[s] = (ring_start[s] + counted) % ring_buffer_len;
+            prev_num_accepted[s] = 1;
+        } else {
+            prev_num_accepted[s] = counted + 1;
+        }
+    }
+    return 0;
+}
+
+int oracle_ring_commit(int64_t *ring_start, int64_t *prev_num_accepted,
+                       int64_t *prev_query_len, int64_t num_states,
+                       const int64_t *slots, int64_t slot_stride, int64_t n,
+                       const int64_t *num_accepted, const int64_t *query_start_loc,
+                       int64_t logical_window, int64_t ring_buffer_len,
+                       int64_t pad_slot_id) {
+    if (!ring_args_ok(ring_start, prev_num_accepted, prev_query_len, num_states, slots, n))
+        return -1;
+    if (ring_buffer_len < 1 || (n > 0 && (!num_accepted || !query_start_loc))) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t s = slots[i * slot_stride];
+        if (!slot_valid(s, pad_slot_id, num_states)) continue;
+        const int64_t counted = prev_num_accepted[s];
+        const int64_t window = prev_query_len[s];
+        const int64_t accepted = num_accepted[i];
+        if (window == 0) {
+            prev_num_accepted[s] = 0;
+        } else if (counted + window > logical_window) {
+            ring_start[s] = (ring_start[s] + counted) % ring_buffer_len;
+            prev_num_accepted[s] = accepted;
+        } else {
+            prev_num_accepted[s] = counted + accepted;
+        }
+        prev_query_len[s] = query_start_loc[i + 1] - query_start_loc[i];
+    }
     return 0;
 }

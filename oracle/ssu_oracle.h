@@ -59,6 +59,33 @@ int oracle_ssu_packed_varlen(
     const double *z, const double *dt_bias, int dt_softplus,
     int64_t pad_slot_id, int disable_state_update, double *out);
 
+/*
+ * ReplaySSM ring trackers: three per-slot counters (ring_start,
+ * prev_num_accepted, prev_query_len), int64 here, [num_states] each. Position i
+ * < n names slot slots[i * slot_stride]; an invalid slot (pad or outside
+ * [0, num_states)) is skipped. Slots of valid positions are assumed distinct.
+ *
+ * ring_update with reset != 0 zeroes the three counters of every named slot;
+ * otherwise it advances each named slot's ring by one decoded token.
+ * ring_commit advances each named slot by the accepted prefix of the previous
+ * speculative window (num_accepted[i]) and records the current window's length
+ * (query_start_loc[i + 1] - query_start_loc[i]).
+ * Return value: 0, or -1 for inconsistent arguments (negative sizes, a ring of
+ * fewer than one entry, a null array that is needed).
+ */
+int oracle_ring_update(int64_t *ring_start, int64_t *prev_num_accepted,
+                       int64_t *prev_query_len, int64_t num_states,
+                       const int64_t *slots, int64_t slot_stride, int64_t n,
+                       int reset, int64_t logical_window,
+                       int64_t ring_buffer_len, int64_t pad_slot_id);
+
+int oracle_ring_commit(int64_t *ring_start, int64_t *prev_num_accepted,
+                       int64_t *prev_query_len, int64_t num_states,
+                       const int64_t *slots, int64_t slot_stride, int64_t n,
+                       const int64_t *num_accepted, const int64_t *query_start_loc,
+                       int64_t logical_window, int64_t ring_buffer_len,
+                       int64_t pad_slot_id);
+
 #ifdef __cplusplus
 }
 #endif

@@ -402,4 +402,87 @@ def pin_page_examples(orc):
         assert changed == written, (changed, written)
 
 
+# -------------------------------------------------------------- ring trackers
+# The ReplaySSM tracker update / reset and the delayed commit of the vLLM
+# `ssu_dispatch` module (its two tracker kernels). Expected values are worked
+# by hand from that definition, or closed forms of repeated application.
+
+def _zeros(n):
+    return np.zeros(n, dtype=np.int64)
+
+
+def pin_ring_reset_and_masks(orc):
+    """Reset zeroes all three counters of every named valid slot and nothing
+    else; pad and out-of-range slots are skipped by update and commit alike; a
+    2-D table is addressed through its stride (first column)."""
+    rs, pn, pq = np.arange(10, 16), np.arange(20, 26), np.arange(30, 36)
+    r = orc.ring_update(rs, pn, pq, [4, -1, 1, 6, 99])
+    assert r.ring_start.tolist() == [10, 0, 12, 13, 0, 15]
+    assert r.prev_num_accepted.tolist() == [20, 0, 22, 23, 0, 25]
+    assert r.prev_query_len.tolist() == [30, 0, 32, 33, 0, 35]
+    # A [3, 2] table: entries 0, 2, 4 are the first column.
+    table = np.array([[2, 5], [-1, 0], [3, 1]])
+    r = orc.ring_update(rs, pn, pq, table, slot_stride=2)
+    assert r.ring_start.tolist() == [10, 11, 0, 0, 14, 15]
+    a = orc.ring_update(_zeros(4), _zeros(4), _zeros(4), [-1, 7], logical_window=2,
+                        ring_buffer_len=4)
+    assert a.prev_num_accepted.tolist() == [0, 0, 0, 0]
+    c = orc.ring_commit([1, 1, 1, 1], [1, 1, 1, 1], [1, 1, 1, 1], [-1, 9], [3, 3], [0, 2, 5],
+                        logical_window=2, ring_buffer_len=4)
+    assert c.ring_start.tolist() == [1, 1, 1, 1] and c.prev_query_len.tolist() == [1, 1, 1, 1]
+
+
+def pin_ring_advance_closed_form(orc):
+    """After a reset and K advances with window W >= 1 and ring length R: the
+    ring was checkpointed c = floor((K-1)/W) times, each time moving past W
+    tokens, so start = (c W) mod R and the count is K - c W. With W = 0 every
+    advance checkpoints: start = (K-1) mod R, count 1."""
+    for W, R in ((1, 4), (3, 8), (5, 7), (0, 5)):
+        r = orc.ring_update(_zeros(3), _zeros(3), _zeros(3), [2])
+        for K in range(1, 21):
+            r = orc.ring_update(r.ring_start, r.prev_num_accepted, r.prev_query_len, [2],
+                                logical_window=W, ring_buffer_len=R)
+            if W == 0:
+                want = ((K - 1) % R, 1)
+            else:
+                c = (K - 1) // W
+                want = ((c * W) % R, K - c * W)
+            got = (int(r.ring_start[2]), int(r.prev_num_accepted[2]))
+            assert got == want, (W, R, K, got, want)
+            assert r.prev_query_len[2] == 0
+
+
+def pin_ring_commit_cases(orc):
+    """One commit over four slots, each worked by hand (window 6, ring 8):
+      slot 0: no previous window (0)     -> count 0, start kept;
+      slot 1: 2 counted + window 3 <= 6  -> count 2 + 4 = 6, start kept;
+      slot 2: 4 counted + window 3 > 6   -> start 1 + 4 = 5, count = accepted 2;
+      slot 3: 5 counted + window 2 > 6   -> start (6 + 5) mod 8 = 3, count 1.
+    Each records its current window length from the query starts."""
+    rs = [7, 3, 1, 6]
+    pn = [9, 2, 4, 5]
+    pq = [0, 3, 3, 2]
+    slots = [0, 1, 2, 3]
+    acc = [5, 4, 2, 1]
+    qsl = [0, 2, 5, 9, 10]
+    c = orc.ring_commit(rs, pn, pq, slots, acc, qsl, logical_window=6, ring_buffer_len=8)
+    assert c.ring_start.tolist() == [7, 3, 5, 3], c
+    assert c.prev_num_accepted.tolist() == [0, 6, 2, 1], c
+    assert c.prev_query_len.tolist() == [2, 3, 4, 1], c
+
+
+def pin_ring_commit_sequence(orc):
+    """An MTP run on one slot, window 4, ring 16, every query 3 tokens long,
+    accepted counts 2, 3, 1, 3, 2 after the first (worked by hand):
+    (start, count, window) = (0,0,3) (0,2,3) (2,3,3) (5,1,3) (5,4,3) (9,2,3)."""
+    z = _zeros(1)
+    r = orc.ring_update(z + 7, z + 7, z + 7, [0])
+    want = [(0, 0, 3), (0, 2, 3), (2, 3, 3), (5, 1, 3), (5, 4, 3), (9, 2, 3)]
+    for step, acc in enumerate([0, 2, 3, 1, 3, 2]):
+        r = orc.ring_commit(r.ring_start, r.prev_num_accepted, r.prev_query_len, [0], [acc],
+                            [0, 3], logical_window=4, ring_buffer_len=16)
+        got = (int(r.ring_start[0]), int(r.prev_num_accepted[0]), int(r.prev_query_len[0]))
+        assert got == want[step], (step, got, want[step])
+
+
 ALL = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

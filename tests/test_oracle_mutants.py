@@ -49,6 +49,19 @@ MUTANTS = [
      "memcpy(s, state_in + r * slot_elems, (size_t)slot_elems * sizeof(double));\n            step_token(&pb, s, begin + t, out);"),
     ("valid_upper_bound", "slot >= 0 && slot < nslots", "slot >= 0 && slot <= nslots - 2"),
     ("pad_id_ignored", "return slot != pad_slot_id && slot >= 0", "return slot >= 0"),
+    ("ring_window_off_by_one", "if (counted + 1 > logical_window) {", "if (counted + 1 >= logical_window) {"),
+    ("ring_no_modulo", "ring_start[s] = (ring_start[s] + counted) % ring_buffer_len;\n            prev_num_accepted[s] = 1;",
+     "ring_start[s] = ring_start[s] + counted;\n            prev_num_accepted[s] = 1;"),
+    ("ring_restart_at_zero", "prev_num_accepted[s] = 1;", "prev_num_accepted[s] = 0;"),
+    ("ring_reset_keeps_query_len", "            prev_query_len[s] = 0;\n            continue;", "            continue;"),
+    ("commit_no_window_keeps_count", "if (window == 0) {\n            prev_num_accepted[s] = 0;", "if (window == 0) {\n            prev_num_accepted[s] = counted;"),
+    ("commit_tests_accepted", "} else if (counted + window > logical_window) {", "} else if (counted + accepted > logical_window) {"),
+    ("commit_checkpoint_keeps_count", "            prev_num_accepted[s] = accepted;\n        } else {", "            prev_num_accepted[s] = counted;\n        } else {"),
+    ("commit_start_by_window", "ring_start[s] = (ring_start[s] + counted) % ring_buffer_len;\n            prev_num_accepted[s] = accepted;",
+     "ring_start[s] = (ring_start[s] + window) % ring_buffer_len;\n            prev_num_accepted[s] = accepted;"),
+    ("commit_window_from_accepted", "prev_query_len[s] = query_start_loc[i + 1] - query_start_loc[i];", "prev_query_len[s] = num_accepted[i];"),
+    ("ring_position_not_strided", "const int64_t s = slots[i * slot_stride];\n        if (!slot_valid(s, pad_slot_id, num_states)) continue;\n        if (reset)",
+     "const int64_t s = slots[i];\n        if (!slot_valid(s, pad_slot_id, num_states)) continue;\n        if (reset)"),
 ]
 
 
