@@ -227,6 +227,29 @@ def traffic_for(workload, kernel_ms):
     return entry.get("hbm_bytes_per_launch")
 
 
+def ring_tracker_times(steps=200):
+    """Launch time of the ReplaySSM ring-tracker advance and commit kernels for a
+    decode batch (256 slots) and a large one (65536), int32 counters."""
+    import torch
+    import selective_state_update_ssu_amd as ssu
+
+    out = {}
+    for n in (256, 65536):
+        num_states = 2 * n
+        g = torch.Generator(device="cuda")
+        g.manual_seed(n)
+        trk = [torch.zeros(num_states, dtype=torch.int32, device="cuda") for _ in range(3)]
+        slots = torch.randperm(num_states, generator=g, device="cuda")[:n].to(torch.int32)
+        acc = torch.ones(n, dtype=torch.int32, device="cuda")
+        qsl = torch.arange(0, 2 * n + 1, 2, dtype=torch.int32, device="cuda")
+        _, adv = time_calls(lambda: ssu.update_replayssm_ring_trackers(
+            *trk, slots, logical_window=8, ring_buffer_len=64), steps, 10)
+        _, com = time_calls(lambda: ssu.commit_replayssm_ring_trackers(
+            *trk, slots, acc, qsl, 8, 64), steps, 10)
+        out[f"n{n}"] = {"advance_us": adv * 1e3, "commit_us": com * 1e3}
+    return out
+
+
 # ------------------------------------------------------------------ CPU leg
 
 def cpu_baseline(seconds):
@@ -434,6 +457,8 @@ def main():
                   file=sys.stderr, flush=True)
     ceil = ceilings()
     copy_gbps = ceil["copy"]
+    rings = ring_tracker_times()
+    print(f"[bench] ring trackers: {json.dumps(rings)}", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     kernel_ms = head["kernel_us"] * 1e-3
@@ -468,6 +493,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "workloads": extra,
+        "ring_trackers": rings,
     }
     print(json.dumps(line))
 

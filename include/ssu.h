@@ -184,6 +184,55 @@ typedef struct ssu_packed_args {
     int64_t steps;            /* table width; >= 1 when a table is given */
 } ssu_packed_args;
 
+/*
+ * ReplaySSM ring trackers: three per-slot counters kept beside the state cache
+ * when decode replays a ring of cached inputs from a checkpointed state
+ * (ring_start, prev_num_accepted, prev_query_len). The update and the delayed
+ * commit follow the two tracker kernels of the vLLM `ssu_dispatch` module source
+ * (`update_replayssm_ring_trackers`, `commit_replayssm_ring_trackers`).
+ *
+ * Position i < n names slot slots[i * slot_stride] (a 2-D [n, w] slot table is
+ * passed with slot_stride w: its first column). Positions whose slot is pad or
+ * outside [0, num_states) are skipped. Per named slot:
+ *   ssu_ring_update, reset != 0: all three counters become 0;
+ *   ssu_ring_update, reset == 0: one token decoded -- when prev_num_accepted + 1
+ *     exceeds logical_window, ring_start advances by prev_num_accepted (mod
+ *     ring_buffer_len) and prev_num_accepted becomes 1, else it grows by 1;
+ *   ssu_ring_commit: settles the previous speculative window. With
+ *     prev_query_len 0 (none), prev_num_accepted becomes 0. Otherwise, when
+ *     prev_num_accepted + prev_query_len exceeds logical_window, ring_start
+ *     advances by prev_num_accepted (mod ring_buffer_len) and prev_num_accepted
+ *     becomes num_accepted[i]; else num_accepted[i] is added to it. Then
+ *     prev_query_len = query_start_loc[i + 1] - query_start_loc[i].
+ * Slots named at valid positions must be distinct. One launch, no allocation,
+ * no synchronisation; n == 0 launches nothing.
+ */
+typedef struct ssu_ring_args {
+    uint32_t struct_size;          /* sizeof(ssu_ring_args) */
+    void *ring_start;              /* [num_states] */
+    void *prev_num_accepted;       /* [num_states] */
+    void *prev_query_len;          /* [num_states] */
+    int32_t tracker_dtype;         /* ssu_index_dtype of the three counters */
+    int64_t num_states;            /* >= 0 */
+    const void *slots;             /* n entries, slot_stride apart */
+    int32_t slot_dtype;            /* ssu_index_dtype */
+    int64_t slot_stride;           /* >= 0, in entries */
+    int64_t n;                     /* positions, >= 0 */
+    const void *num_accepted;      /* commit: [n] */
+    const void *query_start_loc;   /* commit: [n + 1] */
+    int32_t meta_dtype;            /* commit: ssu_index_dtype of the two above */
+    int32_t reset;                 /* update: nonzero resets */
+    int64_t logical_window;        /* >= 0 (advance, commit) */
+    int64_t ring_buffer_len;       /* >= 1 (advance, commit) */
+    int64_t pad_slot_id;
+} ssu_ring_args;
+
+/* Reset or advance the trackers of the named slots. Returns an ssu_status. */
+int ssu_ring_update(const ssu_ring_args *args, void *stream);
+
+/* Commit the previous speculative window of the named slots. Returns an ssu_status. */
+int ssu_ring_commit(const ssu_ring_args *args, void *stream);
+
 /* Run the one-token update on `stream`. Returns an ssu_status. */
 int ssu_one_token(const ssu_one_token_args *args, void *stream);
 

@@ -27,7 +27,9 @@ import torch
 
 from . import _abi
 
-__all__ = ["ssu_one_token", "ssu_packed_varlen", "library_path", "library"]
+__all__ = ["ssu_one_token", "ssu_packed_varlen", "update_replayssm_ring_trackers",
+           "reset_replayssm_ring_trackers", "commit_replayssm_ring_trackers", "library_path",
+           "library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBRARY = os.path.join(_HERE, "_lib", "libssu_amd.so")
@@ -307,3 +309,82 @@ def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens=None, out=None, *,
     if dense_out is not None:
         return dense_out
     return out.view(dense_shape) if dense_shape is not None else out
+
+
+# ------------------------------------------------------------ ring trackers
+
+def _ring_args(ring_start, prev_num_accepted, prev_query_len, state_batch_indices, pad_slot_id):
+    trackers = (ring_start, prev_num_accepted, prev_query_len)
+    dtypes = {t.dtype for t in trackers}
+    if len(dtypes) != 1 or next(iter(dtypes)) not in _INDEX_DTYPES:
+        raise ValueError("ring_start, prev_num_accepted and prev_query_len must share an "
+                         f"int32 or int64 dtype, got {[t.dtype for t in trackers]}")
+    device = ring_start.device
+    if device.type != "cuda":
+        raise ValueError(f"ring trackers must be on a GPU, got {device}")
+    for name, t in zip(("ring_start", "prev_num_accepted", "prev_query_len"), trackers):
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, ring_start on {device}")
+        _contig(name, t)
+    slots, slot_dt = _index("state_batch_indices", state_batch_indices, device)
+    if slots.dim() == 2:
+        stride = slots.stride(0)          # the first column of a slot table
+    elif slots.dim() == 1:
+        stride = slots.stride(0)
+    else:
+        raise ValueError("state_batch_indices must be [n] or [n, steps]")
+    return _abi.RingArgs(
+        struct_size=ctypes.sizeof(_abi.RingArgs), ring_start=_ptr(ring_start),
+        prev_num_accepted=_ptr(prev_num_accepted), prev_query_len=_ptr(prev_query_len),
+        tracker_dtype=_INDEX_DTYPES[ring_start.dtype],
+        num_states=min(t.numel() for t in trackers), slots=_ptr(slots), slot_dtype=slot_dt,
+        slot_stride=stride, n=slots.shape[0], pad_slot_id=int(pad_slot_id))
+
+
+def update_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len,
+                                   state_batch_indices, logical_window=None,
+                                   ring_buffer_len=None, pad_slot_id=-1, stream=None):
+    """Reset the ring trackers of the named slots (logical_window None) or
+    advance them by one decoded token. A 2-D slot table names slots by its first
+    column. num_states is the shortest tracker's length."""
+    lib = library()
+    args = _ring_args(ring_start, prev_num_accepted, prev_query_len, state_batch_indices,
+                      pad_slot_id)
+    if logical_window is None:
+        args.reset, args.logical_window, args.ring_buffer_len = 1, 0, 1
+    else:
+        if ring_buffer_len is None:
+            raise ValueError("advancing needs ring_buffer_len")
+        args.reset, args.logical_window, args.ring_buffer_len = 0, logical_window, ring_buffer_len
+    rc = lib.ssu_ring_update(ctypes.byref(args), _stream(ring_start.device, stream))
+    if rc != _abi.SSU_OK:
+        _raise(lib, rc, "ssu_ring_update")
+
+
+def reset_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len,
+                                  state_batch_indices, pad_slot_id=-1, stream=None):
+    """Zero the three ring trackers of every named slot."""
+    update_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len,
+                                   state_batch_indices, pad_slot_id=pad_slot_id, stream=stream)
+
+
+def commit_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len,
+                                   state_batch_indices, num_accepted_tokens, query_start_loc,
+                                   logical_window, ring_buffer_len, pad_slot_id=-1,
+                                   stream=None):
+    """Settle the previous speculative window of each named slot with the count
+    accepted from it, and record the current window's length from query_start_loc."""
+    lib = library()
+    args = _ring_args(ring_start, prev_num_accepted, prev_query_len, state_batch_indices,
+                      pad_slot_id)
+    na, na_dt = _index("num_accepted_tokens", num_accepted_tokens, ring_start.device)
+    qsl, q_dt = _index("query_start_loc", query_start_loc, ring_start.device)
+    if na.dim() != 1 or na.shape[0] < args.n or qsl.dim() != 1 or qsl.shape[0] < args.n + 1:
+        raise ValueError("num_accepted_tokens needs n entries and query_start_loc n + 1")
+    if na.dtype != qsl.dtype:
+        raise ValueError("num_accepted_tokens and query_start_loc must share a dtype")
+    args.num_accepted, args.query_start_loc, args.meta_dtype = _ptr(na), _ptr(qsl), na_dt
+    args.logical_window, args.ring_buffer_len = logical_window, ring_buffer_len
+    rc = lib.ssu_ring_commit(ctypes.byref(args), _stream(ring_start.device, stream))
+    if rc != _abi.SSU_OK:
+        _raise(lib, rc, "ssu_ring_commit")

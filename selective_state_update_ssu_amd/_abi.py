@@ -10,7 +10,8 @@ SSU_I32, SSU_I64 = 0, 1
 SSU_OK, SSU_ERR_INVALID_ARGUMENT, SSU_ERR_UNSUPPORTED, SSU_ERR_LAUNCH = 0, 1, 2, 3
 ABI_VERSION = 1
 
-EXPORTS = ("ssu_one_token", "ssu_packed_varlen", "ssu_last_error", "ssu_version")
+EXPORTS = ("ssu_one_token", "ssu_packed_varlen", "ssu_ring_update", "ssu_ring_commit",
+           "ssu_last_error", "ssu_version")
 
 
 class Operands(ctypes.Structure):
@@ -48,6 +49,18 @@ class PackedArgs(ctypes.Structure):
     ]
 
 
+class RingArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_uint32),
+        ("ring_start", c_void_p), ("prev_num_accepted", c_void_p), ("prev_query_len", c_void_p),
+        ("tracker_dtype", c_int32), ("num_states", c_int64),
+        ("slots", c_void_p), ("slot_dtype", c_int32), ("slot_stride", c_int64), ("n", c_int64),
+        ("num_accepted", c_void_p), ("query_start_loc", c_void_p), ("meta_dtype", c_int32),
+        ("reset", c_int32), ("logical_window", c_int64), ("ring_buffer_len", c_int64),
+        ("pad_slot_id", c_int64),
+    ]
+
+
 def load(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(
@@ -59,6 +72,9 @@ def load(path: str) -> ctypes.CDLL:
     lib.ssu_one_token.argtypes = [ctypes.POINTER(OneTokenArgs), c_void_p]
     lib.ssu_packed_varlen.restype = c_int32
     lib.ssu_packed_varlen.argtypes = [ctypes.POINTER(PackedArgs), c_void_p]
+    for f in (lib.ssu_ring_update, lib.ssu_ring_commit):
+        f.restype = c_int32
+        f.argtypes = [ctypes.POINTER(RingArgs), c_void_p]
     lib.ssu_last_error.restype = c_char_p
     lib.ssu_last_error.argtypes = []
     lib.ssu_version.restype = c_int32

@@ -25,7 +25,8 @@ STREAM_SOURCES = ["stream_ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["ssu_api.hip", "ssu_kernels_f32.hip", "ssu_kernels_f16.hip", "ssu_kernels_bf16.hip"]
+SOURCES = ["ssu_api.hip", "ssu_kernels_f32.hip", "ssu_kernels_f16.hip", "ssu_kernels_bf16.hip",
+           "ring_trackers.hip"]
 CXXFLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",

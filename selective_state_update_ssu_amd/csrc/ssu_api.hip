@@ -29,6 +29,20 @@ int ok() {
     return SSU_OK;
 }
 
+}  // namespace
+
+int ssu::report(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(t_error, sizeof(t_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ssu::report_ok() { return ok(); }
+
+namespace {
+
 bool log_enabled() {
     static const bool on = [] {
         const char* v = std::getenv("SSU_LOG");

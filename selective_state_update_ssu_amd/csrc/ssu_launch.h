@@ -81,4 +81,9 @@ hipError_t launch_state_f16(KernelParams p, int io_dtype, int dstate, int64_t ns
 hipError_t launch_state_bf16(KernelParams p, int io_dtype, int dstate, int64_t nseq,
                              hipStream_t stream, LaunchShape* shape);
 
+// Error reporting shared by every entry point of the library: set the calling
+// thread's message and return `code` (report) or clear it and return 0 (ok).
+int report(int code, const char* fmt, ...);
+int report_ok();
+
 }  // namespace ssu

@@ -50,7 +50,7 @@ def test_struct_layout_matches_header(tmp_path):
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssu.h"', "int main(void){"]
     checks = []
     for cname, cls in (("ssu_operands", _abi.Operands), ("ssu_one_token_args", _abi.OneTokenArgs),
-                       ("ssu_packed_args", _abi.PackedArgs)):
+                       ("ssu_packed_args", _abi.PackedArgs), ("ssu_ring_args", _abi.RingArgs)):
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
         checks.append((cname, ctypes.sizeof(cls)))
         for fname, _ in cls._fields_:
@@ -184,6 +184,47 @@ def test_packed_rejects(lib, kw, code, needle):
 def test_packed_without_work_is_ok(lib):
     assert packed(lib, nseq=0)[0] == _abi.SSU_OK
     assert packed(lib, rows=0)[0] == _abi.SSU_OK
+
+
+def ring(lib, commit=False, **kw):
+    a = _abi.RingArgs(struct_size=ctypes.sizeof(_abi.RingArgs), ring_start=addr(20),
+                      prev_num_accepted=addr(21), prev_query_len=addr(22),
+                      tracker_dtype=_abi.SSU_I32, num_states=64, slots=addr(23),
+                      slot_dtype=_abi.SSU_I32, slot_stride=1, n=8, num_accepted=addr(24),
+                      query_start_loc=addr(25), meta_dtype=_abi.SSU_I32, reset=0,
+                      logical_window=4, ring_buffer_len=16, pad_slot_id=-1)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    f = lib.ssu_ring_commit if commit else lib.ssu_ring_update
+    return f(ctypes.byref(a), None), lib.ssu_last_error().decode()
+
+
+@pytest.mark.parametrize("commit,kw,needle", [
+    (False, dict(struct_size=3), "struct_size"),
+    (False, dict(n=-1), "n and num_states"),
+    (False, dict(slot_stride=-1), "slot_stride"),
+    (False, dict(tracker_dtype=2), "tracker_dtype"),
+    (False, dict(slot_dtype=7), "slot_dtype"),
+    (False, dict(ring_buffer_len=0), "ring_buffer_len"),
+    (False, dict(logical_window=-1), "logical_window"),
+    (False, dict(slots=None), "slots"),
+    (False, dict(prev_query_len=None), "tracker pointers"),
+    (False, dict(ring_start=addr(20) + 2), "aligned"),
+    (True, dict(meta_dtype=5), "meta_dtype"),
+    (True, dict(query_start_loc=None), "query_start_loc"),
+    (True, dict(ring_buffer_len=-3), "ring_buffer_len"),
+])
+def test_ring_rejects(lib, commit, kw, needle):
+    rc, msg = ring(lib, commit, **kw)
+    assert rc == INV, (rc, msg)
+    assert needle in msg, msg
+
+
+def test_ring_reset_needs_no_ring_length_and_empty_is_ok(lib):
+    assert ring(lib, n=0)[0] == _abi.SSU_OK
+    assert ring(lib, True, n=0)[0] == _abi.SSU_OK
+    # reset ignores the window parameters, but still checks its pointers
+    assert ring(lib, reset=1, ring_buffer_len=0, slots=None)[0] == INV
 
 
 def test_binding_refuses_host_tensors():
