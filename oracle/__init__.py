@@ -34,6 +34,13 @@ def build(source: str = SOURCE, output: str = LIBRARY) -> str:
     return output
 
 
+class _Rounding(ctypes.Structure):
+    _fields_ = [("sr_format", ctypes.c_int), ("rand_seed", ctypes.c_uint64),
+                ("philox_rounds", ctypes.c_int)]
+
+
+SR_FORMATS = {None: 0, "f16": 1, "bf16": 2}
+
 _dp = ctypes.POINTER(ctypes.c_double)
 _ip = ctypes.POINTER(ctypes.c_int64)
 _i64 = ctypes.c_int64
@@ -69,16 +76,22 @@ class Oracle:
         self.path = path
         lib = ctypes.CDLL(path)
         lib.oracle_ssu_one_token.restype = _int
+        _rp = ctypes.POINTER(_Rounding)
         lib.oracle_ssu_one_token.argtypes = [
             _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64,
             _dp, _dp, _int, _dp, _dp, _dp, _dp, _dp, _dp, _int,
-            _ip, _ip, _i64, _int, _dp]
+            _ip, _ip, _i64, _int, _rp, _dp]
         lib.oracle_ssu_packed_varlen.restype = _int
         lib.oracle_ssu_packed_varlen.argtypes = [
             _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
             _ip, _ip, _ip, _i64, _i64, _ip, _i64, _i64, _i64,
             _dp, _dp, _int, _dp, _dp, _dp, _dp, _dp, _dp, _int,
-            _i64, _int, _dp]
+            _i64, _int, _rp, _dp]
+        _u32p = ctypes.POINTER(ctypes.c_uint32)
+        lib.oracle_philox4x32.restype = None
+        lib.oracle_philox4x32.argtypes = [_u32p, _u32p, _int, _u32p]
+        lib.oracle_round_stochastic.restype = None
+        lib.oracle_round_stochastic.argtypes = [_dp, _u32p, _i64, _int, _dp]
         for f in (lib.oracle_ring_update, lib.oracle_ring_commit):
             f.restype = _int
         lib.oracle_ring_update.argtypes = [_ip, _ip, _ip, _i64, _ip, _i64, _i64, _int, _i64,
@@ -105,9 +118,35 @@ class Oracle:
         return (state, x, dt, dt_per_dim, _f64(A), _f64(B), _f64(C), _f64(D),
                 _f64(z), _f64(dt_bias), out, rows)
 
+    @staticmethod
+    def _rounding(sr_format, rand_seed, philox_rounds):
+        if sr_format is None:
+            return None
+        return ctypes.byref(_Rounding(SR_FORMATS[sr_format], int(rand_seed) & (2**64 - 1),
+                                      int(philox_rounds)))
+
+    def philox4x32(self, counter, key, rounds=10):
+        """The four output words of Philox4x32 for one counter and key."""
+        c = (ctypes.c_uint32 * 4)(*[int(v) & 0xFFFFFFFF for v in counter])
+        k = (ctypes.c_uint32 * 2)(*[int(v) & 0xFFFFFFFF for v in key])
+        o = (ctypes.c_uint32 * 4)()
+        self.lib.oracle_philox4x32(c, k, int(rounds), o)
+        return list(o)
+
+    def round_stochastic(self, v, words, fmt):
+        """SR of each v[i] to fmt ("f16" or "bf16") with random word words[i]."""
+        v = _f64(v).reshape(-1)
+        w = np.ascontiguousarray(np.asarray(words, dtype=np.uint32).reshape(-1))
+        assert v.shape == w.shape
+        out = np.empty_like(v)
+        self.lib.oracle_round_stochastic(_p(v, _dp), w.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                         v.shape[0], SR_FORMATS[fmt], _p(out, _dp))
+        return out
+
     def one_token(self, state, x, dt, A, B, C, *, D=None, z=None, dt_bias=None,
                   dt_softplus=False, src=None, dst=None, pad_slot_id=-1,
-                  disable_state_update=False, out_init=None) -> Result:
+                  disable_state_update=False, out_init=None, sr_format=None, rand_seed=0,
+                  philox_rounds=10) -> Result:
         """One token per sequence: row b of x/dt/B/C/z/out is sequence b."""
         (state, x, dt, dt_per_dim, A, B, C, D, z, dt_bias, out,
          batch) = self._common(state, x, dt, A, B, C, D, z, dt_bias, out_init)
@@ -120,7 +159,7 @@ class Oracle:
             _p(x, _dp), _p(dt, _dp), dt_per_dim, _p(A, _dp), _p(B, _dp), _p(C, _dp),
             _p(D, _dp), _p(z, _dp), _p(dt_bias, _dp), int(bool(dt_softplus)),
             _p(src, _ip), _p(dst, _ip), int(pad_slot_id), int(bool(disable_state_update)),
-            _p(out, _dp))
+            self._rounding(sr_format, rand_seed, philox_rounds), _p(out, _dp))
         if rc != 0:
             raise ValueError("oracle_ssu_one_token rejected its arguments")
         return Result(out, state_out)
@@ -128,7 +167,8 @@ class Oracle:
     def packed_varlen(self, state, x, dt, A, B, C, cu_seqlens, *, num_accepted=None,
                       src_table=None, src_strides=None, dst_table=None, dst_strides=None,
                       steps=None, D=None, z=None, dt_bias=None, dt_softplus=False,
-                      pad_slot_id=-1, disable_state_update=False, out_init=None) -> Result:
+                      pad_slot_id=-1, disable_state_update=False, out_init=None,
+                      sr_format=None, rand_seed=0, philox_rounds=10) -> Result:
         """Packed varlen form. A 2-D table [nseq, steps] takes strides (steps, 1)
         unless strides are given; a flat table needs explicit strides and steps."""
         (state, x, dt, dt_per_dim, A, B, C, D, z, dt_bias, out,
@@ -160,7 +200,8 @@ class Oracle:
             _p(cu, _ip), _p(na, _ip), _p(st, _ip), sss, sst, _p(dtb, _ip), dss, dst_,
             int(steps), _p(x, _dp), _p(dt, _dp), dt_per_dim, _p(A, _dp), _p(B, _dp),
             _p(C, _dp), _p(D, _dp), _p(z, _dp), _p(dt_bias, _dp), int(bool(dt_softplus)),
-            int(pad_slot_id), int(bool(disable_state_update)), _p(out, _dp))
+            int(pad_slot_id), int(bool(disable_state_update)),
+            self._rounding(sr_format, rand_seed, philox_rounds), _p(out, _dp))
         if rc != 0:
             raise ValueError("oracle_ssu_packed_varlen rejected its arguments")
         return Result(out, state_out)

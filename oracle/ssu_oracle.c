@@ -42,6 +42,15 @@
  *    position * step_stride.
  *  - The dense [batch, steps, ...] form is the packed form with regular starts
  *    (`selective_state_update` body), so it needs no function of its own here.
+ *  - Stochastic rounding of 16-bit state: the vLLM dispatch page forwards a
+ *    random seed and a Philox round count (default 10) to the state update when
+ *    stochastic rounding is enabled; the rounding rule and the random-number
+ *    layout are not on the pages. Reading taken here: unbiased stochastic
+ *    rounding of the exact state value to the target format (round away from
+ *    zero with probability equal to the fraction of the quantum the value passes),
+ *    driven by Philox4x32 as published (Salmon, Moraes, Dror, Shaw, "Parallel
+ *    random numbers: as easy as 1, 2, 3", SC'11), with the counter layout
+ *    documented in ssu_oracle.h.
  *  - ReplaySSM ring trackers: the update / reset and the delayed commit of the
  *    vLLM `ssu_dispatch` module source (the two tracker kernels and their
  *    wrappers `update_replayssm_ring_trackers` and
@@ -70,6 +79,86 @@ typedef struct {
     const double *x, *dt, *A, *B, *C, *D, *z, *dt_bias;
     int dt_per_dim, dt_softplus;
 } problem;
+
+/* ------------------------------------------------------ stochastic rounding */
+
+/* One Philox4x32 round: two 32x32->64 products of counter words 0 and 2 with
+ * the multipliers; the high halves are mixed with the other two counter words
+ * and the key, the low halves pass through. */
+void oracle_philox4x32(const uint32_t counter[4], const uint32_t key[2], int rounds,
+                       uint32_t out[4]) {
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;   /* round multipliers */
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;   /* key increments */
+    uint32_t c0 = counter[0], c1 = counter[1], c2 = counter[2], c3 = counter[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < rounds; ++r) {
+        if (r > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint64_t p0 = (uint64_t)M0 * c0;
+        const uint64_t p1 = (uint64_t)M1 * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* SR(v): q is the target format's spacing at |v| (2^(e - mantissa bits), with e
+ * clamped to the smallest normal exponent so subnormals share one spacing),
+ * m = floor(|v| / q), frac = |v| / q - m. The result is m q, or (m + 1) q when
+ * the k-bit uniform U taken from the top of w satisfies U >= 1 - frac; past the
+ * largest finite value it is infinite. NaN, infinities and zeros pass through. */
+static double round_stochastic(double v, uint32_t w, int format) {
+    if (v != v || v == 0.0 || isinf(v)) return v;
+    const int mant = format == 1 ? 10 : 7;           /* explicit mantissa bits */
+    const int emin = format == 1 ? -14 : -126;       /* smallest normal exponent */
+    const int kbits = format == 1 ? 24 : 16;         /* random bits used */
+    const double maxfin = format == 1 ? 65504.0 : ldexp(2.0 - ldexp(1.0, -7), 127);
+    const double a = fabs(v);
+    int e;
+    frexp(a, &e);                                    /* a = f * 2^e, f in [0.5, 1) */
+    e -= 1;                                          /* a in [2^e, 2^(e+1)) */
+    const int qexp = (e > emin ? e : emin) - mant;
+    const double t = ldexp(a, -qexp);
+    const double m = floor(t);
+    const double frac = t - m;
+    const double U = ldexp((double)(w >> (32 - kbits)), -kbits);
+    double r = ldexp(m + (U >= 1.0 - frac ? 1.0 : 0.0), qexp);
+    if (r > maxfin) r = INFINITY;
+    return v < 0 ? -r : r;
+}
+
+void oracle_round_stochastic(const double *v, const uint32_t *w, int64_t n, int format,
+                             double *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = round_stochastic(v[i], w[i], format);
+}
+
+/* Round the fp64 state s ([nheads, headdim, dstate]) written by packed row `row`
+ * into dst, stochastically when requested. */
+static void store_state(double *dst, const double *s, int64_t elems, int64_t row,
+                        const oracle_rounding *rd) {
+    if (!rd || rd->sr_format == 0) {
+        memcpy(dst, s, (size_t)elems * sizeof(double));
+        return;
+    }
+    const uint32_t key[2] = {(uint32_t)rd->rand_seed, (uint32_t)(rd->rand_seed >> 32)};
+    for (int64_t e = 0; e < elems; ++e) {
+        const uint32_t ctr[4] = {(uint32_t)(e / 4), (uint32_t)row, (uint32_t)((uint64_t)row >> 32), 0};
+        uint32_t words[4];
+        oracle_philox4x32(ctr, key, rd->philox_rounds, words);
+        dst[e] = round_stochastic(s[e], words[e % 4], rd->sr_format);
+    }
+}
 
 /*
  * Advance one sequence's fp64 state `s` ([nheads, headdim, dstate]) by the token
@@ -125,7 +214,7 @@ int oracle_ssu_one_token(const double *state_in, double *state_out,
                          const double *dt_bias, int dt_softplus,
                          const int64_t *src, const int64_t *dst,
                          int64_t pad_slot_id, int disable_state_update,
-                         double *out) {
+                         const oracle_rounding *rounding, double *out) {
     const problem pb = {nslots, nheads, headdim, dstate, ngroups,
                         x,      dt,     A,       B,      C,
                         D,      z,      dt_bias, dt_per_dim, dt_softplus};
@@ -144,7 +233,7 @@ int oracle_ssu_one_token(const double *state_in, double *state_out,
         memcpy(s, state_in + r * slot_elems, (size_t)slot_elems * sizeof(double));
         step_token(&pb, s, b, out);
         if (!disable_state_update && slot_valid(w, pad_slot_id, nslots))
-            memcpy(state_out + w * slot_elems, s, (size_t)slot_elems * sizeof(double));
+            store_state(state_out + w * slot_elems, s, slot_elems, b, rounding);
     }
     free(s);
     return 0;
@@ -159,7 +248,8 @@ int oracle_ssu_packed_varlen(
     int64_t steps, const double *x, const double *dt, int dt_per_dim,
     const double *A, const double *B, const double *C, const double *D,
     const double *z, const double *dt_bias, int dt_softplus,
-    int64_t pad_slot_id, int disable_state_update, double *out) {
+    int64_t pad_slot_id, int disable_state_update, const oracle_rounding *rounding,
+    double *out) {
     const problem pb = {nslots, nheads, headdim, dstate, ngroups,
                         x,      dt,     A,       B,      C,
                         D,      z,      dt_bias, dt_per_dim, dt_softplus};
@@ -204,8 +294,7 @@ int oracle_ssu_packed_varlen(
             else
                 w = r;
             if (slot_valid(w, pad_slot_id, nslots))
-                memcpy(state_out + w * slot_elems, s,
-                       (size_t)slot_elems * sizeof(double));
+                store_state(state_out + w * slot_elems, s, slot_elems, begin + t, rounding);
         }
     }
     free(s);

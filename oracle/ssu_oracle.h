@@ -35,6 +35,21 @@
 extern "C" {
 #endif
 
+/*
+ * Stochastic rounding of stored states. With sr_format != 0 every state the call
+ * writes is rounded stochastically to fp16 (sr_format 1) or bf16 (2) -- the
+ * fp64 result holds the exact 16-bit value -- using Philox4x32 with
+ * philox_rounds rounds keyed by the 64-bit rand_seed. The random word of element
+ * e = (h * headdim + p) * dstate + n of the state written by packed row `row` is
+ * word e % 4 of Philox(counter = (e / 4, row % 2^32, row / 2^32, 0)). With
+ * sr_format 0 stored states are the unrounded fp64 values.
+ */
+typedef struct {
+    int sr_format;          /* 0 none, 1 fp16, 2 bf16 */
+    uint64_t rand_seed;
+    int philox_rounds;
+} oracle_rounding;
+
 /* One token per sequence (row b is sequence b). src/dst may be NULL. */
 int oracle_ssu_one_token(const double *state_in, double *state_out,
                          int64_t nslots, int64_t nheads, int64_t headdim,
@@ -45,7 +60,7 @@ int oracle_ssu_one_token(const double *state_in, double *state_out,
                          const double *dt_bias, int dt_softplus,
                          const int64_t *src, const int64_t *dst,
                          int64_t pad_slot_id, int disable_state_update,
-                         double *out);
+                         const oracle_rounding *rounding, double *out);
 
 /* Packed variable-length form: sequence b owns rows [cu[b], cu[b+1]). */
 int oracle_ssu_packed_varlen(
@@ -57,7 +72,19 @@ int oracle_ssu_packed_varlen(
     int64_t steps, const double *x, const double *dt, int dt_per_dim,
     const double *A, const double *B, const double *C, const double *D,
     const double *z, const double *dt_bias, int dt_softplus,
-    int64_t pad_slot_id, int disable_state_update, double *out);
+    int64_t pad_slot_id, int disable_state_update, const oracle_rounding *rounding,
+    double *out);
+
+/* Philox4x32 (Salmon et al., SC'11): `rounds` rounds of the 4x32 round function
+ * on counter[4] with key[2], the key bumped by the Weyl constants between
+ * rounds. Writes the four output words to out[4]. */
+void oracle_philox4x32(const uint32_t counter[4], const uint32_t key[2], int rounds,
+                       uint32_t out[4]);
+
+/* Stochastic rounding of v to fp16 (format 1) or bf16 (2) with random word w,
+ * for n values: out[i] = SR(v[i], w[i]). */
+void oracle_round_stochastic(const double *v, const uint32_t *w, int64_t n, int format,
+                             double *out);
 
 /*
  * ReplaySSM ring trackers: three per-slot counters (ring_start,

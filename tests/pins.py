@@ -485,4 +485,142 @@ def pin_ring_commit_sequence(orc):
         assert got == want[step], (step, got, want[step])
 
 
+# -------------------------------------------------------- stochastic rounding
+
+_ROCRAND = {}
+
+
+def _rocrand_philox(vectors):
+    """Philox4x32-10 words from rocRAND's host-callable engine (a library
+    routine), for (key0, key1, c0, c1, c2, c3) tuples with c1 < 2^30."""
+    import subprocess
+    import tempfile
+    if "exe" not in _ROCRAND:
+        d = tempfile.mkdtemp(prefix="rocrand_philox_")
+        exe = os.path.join(d, "rocrand_philox")
+        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "rocrand_philox.cpp")
+        subprocess.run(["/opt/rocm/bin/hipcc", "-O1", "--offload-arch=gfx950", "-o", exe, src],
+                       check=True, capture_output=True)
+        _ROCRAND["exe"] = exe
+    text = "".join(" ".join(f"{v:x}" for v in vec) + "\n" for vec in vectors)
+    out = subprocess.run([_ROCRAND["exe"]], input=text, capture_output=True, text=True,
+                         check=True).stdout.split("\n")
+    return [[int(w, 16) for w in line.split()] for line in out if line.strip()]
+
+
+def pin_philox_matches_rocrand(orc):
+    """The oracle's Philox4x32 at 10 rounds equals rocRAND's Philox4x32-10 on
+    edge and random keys and counters."""
+    rng = np.random.default_rng(41)
+    vecs = [(0, 0, 0, 0, 0, 0), (0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0x3FFFFFFF, 0xFFFFFFFF,
+                                 0xFFFFFFFF), (1, 0, 7, 3, 0, 0), (0xDEADBEEF, 0, 12345, 0, 1, 0)]
+    for _ in range(60):
+        k0, k1, c0, c2, c3 = (int(v) for v in rng.integers(0, 2**32, 5))
+        vecs.append((k0, k1, c0, int(rng.integers(0, 2**30)), c2, c3))
+    ref = _rocrand_philox(vecs)
+    for vec, want in zip(vecs, ref):
+        got = orc.philox4x32(vec[2:], vec[:2], 10)
+        assert got == want, (vec, [hex(g) for g in got], [hex(w) for w in want])
+
+
+def _fp32_values(rng, n, lo_exp, hi_exp):
+    """Random fp32 values with exponents in [lo_exp, hi_exp], both signs."""
+    m = rng.integers(0, 2**23, n)
+    e = rng.integers(lo_exp, hi_exp + 1, n)
+    v = (1.0 + m / 2.0**23) * np.exp2(e)
+    v = v.astype(np.float32).astype(np.float64)
+    return v * np.where(rng.random(n) < 0.5, -1.0, 1.0)
+
+
+def pin_stochastic_rounding_is_unbiased(orc):
+    """Averaged over the random words, SR returns its input exactly: it rounds
+    away from zero with probability equal to the fraction of the spacing the
+    value passes. For an fp32 input that fraction has at most b bits (b = 16 for
+    bf16, 13 for fp16 normals, 13 + (-14 - e) for fp16 subnormals of exponent e),
+    and U >= 1 - frac then depends only on U's top b bits, so the 2^b words whose
+    remaining bits are zero give exactly the mean over all words."""
+    rng = np.random.default_rng(43)
+    cases = [("bf16", 16, _fp32_values(rng, 6, -130, 120)),
+             ("f16", 13, _fp32_values(rng, 4, -14, 15)),
+             ("f16", 15, _fp32_values(rng, 2, -16, -16)),
+             ("f16", 17, _fp32_values(rng, 2, -18, -18)),
+             ("f16", 20, _fp32_values(rng, 1, -21, -21))]
+    for fmt, b, values in cases:
+        words = (np.arange(2**b, dtype=np.uint64) << (32 - b)).astype(np.uint32)
+        for v in values:
+            r = orc.round_stochastic(np.full(words.shape, v), words, fmt)
+            assert np.all(np.isfinite(r))
+            assert math.fsum(r) / 2**b == v, (fmt, v, math.fsum(r) / 2**b)
+
+
+def _format_neighbours(v, fmt):
+    """The two values of the format bracketing each v (toward and away from
+    zero), from torch's round-to-nearest conversion and the adjacent bit
+    patterns (the magnitude bits of a 16-bit float count up by one per value)."""
+    import torch
+    tdt = torch.bfloat16 if fmt == "bf16" else torch.float16
+    n = torch.tensor(v).to(torch.float32).to(tdt)
+    nb = n.view(torch.int16).numpy().astype(np.int32)
+    nv = n.double().numpy()
+    up = torch.tensor((nb + 1).astype(np.int16)).view(tdt).double().numpy()
+    dn = torch.tensor(np.maximum(nb - 1, nb & ~0x7FFF).astype(np.int16)).view(tdt).double().numpy()
+    toward = np.where(np.abs(nv) <= np.abs(v), nv, dn)
+    away = np.where(np.abs(nv) <= np.abs(v), np.where(nv == v, nv, up), nv)
+    return toward, away
+
+
+def pin_stochastic_rounding_neighbours(orc):
+    """SR lands on one of the two neighbours of v in the target format, keeps
+    representable values, is odd-symmetric, passes 0/inf/nan, and overflows past
+    the largest finite value to infinity."""
+    rng = np.random.default_rng(47)
+    for fmt in ("bf16", "f16"):
+        v = _fp32_values(rng, 4000, -20 if fmt == "f16" else -100, 14)
+        w = rng.integers(0, 2**32, v.shape[0], dtype=np.uint64).astype(np.uint32)
+        r = orc.round_stochastic(v, w, fmt)
+        toward, away = _format_neighbours(v, fmt)
+        assert np.all((r == toward) | (r == away)), fmt
+        assert (r == away).any() and (r == toward).any(), fmt
+        rep = toward[:200]
+        assert np.array_equal(orc.round_stochastic(rep, w[:200], fmt), rep), fmt
+        assert np.array_equal(orc.round_stochastic(-v, w, fmt), -r), fmt
+    sp = orc.round_stochastic([0.0, np.inf, -np.inf, np.nan], [0xFFFFFFFF] * 4, "f16")
+    assert sp[0] == 0 and sp[1] == np.inf and sp[2] == -np.inf and np.isnan(sp[3])
+    assert orc.round_stochastic([65510.0], [0xFFFFFFFF], "f16")[0] == np.inf
+    assert orc.round_stochastic([65510.0], [0], "f16")[0] == 65504.0
+    bf16_max = (2 - 2.0**-7) * 2.0**127
+    big = float(np.float32(3.396e38))            # between bf16's maximum and fp32's
+    assert orc.round_stochastic([big], [0xFFFFFFFF], "bf16")[0] == np.inf
+    assert orc.round_stochastic([big], [0], "bf16")[0] == bf16_max
+
+
+def pin_stochastic_rounding_in_the_update(orc):
+    """A stored 16-bit state is SR of the unrounded state with the random word
+    of its element: word e % 4 of Philox(counter = (e / 4, row lo, row hi, 0),
+    key = seed), e the element's index within the slot and row the token's
+    packed row; rounds as given."""
+    rng = np.random.default_rng(53)
+    H, P, N, G, L = 2, 3, 8, 1, 3
+    pb = _rand_problem(rng, rows=L, H=H, P=P, N=N, G=G, nslots=2 * L)
+    table = np.array([[0, 1, 2]])
+    dtab = np.array([[3, 4, 5]])
+    seed = 0x1234_5678_9ABC_DEF0
+    for fmt, rounds in (("bf16", 10), ("f16", 7)):
+        plain = orc.packed_varlen(cu_seqlens=[0, L], src_table=table, dst_table=dtab,
+                                  dt_softplus=True, **pb)
+        sr = orc.packed_varlen(cu_seqlens=[0, L], src_table=table, dst_table=dtab,
+                               dt_softplus=True, sr_format=fmt, rand_seed=seed,
+                               philox_rounds=rounds, **pb)
+        assert np.array_equal(plain.out, sr.out)
+        for t in range(L):
+            vals = plain.state[dtab[0, t]].reshape(-1)
+            words = np.array([orc.philox4x32([e // 4, t, 0, 0],
+                                             [seed & 0xFFFFFFFF, seed >> 32], rounds)[e % 4]
+                              for e in range(vals.shape[0])], dtype=np.uint32)
+            want = orc.round_stochastic(vals, words, fmt)
+            assert np.array_equal(sr.state[dtab[0, t]].reshape(-1), want), (fmt, t)
+        for s in range(3):
+            assert np.array_equal(sr.state[s], pb["state"][s])
+
+
 ALL = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -60,6 +60,18 @@ MUTANTS = [
     ("commit_start_by_window", "ring_start[s] = (ring_start[s] + counted) % ring_buffer_len;\n            prev_num_accepted[s] = accepted;",
      "ring_start[s] = (ring_start[s] + window) % ring_buffer_len;\n            prev_num_accepted[s] = accepted;"),
     ("commit_window_from_accepted", "prev_query_len[s] = query_start_loc[i + 1] - query_start_loc[i];", "prev_query_len[s] = num_accepted[i];"),
+    ("sr_strict_threshold", "(U >= 1.0 - frac ? 1.0 : 0.0)", "(U > 1.0 - frac ? 1.0 : 0.0)"),
+    ("sr_threshold_frac", "(U >= 1.0 - frac ? 1.0 : 0.0)", "(U >= frac ? 1.0 : 0.0)"),
+    ("sr_random_bits", "const int kbits = format == 1 ? 24 : 16;", "const int kbits = format == 1 ? 16 : 16;"),
+    ("sr_exponent_off_by_one", "    e -= 1;                                          /* a in [2^e, 2^(e+1)) */\n", ""),
+    ("sr_f16_subnormal_spacing", "const int emin = format == 1 ? -14 : -126;", "const int emin = format == 1 ? -15 : -126;"),
+    ("sr_no_overflow", "    if (r > maxfin) r = INFINITY;\n", ""),
+    ("philox_multiplier_swap", "const uint64_t p0 = (uint64_t)M0 * c0;", "const uint64_t p0 = (uint64_t)M1 * c0;"),
+    ("philox_no_key_bump", "            k0 += W0;\n            k1 += W1;\n", "            k1 += W1;\n"),
+    ("philox_key_words_swapped", "const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;", "const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k1;"),
+    ("sr_counter_element", "const uint32_t ctr[4] = {(uint32_t)(e / 4),", "const uint32_t ctr[4] = {(uint32_t)(e),"),
+    ("sr_word_index", "words[e % 4]", "words[0]"),
+    ("sr_row_of_token", "store_state(state_out + w * slot_elems, s, slot_elems, begin + t, rounding);", "store_state(state_out + w * slot_elems, s, slot_elems, begin, rounding);"),
     ("ring_position_not_strided", "const int64_t s = slots[i * slot_stride];\n        if (!slot_valid(s, pad_slot_id, num_states)) continue;\n        if (reset)",
      "const int64_t s = slots[i];\n        if (!slot_valid(s, pad_slot_id, num_states)) continue;\n        if (reset)"),
 ]
