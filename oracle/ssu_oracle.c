@@ -133,7 +133,9 @@ static double round_stochastic(double v, uint32_t w, int format) {
     const double m = floor(t);
     const double frac = t - m;
     const double U = ldexp((double)(w >> (32 - kbits)), -kbits);
-    double r = ldexp(m + (U >= 1.0 - frac ? 1.0 : 0.0), qexp);
+    /* U >= 1 - frac, decided exactly: U - 1 is exact and a rounded sum keeps
+     * the sign of the exact one. */
+    double r = ldexp(m + ((U - 1.0) + frac >= 0.0 ? 1.0 : 0.0), qexp);
     if (r > maxfin) r = INFINITY;
     return v < 0 ? -r : r;
 }

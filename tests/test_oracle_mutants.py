@@ -60,8 +60,8 @@ MUTANTS = [
     ("commit_start_by_window", "ring_start[s] = (ring_start[s] + counted) % ring_buffer_len;\n            prev_num_accepted[s] = accepted;",
      "ring_start[s] = (ring_start[s] + window) % ring_buffer_len;\n            prev_num_accepted[s] = accepted;"),
     ("commit_window_from_accepted", "prev_query_len[s] = query_start_loc[i + 1] - query_start_loc[i];", "prev_query_len[s] = num_accepted[i];"),
-    ("sr_strict_threshold", "(U >= 1.0 - frac ? 1.0 : 0.0)", "(U > 1.0 - frac ? 1.0 : 0.0)"),
-    ("sr_threshold_frac", "(U >= 1.0 - frac ? 1.0 : 0.0)", "(U >= frac ? 1.0 : 0.0)"),
+    ("sr_strict_threshold", "((U - 1.0) + frac >= 0.0 ? 1.0 : 0.0)", "((U - 1.0) + frac > 0.0 ? 1.0 : 0.0)"),
+    ("sr_threshold_frac", "((U - 1.0) + frac >= 0.0 ? 1.0 : 0.0)", "(U >= frac ? 1.0 : 0.0)"),
     ("sr_random_bits", "const int kbits = format == 1 ? 24 : 16;", "const int kbits = format == 1 ? 16 : 16;"),
     ("sr_exponent_off_by_one", "    e -= 1;                                          /* a in [2^e, 2^(e+1)) */\n", ""),
     ("sr_f16_subnormal_spacing", "const int emin = format == 1 ? -14 : -126;", "const int emin = format == 1 ? -15 : -126;"),
