@@ -154,11 +154,22 @@ static void store_state(double *dst, const double *s, int64_t elems, int64_t row
         return;
     }
     const uint32_t key[2] = {(uint32_t)rd->rand_seed, (uint32_t)(rd->rand_seed >> 32)};
+    const int bf16 = rd->sr_format == 2;
+    const int64_t group = bf16 ? 8 : 4;          /* elements per Philox call */
     for (int64_t e = 0; e < elems; ++e) {
-        const uint32_t ctr[4] = {(uint32_t)(e / 4), (uint32_t)row, (uint32_t)((uint64_t)row >> 32), 0};
+        const uint32_t ctr[4] = {(uint32_t)(e / group), (uint32_t)row,
+                                 (uint32_t)((uint64_t)row >> 32), 0};
         uint32_t words[4];
         oracle_philox4x32(ctr, key, rd->philox_rounds, words);
-        dst[e] = round_stochastic(s[e], words[e % 4], rd->sr_format);
+        uint32_t w;
+        if (bf16) {
+            const uint32_t word = words[(e % 8) / 2];
+            const uint32_t bits16 = (e % 2) ? (word >> 16) : (word & 0xFFFFu);
+            w = bits16 << 16;                    /* round_stochastic reads the top bits */
+        } else {
+            w = words[e % 4];
+        }
+        dst[e] = round_stochastic(s[e], w, rd->sr_format);
     }
 }
 

@@ -39,10 +39,13 @@ extern "C" {
  * Stochastic rounding of stored states. With sr_format != 0 every state the call
  * writes is rounded stochastically to fp16 (sr_format 1) or bf16 (2) -- the
  * fp64 result holds the exact 16-bit value -- using Philox4x32 with
- * philox_rounds rounds keyed by the 64-bit rand_seed. The random word of element
- * e = (h * headdim + p) * dstate + n of the state written by packed row `row` is
- * word e % 4 of Philox(counter = (e / 4, row % 2^32, row / 2^32, 0)). With
- * sr_format 0 stored states are the unrounded fp64 values.
+ * philox_rounds rounds keyed by the 64-bit rand_seed. Element
+ * e = (h * headdim + p) * dstate + n of the state written by packed row `row`
+ * draws its random bits from Philox(counter = (e / G, row % 2^32, row / 2^32, 0)):
+ *   fp16 (G = 4): the top 24 bits of word e % 4;
+ *   bf16 (G = 8): 16 bits of word (e % 8) / 2, its low half for even e and its
+ *                 high half for odd e.
+ * With sr_format 0 stored states are the unrounded fp64 values.
  */
 typedef struct {
     int sr_format;          /* 0 none, 1 fp16, 2 bf16 */

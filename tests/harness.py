@@ -45,6 +45,7 @@ def gpu_run(w: Workload, heads_per_block=0, loads_per_lane=0, tile_order=0):
     out = w.out_sentinel()
     common = dict(D=w.D, z=w.z, dt_bias=w.dt_bias, dt_softplus=w.dt_softplus,
                   pad_slot_id=w.pad_slot_id, disable_state_update=w.disable_state_update,
+                  rand_seed=w.rand_seed, philox_rounds=w.philox_rounds,
                   heads_per_block=heads_per_block, loads_per_lane=loads_per_lane,
                   tile_order=tile_order)
     if w.mode == "one_token":
@@ -72,12 +73,23 @@ def gpu_run(w: Workload, heads_per_block=0, loads_per_lane=0, tile_order=0):
 
 # --------------------------------------------------------------- oracle side
 
-def oracle_full(w: Workload, state=None):
-    """The oracle on the whole workload (small problems)."""
+def sr_args(w: Workload, rounding=True):
+    """The oracle's stochastic-rounding arguments for a workload (none unless a
+    seed is set and the state is 16-bit)."""
+    if not rounding or w.rand_seed is None or w.state.dtype == torch.float32:
+        return {}
+    fmt = "bf16" if w.state.dtype == torch.bfloat16 else "f16"
+    return dict(sr_format=fmt, rand_seed=int(w.rand_seed.item()), philox_rounds=w.philox_rounds)
+
+
+def oracle_full(w: Workload, state=None, rounding=True):
+    """The oracle on the whole workload (small problems). With rounding=False a
+    stochastic-rounding workload is run without it (the unrounded states)."""
     orc = oracle.default()
     st = f64(w.state if state is None else state)
     common = dict(D=f64(w.D), z=f64(w.z), dt_bias=f64(w.dt_bias), dt_softplus=w.dt_softplus,
-                  pad_slot_id=w.pad_slot_id, disable_state_update=w.disable_state_update)
+                  pad_slot_id=w.pad_slot_id, disable_state_update=w.disable_state_update,
+                  **sr_args(w, rounding))
     if w.mode == "one_token":
         return orc.one_token(st, f64(w.x), f64(w.dt), f64(w.A), f64(w.B), f64(w.C),
                              src=i64(w.src), dst=i64(w.dst), **common)
@@ -93,11 +105,16 @@ def _valid(s, pad, nslots):
     return s != pad and 0 <= s < nslots
 
 
-def oracle_sample(w: Workload, seqs, state_before):
+def oracle_sample(w: Workload, seqs, state_before, rounding=True):
     """The oracle on sequences `seqs` of a workload with 2-D (or no) tables.
     Returns (rows, out_ref [len(rows), H, P], slots, state_ref [len(slots), ...]):
-    `rows` index the full out tensor, `slots` the full state cache."""
+    `rows` index the full out tensor, `slots` the full state cache. Stochastic
+    rounding numbers rows within the sample, so with a seed `seqs` must be a
+    prefix 0..k-1 (whose rows keep their numbers)."""
     orc = oracle.default()
+    sr = sr_args(w, rounding)
+    if sr:
+        assert list(seqs) == list(range(len(seqs))), "stochastic rounding needs a prefix sample"
     nslots = w.state.shape[0]
     pad = w.pad_slot_id
     seqs = list(seqs)
@@ -119,7 +136,7 @@ def oracle_sample(w: Workload, seqs, state_before):
                             f64(w.B[rows]), f64(w.C[rows]), D=f64(w.D),
                             z=None if w.z is None else f64(w.z[rows]), dt_bias=f64(w.dt_bias),
                             dt_softplus=w.dt_softplus, src=rs, dst=ds, pad_slot_id=-1,
-                            disable_state_update=w.disable_state_update)
+                            disable_state_update=w.disable_state_update, **sr)
         return rows, res.out, used, res.state[:len(used)]
 
     cu = i64(w.cu_seqlens)
@@ -166,7 +183,8 @@ def oracle_sample(w: Workload, seqs, state_before):
         np.array(sub_cu), num_accepted=sub_na,
         src_table=sub_src, dst_table=sub_dst, steps=steps if (sub_src is not None or sub_dst is not None) else None,
         D=f64(w.D), z=None if w.z is None else f64(w.z[sel]), dt_bias=f64(w.dt_bias),
-        dt_softplus=w.dt_softplus, pad_slot_id=-1, disable_state_update=w.disable_state_update)
+        dt_softplus=w.dt_softplus, pad_slot_id=-1, disable_state_update=w.disable_state_update,
+        **sr)
     return rows, res.out, used, res.state[:len(used)]
 
 
@@ -277,3 +295,45 @@ def check_placement(name, w: Workload, out_gpu, state_after, state_before):
     live = torch.as_tensor(~untouched, device=out_gpu.device)
     assert torch.isfinite(out_gpu[live].float()).all(), f"{name}: non-finite values in written out rows"
     return written, untouched
+
+
+def _neighbours(v, dtype):
+    """The two values of a 16-bit format bracketing each v (toward and away from
+    zero), from torch's rounding and the adjacent bit patterns."""
+    n = torch.tensor(v).to(torch.float32).to(dtype)
+    nb = n.view(torch.int16).numpy().astype(np.int32)
+    nv = n.double().numpy()
+    up = torch.tensor((nb + 1).astype(np.int16)).view(dtype).double().numpy()
+    dn = torch.tensor(np.maximum(nb - 1, nb & ~0x7FFF).astype(np.int16)).view(dtype).double().numpy()
+    toward = np.where(np.abs(nv) <= np.abs(v), nv, dn)
+    away = np.where(np.abs(nv) <= np.abs(v), np.where(nv == v, nv, up), nv)
+    return toward, away
+
+
+def check_slots_sr(name, state_after, state_before, slots, state_sr, state_plain,
+                   max_flip_rate=2e-3):
+    """Stochastically rounded slots: the GPU value equals the oracle's
+    stochastic rounding (same random words) except where the GPU's fp32 state and
+    the oracle's fp64 state fall on opposite sides of a rounding threshold. Such
+    elements must be rare and, like every element, within the 16-bit tolerance of
+    the exact state (near-zero states from cancellation can sit several 16-bit
+    spacings from their fp32 value). Slots the oracle leaves unchanged must be
+    bit-identical."""
+    idx = torch.as_tensor(slots, dtype=torch.long, device=state_after.device)
+    after = f64(state_after[idx])
+    before = f64(state_before[idx])
+    flips = total = 0
+    for i, s in enumerate(slots):
+        if np.array_equal(state_sr[i], before[i]) and np.array_equal(state_plain[i], before[i]):
+            assert np.array_equal(after[i], before[i]), f"{name}: slot {s} changed on the GPU"
+            continue
+        g, want, exact = after[i].reshape(-1), state_sr[i].reshape(-1), state_plain[i].reshape(-1)
+        bad = g != want
+        err = np.abs(g - exact)
+        ratio = float((err / (1e-2 + 2e-2 * np.abs(exact))).max())
+        assert ratio <= 1.0, f"{name}: slot {s}: error beyond the 16-bit tolerance ({ratio:.3f})"
+        flips += int(bad.sum())
+        total += g.size
+    rate = flips / max(total, 1)
+    assert rate <= max_flip_rate, f"{name}: {flips} of {total} elements rounded the other way"
+    return rate

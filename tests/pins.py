@@ -594,11 +594,22 @@ def pin_stochastic_rounding_neighbours(orc):
     assert orc.round_stochastic([big], [0], "bf16")[0] == bf16_max
 
 
+def _sr_word(orc, e, row, seed, rounds, fmt):
+    """The random word element e of row `row` uses, with its bits at the top:
+    fp16 takes word e % 4 of Philox(e / 4, ...); bf16 takes the low (even e) or
+    high (odd e) half of word (e % 8) / 2 of Philox(e / 8, ...)."""
+    key = [seed & 0xFFFFFFFF, seed >> 32]
+    if fmt == "f16":
+        return orc.philox4x32([e // 4, row, 0, 0], key, rounds)[e % 4]
+    word = orc.philox4x32([e // 8, row, 0, 0], key, rounds)[(e % 8) // 2]
+    half = (word >> 16) if e % 2 else (word & 0xFFFF)
+    return half << 16
+
+
 def pin_stochastic_rounding_in_the_update(orc):
-    """A stored 16-bit state is SR of the unrounded state with the random word
-    of its element: word e % 4 of Philox(counter = (e / 4, row lo, row hi, 0),
-    key = seed), e the element's index within the slot and row the token's
-    packed row; rounds as given."""
+    """A stored 16-bit state is SR of the unrounded state with the random bits
+    of its element (layout in `_sr_word`; e the element's index within the slot,
+    row the token's packed row); rounds as given."""
     rng = np.random.default_rng(53)
     H, P, N, G, L = 2, 3, 8, 1, 3
     pb = _rand_problem(rng, rows=L, H=H, P=P, N=N, G=G, nslots=2 * L)
@@ -614,8 +625,7 @@ def pin_stochastic_rounding_in_the_update(orc):
         assert np.array_equal(plain.out, sr.out)
         for t in range(L):
             vals = plain.state[dtab[0, t]].reshape(-1)
-            words = np.array([orc.philox4x32([e // 4, t, 0, 0],
-                                             [seed & 0xFFFFFFFF, seed >> 32], rounds)[e % 4]
+            words = np.array([_sr_word(orc, e, t, seed, rounds, fmt)
                               for e in range(vals.shape[0])], dtype=np.uint32)
             want = orc.round_stochastic(vals, words, fmt)
             assert np.array_equal(sr.state[dtab[0, t]].reshape(-1), want), (fmt, t)

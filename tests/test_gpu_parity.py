@@ -59,6 +59,15 @@ def test_named_workload(name):
     w = wl.NAMED[name](DEV)
     out, after, before = hz.gpu_run(w)
     written, untouched = hz.check_placement(name, w, out, after, before)
+    if hz.sr_args(w):
+        # Stochastic rounding numbers rows, so the sample is a prefix of sequences.
+        seqs = list(range(12))
+        rows, out_ref, slots, state_sr = hz.oracle_sample(w, seqs, before)
+        _, _, _, state_plain = hz.oracle_sample(w, seqs, before, rounding=False)
+        e_out = hz.check_out_rows(name + " out", out, rows, out_ref)
+        e_st = hz.check_slots_sr(name + " state", after, before, slots, state_sr, state_plain)
+        _say(f"[parity] {name}: rounding flips {e_st:.2e}")
+        return
     seqs = _sample(w, untouched)
     rows, out_ref, slots, state_ref = hz.oracle_sample(w, seqs, before)
     e_out = hz.check_out_rows(name + " out", out, rows, out_ref)
@@ -308,3 +317,67 @@ def test_tied_parameter_views_bit_identical():
     w.D = w.D[:, None].contiguous()
     o2, s2, _ = hz.gpu_run(w)
     assert torch.equal(hz.bits(o1), hz.bits(o2)) and torch.equal(hz.bits(s1), hz.bits(s2))
+
+
+# ------------------------------------------------------- stochastic rounding
+
+@pytest.mark.parametrize("state_dtype,mode,rounds", [("bf16", "one_token", 10),
+                                                      ("f16", "one_token", 10),
+                                                      ("bf16", "packed", 7),
+                                                      ("f16", "packed", 10)])
+def test_stochastic_rounding(state_dtype, mode, rounds):
+    """Stored 16-bit states equal the oracle's stochastic rounding with the same
+    Philox words (up to rare threshold flips between the fp32 and fp64 states);
+    out and placement are those of the round-to-nearest call."""
+    if mode == "one_token":
+        w = wl.one_token("sr", 1001, batch=9, H=8, P=64, N=128, G=2, nslots=24, device=DEV,
+                         state_dtype=state_dtype, io="bf16", pad_fraction=0.2,
+                         dst_mode="distinct")
+    else:
+        w = wl.packed("sr", 1002, nseq=7, max_len=4, H=4, P=64, N=64, G=1, nslots=40,
+                      device=DEV, state_dtype=state_dtype, lengths=[3, 1, 4, 0, 2, 4, 1],
+                      pad_fraction=0.15)
+    w.rand_seed = torch.tensor([0x0123_4567_89AB_CDEF], dtype=torch.int64, device=DEV)
+    w.philox_rounds = rounds
+    out, after, before = hz.gpu_run(w)
+    hz.check_placement("sr", w, out, after, before)
+    ref_sr = hz.oracle_full(w)
+    ref_plain = hz.oracle_full(w, rounding=False)
+    hz.check_out_rows("sr out", out, np.arange(w.rows), ref_plain.out)
+    rate = hz.check_slots_sr("sr state", after, before, list(range(w.state.shape[0])),
+                             ref_sr.state, ref_plain.state)
+    seed = w.rand_seed
+    w.rand_seed = None
+    out_rne, _, _ = hz.gpu_run(w)
+    assert torch.equal(hz.bits(out), hz.bits(out_rne))
+    _say(f"[parity] stochastic rounding {state_dtype} {mode}: flip rate {rate:.2e}")
+    del seed
+
+
+def test_stochastic_rounding_leaves_fp32_state_alone():
+    w = wl.one_token("sr32", 1003, batch=5, H=4, P=64, N=128, G=1, nslots=12, device=DEV)
+    o1, s1, _ = hz.gpu_run(w)
+    w.rand_seed = torch.tensor([99], dtype=torch.int64, device=DEV)
+    o2, s2, _ = hz.gpu_run(w)
+    assert torch.equal(hz.bits(o1), hz.bits(o2)) and torch.equal(hz.bits(s1), hz.bits(s2))
+
+
+def test_stochastic_rounding_is_unbiased_on_average():
+    """Averaged over 64 seeds, the stored bf16 state of a fixed update is closer to
+    the fp32 state than its round-to-nearest value is, on average."""
+    w = wl.one_token("srmean", 1004, batch=4, H=4, P=64, N=128, G=1, nslots=8, device=DEV,
+                     state_dtype="bf16", io="bf16", dst_mode="distinct")
+    w32 = wl.one_token("srmean", 1004, batch=4, H=4, P=64, N=128, G=1, nslots=8, device=DEV,
+                       state_dtype="bf16", io="bf16", dst_mode="distinct")
+    w32.state = w32.state.float()
+    _, exact, _ = hz.gpu_run(w32)
+    _, rne, _ = hz.gpu_run(w)
+    dst = w.dst.long()
+    acc = torch.zeros_like(exact[dst])
+    for k in range(64):
+        w.rand_seed = torch.tensor([1000 + k], dtype=torch.int64, device=DEV)
+        _, sr, _ = hz.gpu_run(w)
+        acc += sr[dst].float()
+    mean_err = (acc / 64 - exact[dst]).abs().mean().item()
+    rne_err = (rne[dst].float() - exact[dst]).abs().mean().item()
+    assert mean_err < 0.5 * rne_err, (mean_err, rne_err)

@@ -69,8 +69,10 @@ MUTANTS = [
     ("philox_multiplier_swap", "const uint64_t p0 = (uint64_t)M0 * c0;", "const uint64_t p0 = (uint64_t)M1 * c0;"),
     ("philox_no_key_bump", "            k0 += W0;\n            k1 += W1;\n", "            k1 += W1;\n"),
     ("philox_key_words_swapped", "const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;", "const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k1;"),
-    ("sr_counter_element", "const uint32_t ctr[4] = {(uint32_t)(e / 4),", "const uint32_t ctr[4] = {(uint32_t)(e),"),
-    ("sr_word_index", "words[e % 4]", "words[0]"),
+    ("sr_counter_element", "const uint32_t ctr[4] = {(uint32_t)(e / group),", "const uint32_t ctr[4] = {(uint32_t)(e),"),
+    ("sr_word_index", "w = words[e % 4];", "w = words[0];"),
+    ("sr_bf16_half_swapped", "(e % 2) ? (word >> 16) : (word & 0xFFFFu)", "(e % 2) ? (word & 0xFFFFu) : (word >> 16)"),
+    ("sr_bf16_group", "const int64_t group = bf16 ? 8 : 4;", "const int64_t group = 4;"),
     ("sr_row_of_token", "store_state(state_out + w * slot_elems, s, slot_elems, begin + t, rounding);", "store_state(state_out + w * slot_elems, s, slot_elems, begin, rounding);"),
     ("ring_position_not_strided", "const int64_t s = slots[i * slot_stride];\n        if (!slot_valid(s, pad_slot_id, num_states)) continue;\n        if (reset)",
      "const int64_t s = slots[i];\n        if (!slot_valid(s, pad_slot_id, num_states)) continue;\n        if (reset)"),
