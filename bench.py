@@ -138,6 +138,7 @@ def make_call(w, hpb, lpl=0, order=0):
     out = torch.empty_like(w.x)
     common = dict(D=w.D, z=w.z, dt_bias=w.dt_bias, dt_softplus=w.dt_softplus,
                   pad_slot_id=w.pad_slot_id, disable_state_update=w.disable_state_update,
+                  rand_seed=w.rand_seed, philox_rounds=w.philox_rounds,
                   heads_per_block=hpb, loads_per_lane=lpl, tile_order=order)
     if w.mode == "one_token":
         return lambda: ssu.ssu_one_token(state, w.x, w.dt, w.A, w.B, w.C, out,
@@ -445,8 +446,8 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for name in ("tiny", "bf16_state", "nemotron_h", "nemotron_h_readonly", "packed_mtp",
-                     "dense_mtp"):
+        for name in ("tiny", "bf16_state", "bf16_state_sr", "nemotron_h", "nemotron_h_readonly",
+                     "packed_mtp", "dense_mtp"):
             if name == args.workload:
                 continue
             rec = run_workload(name, max(20, args.steps // 2), max(5, args.warmup // 2),

@@ -51,6 +51,19 @@
  * reads, cu_seqlens is non-decreasing, and `out` does not overlap any input.
  * A sequence may write the slot it reads (in-place update).
  *
+ * Stochastic rounding. With a 16-bit state and rand_seed set, every stored state
+ * element is rounded stochastically instead of to nearest: with q the spacing of
+ * the state format at |v|, m = floor(|v| / q) and frac = |v| / q - m, the stored
+ * magnitude is (m + 1) q when U >= 1 - frac and m q otherwise (infinite past the
+ * largest finite value), U being a uniform number of 16 (bf16) or 24 (fp16) bits
+ * taken from the top of a random word. Element e = (h * headdim + p) * dstate + n
+ * of the state written by packed row r (row b for ssu_one_token) uses word e % 4
+ * of Philox4x32 (Salmon et al., SC'11) with philox_rounds rounds, counter
+ * (e / 4, r mod 2^32, r / 2^32, 0) and key (seed mod 2^32, seed / 2^32). The vLLM
+ * dispatch page forwards exactly these two knobs (a device seed and a round count,
+ * 10 by default) when stochastic rounding is enabled; the rule and the counter
+ * layout are this library's. `out` is always rounded to nearest.
+ *
  * Errors. Each entry point returns an ssu_status. On failure nothing is launched
  * and ssu_last_error() names the offending argument or capability. Calls from
  * different host threads are independent; the error text is per thread.
@@ -115,6 +128,10 @@ typedef struct ssu_operands {
 
     int64_t pad_slot_id;      /* slot id meaning "no slot"; -1 by convention */
     int32_t disable_state_update; /* nonzero: compute out, write no state */
+    const void *rand_seed;    /* device pointer to one int64 seed, or NULL: with a
+                                 16-bit state, stored states are rounded
+                                 stochastically (no effect on an fp32 state) */
+    int32_t philox_rounds;    /* Philox rounds for rand_seed; 0 means 10 */
 
     int32_t heads_per_block;  /* launch shape: heads of one group per workgroup,
                                  0 = library default, else 1, 2 or 4 dividing

@@ -92,8 +92,20 @@ def _per_head(name, t, heads):
     return t.contiguous()
 
 
+def _seed(rand_seed, device):
+    if rand_seed is None:
+        return None
+    if rand_seed.dtype != torch.int64 or rand_seed.numel() != 1:
+        raise ValueError(f"rand_seed must be a one-element int64 tensor, got {rand_seed.dtype} "
+                         f"{tuple(rand_seed.shape)}")
+    if rand_seed.device != device:
+        raise ValueError(f"rand_seed is on {rand_seed.device}, state is on {device}")
+    return rand_seed
+
+
 def _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus, pad_slot_id,
-              disable_state_update, heads_per_block, loads_per_lane, tile_order):
+              disable_state_update, heads_per_block, loads_per_lane, tile_order,
+              rand_seed=None, philox_rounds=10):
     if state.dim() != 4:
         raise ValueError(f"state must be [slots, heads, dim, dstate], got {tuple(state.shape)}")
     if state.dtype not in _STATE_DTYPES:
@@ -141,6 +153,7 @@ def _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus, pad_slot_i
         dt=_ptr(dt), dt_per_dim=dt_per_dim, A=_ptr(A), D=_ptr(D), dt_bias=_ptr(dt_bias),
         dt_softplus=int(bool(dt_softplus)), pad_slot_id=int(pad_slot_id),
         disable_state_update=int(bool(disable_state_update)),
+        rand_seed=_ptr(_seed(rand_seed, state.device)), philox_rounds=int(philox_rounds),
         heads_per_block=int(heads_per_block), loads_per_lane=int(loads_per_lane),
         tile_order=int(tile_order))
     return op, out, rows
@@ -173,16 +186,19 @@ def _raise(lib, rc, entry):
 
 def ssu_one_token(state, x, dt, A, B, C, out=None, *, D=None, z=None, dt_bias=None,
                   dt_softplus=False, state_batch_indices=None, dst_state_batch_indices=None,
-                  pad_slot_id=-1, disable_state_update=False, heads_per_block=0,
-                  loads_per_lane=0, tile_order=0, stream=None):
+                  pad_slot_id=-1, disable_state_update=False, rand_seed=None,
+                  philox_rounds=10, heads_per_block=0, loads_per_lane=0, tile_order=0,
+                  stream=None):
     """One decode token per sequence (row b is sequence b). Updates `state` in place
     at the destination slots and returns `out` [batch, heads, dim].
+    rand_seed (a one-element int64 device tensor) turns on stochastic rounding of
+    stored fp16/bf16 states with Philox4x32-`philox_rounds`.
     heads_per_block / loads_per_lane / tile_order pick the launch shape (0: the
     library default)."""
     lib = library()
     op, out, batch = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
                                pad_slot_id, disable_state_update, heads_per_block,
-                               loads_per_lane, tile_order)
+                               loads_per_lane, tile_order, rand_seed, philox_rounds)
     src, src_dt = _index("state_batch_indices", state_batch_indices, state.device)
     dst, dst_dt = _index("dst_state_batch_indices", dst_state_batch_indices, state.device)
     for name, t in (("state_batch_indices", src), ("dst_state_batch_indices", dst)):
@@ -226,8 +242,8 @@ def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens=None, out=None, *,
                       num_accepted_tokens=None, state_batch_indices=None,
                       dst_state_batch_indices=None, D=None, z=None, dt_bias=None,
                       dt_softplus=False, pad_slot_id=-1, disable_state_update=False,
-                      steps=None, heads_per_block=0, loads_per_lane=0, tile_order=0,
-                      stream=None):
+                      rand_seed=None, philox_rounds=10, steps=None, heads_per_block=0,
+                      loads_per_lane=0, tile_order=0, stream=None):
     """Packed variable-length multi-token update. Returns `out`.
 
     x is the packed [rows, heads, dim] form, sequence b owning rows
@@ -257,7 +273,7 @@ def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens=None, out=None, *,
             seq_len = max(dsteps, 1)
     op, out, rows = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
                               pad_slot_id, disable_state_update, heads_per_block,
-                              loads_per_lane, tile_order)
+                              loads_per_lane, tile_order, rand_seed, philox_rounds)
     cu, meta = _index("cu_seqlens", cu_seqlens, state.device)
     na, na_dt = _index("num_accepted_tokens", num_accepted_tokens, state.device)
     if cu is not None:

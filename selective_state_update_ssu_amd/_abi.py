@@ -24,6 +24,7 @@ class Operands(ctypes.Structure):
         ("dt", c_void_p), ("dt_per_dim", c_int32),
         ("A", c_void_p), ("D", c_void_p), ("dt_bias", c_void_p), ("dt_softplus", c_int32),
         ("pad_slot_id", c_int64), ("disable_state_update", c_int32),
+        ("rand_seed", c_void_p), ("philox_rounds", c_int32),
         ("heads_per_block", c_int32), ("loads_per_lane", c_int32), ("tile_order", c_int32),
     ]
 

@@ -94,6 +94,9 @@ int check_operands(const ssu_operands& op, int64_t rows, bool work, bool packed)
     if (hpb > 1 && hpg % hpb != 0)
         return fail(SSU_ERR_INVALID_ARGUMENT,
                     "heads_per_block (%d) must divide nheads / ngroups (%lld)", hpb, (long long)hpg);
+    if (op.philox_rounds < 0 || op.philox_rounds > 64)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "philox_rounds must be in [0, 64], got %d",
+                    op.philox_rounds);
     if (op.tile_order < 0 || op.tile_order > 2)
         return fail(SSU_ERR_INVALID_ARGUMENT, "tile_order must be 0, 1 or 2, got %d", op.tile_order);
     if (op.loads_per_lane != 0 && op.loads_per_lane != 2 && op.loads_per_lane != 4)
@@ -128,7 +131,7 @@ int check_operands(const ssu_operands& op, int64_t rows, bool work, bool packed)
         size_t a;
     } al[] = {{"x", op.x, iosz},  {"B", op.B, iosz},   {"C", op.C, iosz}, {"z", op.z, iosz},
               {"out", op.out, iosz}, {"dt", op.dt, 4}, {"A", op.A, 4},    {"D", op.D, 4},
-              {"dt_bias", op.dt_bias, 4}};
+              {"dt_bias", op.dt_bias, 4}, {"rand_seed", op.rand_seed, 8}};
     for (const auto& q : al)
         if (q.p && reinterpret_cast<uintptr_t>(q.p) % q.a != 0)
             return fail(SSU_ERR_INVALID_ARGUMENT, "%s is not aligned to its element size", q.name);
@@ -165,10 +168,13 @@ struct Shape {
 Shape default_shape(const ssu_operands& op, bool packed) {
     const bool read_only = op.disable_state_update != 0;
     Shape s;
+    const bool sr = op.rand_seed && op.state_dtype != SSU_F32 && !read_only;
     if (packed)
         s = {2, 4, 0};
     else if (read_only)
         s = {2, 4, 1};
+    else if (sr)  // the Philox work of stochastic rounding wants bigger tiles
+        s = {1, 4, 1};
     else
         s = {op.state_dtype == SSU_F32 ? 2 : 1, 2, 1};
     const int64_t hpg = op.nheads / op.ngroups;
@@ -189,6 +195,9 @@ void fill_common(ssu::KernelParams& k, const ssu_operands& op, bool packed) {
     k.A = op.A;
     k.D = op.D;
     k.dt_bias = op.dt_bias;
+    // Stochastic rounding only changes 16-bit stores.
+    k.rand_seed = op.state_dtype == SSU_F32 ? nullptr : static_cast<const int64_t*>(op.rand_seed);
+    k.philox_rounds = op.philox_rounds ? op.philox_rounds : 10;
     k.nslots = op.nslots;
     k.pad_slot_id = op.pad_slot_id;
     k.nheads = static_cast<int32_t>(op.nheads);
@@ -219,9 +228,9 @@ int launch(const ssu::KernelParams& k, const ssu_operands& op, int64_t nseq, voi
     if (log_enabled())
         std::fprintf(stderr,
                      "[ssu] %s: state=%s io=%s dstate=%d heads_per_block=%d loads_per_lane=%d "
-                     "xcd_order=%d rows_per_block=%u grid=%u block=%u lds=%u B -> %s\n",
+                     "xcd_order=%d sr=%d rows_per_block=%u grid=%u block=%u lds=%u B -> %s\n",
                      entry, dtype_name(op.state_dtype), dtype_name(io), N, k.heads_per_block,
-                     k.loads_per_lane, k.xcd_order,
+                     k.loads_per_lane, k.xcd_order, k.rand_seed != nullptr,
                      shape.rows_per_block, shape.grid, shape.block, shape.lds_bytes,
                      hipGetErrorString(e));
     if (e == hipErrorInvalidConfiguration)

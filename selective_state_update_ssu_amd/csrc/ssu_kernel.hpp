@@ -137,6 +137,75 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// ------------------------------------------------------- stochastic rounding
+
+// Philox4x32 (Salmon, Moraes, Dror, Shaw, SC'11): per round, the products of
+// counter words 0 and 2 with the two multipliers; high halves are mixed with the
+// other counter words and the key, low halves pass through; the key steps by the
+// two Weyl increments between rounds.
+__device__ __forceinline__ void philox4x32_rounds(uint32_t (&c)[4], uint32_t k0, uint32_t k1,
+                                                  int rounds) {
+#pragma unroll 10
+    for (int r = 0; r < rounds; ++r) {
+        if (r) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        // One 32x32->64 multiply-add each (v_mad_u64_u32) gives both halves.
+        const uint64_t p0 = static_cast<uint64_t>(c[0]) * 0xD2511F53u;
+        const uint64_t p1 = static_cast<uint64_t>(c[2]) * 0xCD9E8D57u;
+        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c[1] ^ k0;
+        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = static_cast<uint32_t>(p1);
+        c[2] = n2;
+        c[3] = static_cast<uint32_t>(p0);
+    }
+}
+
+// The round count is a run-time value; the common 10 gets a fully unrolled copy.
+__device__ __forceinline__ void philox4x32(uint32_t (&c)[4], uint32_t k0, uint32_t k1,
+                                           int rounds) {
+    if (rounds == 10)
+        philox4x32_rounds(c, k0, k1, 10);
+    else
+        philox4x32_rounds(c, k0, k1, rounds);
+}
+
+// A power of two 2^k for k in [-126, 127], exactly.
+__device__ __forceinline__ float pow2f(int k) {
+    return __uint_as_float(static_cast<unsigned>(127 + k) << 23);
+}
+
+// Stochastic rounding of v with random word w (its top bits used), as 16-bit
+// patterns. bf16: adding the word's top 16 bits below the bf16 mantissa and
+// truncating rounds away from zero exactly when U >= 1 - frac (U = those bits /
+// 2^16).
+__device__ __forceinline__ unsigned sr_bits_bf16(float v, uint32_t w) {
+    const unsigned u = __float_as_uint(v);
+    if ((u & 0x7f800000u) == 0x7f800000u)  // inf, nan: plain conversion
+        return __builtin_bit_cast(unsigned short, static_cast<__bf16>(v));
+    return (u + (w >> 16)) >> 16;
+}
+
+// fp16: by exact power-of-two scaling to the fp16 spacing at |v| (normals share
+// exponent -14 with the subnormals below them); the threshold U >= 1 - frac is
+// decided as the sign of (U - 1) + frac, which rounding cannot change.
+__device__ __forceinline__ unsigned sr_bits_f16(float v, uint32_t w) {
+    const float a = fabsf(v);
+    if (!(a < __builtin_inff()) || a == 0.f)
+        return __builtin_bit_cast(unsigned short, static_cast<_Float16>(v));
+    const int e = static_cast<int>(__float_as_uint(a) >> 23) - 127;
+    const int qexp = (e > -14 ? e : -14) - 10;
+    const float t = a * pow2f(-qexp);
+    const float m = floorf(t);
+    const float frac = t - m;
+    const float U = static_cast<float>(w >> 8) * pow2f(-24);
+    float r = (m + (((U - 1.f) + frac >= 0.f) ? 1.f : 0.f)) * pow2f(qexp);
+    if (r > 65504.f) r = __builtin_inff();
+    return __builtin_bit_cast(unsigned short, static_cast<_Float16>(copysignf(r, v)));
+}
+
 // ------------------------------------------------------------------- math
 
 __device__ __forceinline__ float softplus_f32(float v) {
@@ -198,7 +267,7 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t n) {
 
 // ------------------------------------------------------------------ kernel
 
-template <typename ST, typename IT, int N, int LOADS, bool PACKED>
+template <typename ST, typename IT, int N, int LOADS, bool PACKED, bool SR>
 __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void ssu_update_kernel(
     const KernelParams p) {
     // Lane geometry.
@@ -272,6 +341,12 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
     if (!slot_ok(r, p)) return;
 
     // ---- per-head constants
+    uint32_t key0 = 0, key1 = 0;
+    if constexpr (SR) {
+        const uint64_t seed = static_cast<uint64_t>(uniform64(*p.rand_seed));
+        key0 = static_cast<uint32_t>(seed);
+        key1 = static_cast<uint32_t>(seed >> 32);
+    }
     const float a_h = p.A[h];
     const float d_h = p.D ? p.D[h] : 0.f;
     const float bias_h = p.dt_bias ? p.dt_bias[h] : 0.f;
@@ -454,8 +529,51 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
 #pragma unroll
             for (int i = 0; i < RL; ++i) {
                 words_t o;
+                if constexpr (SR) {
+                    // Random bits for this lane's VEC elements e0 .. e0 + VEC - 1:
+                    // fp16 takes the top 24 bits of word e % 4 of Philox(e / 4, row);
+                    // bf16 the low / high half (even / odd e) of word (e % 8) / 2 of
+                    // Philox(e / 8, row).
+                    const int64_t row = begin + t;
+                    const uint32_t rlo = static_cast<uint32_t>(row);
+                    const uint32_t rhi = static_cast<uint32_t>(static_cast<uint64_t>(row) >> 32);
+                    const uint32_t e0 =
+                        static_cast<uint32_t>((static_cast<int64_t>(h) * P + prow_of[i]) * N + n0);
+                    unsigned half[VEC];
+                    if constexpr (__is_same(ST, __bf16)) {
+                        constexpr int PER = VEC < 8 ? VEC : 8;  // elements per call here
 #pragma unroll
-                for (int k = 0; k < W; ++k) o[k] = Pack<ST>::narrow(&s[i][k * Pack<ST>::kPerWord]);
+                        for (int j = 0; j < VEC / PER; ++j) {
+                            uint32_t c[4] = {e0 / 8 + j, rlo, rhi, 0u};
+                            philox4x32(c, key0, key1, p.philox_rounds);
+                            // VEC = 4 (dstate 16): e0 % 8 is 0 or 4, i.e. words 0-1 or 2-3.
+                            const bool upper = PER < 8 && (e0 & 4u);
+                            const uint32_t wsel[4] = {upper ? c[2] : c[0], upper ? c[3] : c[1],
+                                                      c[2], c[3]};
+#pragma unroll
+                            for (int k = 0; k < PER; ++k) {
+                                const uint32_t word = wsel[k / 2];
+                                const uint32_t bits = (k & 1) ? (word >> 16) : (word & 0xFFFFu);
+                                half[PER * j + k] = sr_bits_bf16(s[i][PER * j + k], bits << 16);
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < VEC / 4; ++j) {
+                            uint32_t c[4] = {e0 / 4 + j, rlo, rhi, 0u};
+                            philox4x32(c, key0, key1, p.philox_rounds);
+#pragma unroll
+                            for (int k = 0; k < 4; ++k)
+                                half[4 * j + k] = sr_bits_f16(s[i][4 * j + k], c[k]);
+                        }
+                    }
+#pragma unroll
+                    for (int k = 0; k < W; ++k) o[k] = half[2 * k] | (half[2 * k + 1] << 16);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < W; ++k)
+                        o[k] = Pack<ST>::narrow(&s[i][k * Pack<ST>::kPerWord]);
+                }
                 if (full_block || prow_of[i] < P)
                     __builtin_nontemporal_store(o, reinterpret_cast<words_t*>(tile + off[i]));
             }
@@ -475,10 +593,23 @@ hipError_t launch_instance(KernelParams p, int64_t nseq, hipStream_t stream, Lau
     const dim3 block(static_cast<unsigned>(kHeadThreads * p.heads_per_block));
     const unsigned lds = lds_bytes(N, p.heads_per_block, RB, p.packed ? kStageTokens : 1);
     if (shape) *shape = LaunchShape{grid.x, block.x, lds, static_cast<unsigned>(RB)};
+    if constexpr (sizeof(ST) == 2) {
+        if (p.rand_seed) {
+            if (p.packed)
+                hipLaunchKernelGGL((ssu_update_kernel<ST, IT, N, LOADS, true, true>), grid, block,
+                                   lds, stream, p);
+            else
+                hipLaunchKernelGGL((ssu_update_kernel<ST, IT, N, LOADS, false, true>), grid,
+                                   block, lds, stream, p);
+            return hipGetLastError();
+        }
+    }
     if (p.packed)
-        hipLaunchKernelGGL((ssu_update_kernel<ST, IT, N, LOADS, true>), grid, block, lds, stream, p);
+        hipLaunchKernelGGL((ssu_update_kernel<ST, IT, N, LOADS, true, false>), grid, block, lds,
+                           stream, p);
     else
-        hipLaunchKernelGGL((ssu_update_kernel<ST, IT, N, LOADS, false>), grid, block, lds, stream, p);
+        hipLaunchKernelGGL((ssu_update_kernel<ST, IT, N, LOADS, false, false>), grid, block, lds,
+                           stream, p);
     return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ struct KernelParams {
     const float* A;
     const float* D;        // may be null
     const float* dt_bias;  // may be null
+    const int64_t* rand_seed;  // may be null: round stored 16-bit states to nearest
 
     // Slot resolution.
     const void* src;    // one-token: [batch] vector; packed: table; may be null
@@ -60,6 +61,7 @@ struct KernelParams {
     int32_t dt_per_dim;
     int32_t dt_softplus;
     int32_t disable_state_update;
+    int32_t philox_rounds;
 };
 
 // Compute dies (XCDs) the hardware deals consecutive workgroups to, round robin.

@@ -29,6 +29,7 @@ Named workloads (one GPU each, at their real decode shapes):
               5 % of sequences have an all-pad table row.
   dense_mtp   the Mamba2-2.7B shape in the dense [256, 2, ...] layout (one draft
               token per sequence), slot table [256, 2] of 1024 slots, 5 % pads.
+  bf16_state_sr  bf16_state with stochastic rounding of the stored states.
 """
 from __future__ import annotations
 
@@ -83,6 +84,8 @@ class Workload:
     D: Optional[torch.Tensor] = None       # [H] fp32
     z: Optional[torch.Tensor] = None       # [rows, H, P]
     dt_bias: Optional[torch.Tensor] = None  # [H] fp32
+    rand_seed: Optional[torch.Tensor] = None  # [1] int64: stochastic rounding of 16-bit state
+    philox_rounds: int = 10
     dt_softplus: bool = True
     pad_slot_id: int = -1
     disable_state_update: bool = False
@@ -254,6 +257,14 @@ def dense_mtp(device, seed=5):
                   with_z=True, pad_fraction=0.05, dense=True)
 
 
+def bf16_state_sr(device, seed=2):
+    """bf16_state with stochastic rounding of the stored states (seeded Philox)."""
+    w = bf16_state(device, seed)
+    w.name = "bf16_state_sr"
+    w.rand_seed = torch.tensor([0x5EED_0000_2B16 + seed], dtype=torch.int64, device=device)
+    return w
+
+
 def packed_mtp(device, seed=4):
     return packed("packed_mtp", seed, nseq=256, max_len=4, H=80, P=64, N=128, G=1,
                   nslots=2048, device=device, state_dtype="f32", io="bf16",
@@ -268,4 +279,5 @@ NAMED = {
     "nemotron_h_readonly": lambda device, seed=3: nemotron_h(device, seed, True),
     "packed_mtp": packed_mtp,
     "dense_mtp": dense_mtp,
+    "bf16_state_sr": bf16_state_sr,
 }
