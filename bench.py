@@ -295,6 +295,31 @@ def torch_index(idx):
 
 # ------------------------------------------------------------ profile summary
 
+def readable_kernel_name(mangled):
+    """ssu_update_kernel<state, io, dstate, loads per lane, packed, stochastic>
+    from the mangled name (the template arguments of this one kernel)."""
+    import re
+    m = re.match(r"_ZN3ssu17ssu_update_kernelI(.*)EEvNS_12KernelParamsE$", mangled)
+    if not m:
+        return mangled
+    types = {"f": "float", "DF16_": "_Float16", "DF16b": "__bf16"}
+    args, rest = [], m.group(1)
+    while rest:
+        for code, name in types.items():
+            if rest.startswith(code):
+                args.append(name)
+                rest = rest[len(code):]
+                break
+        else:
+            lit = re.match(r"L([ib])(\d+)E", rest)
+            if not lit:
+                return mangled
+            args.append(("true" if lit.group(2) == "1" else "false") if lit.group(1) == "b"
+                         else lit.group(2))
+            rest = rest[lit.end():]
+    return f"ssu_update_kernel<{', '.join(args)}>"
+
+
 def _csv_rows(pattern):
     import csv
     rows = []
@@ -340,7 +365,7 @@ def summarize(prof_dir, workload, cmd):
     traffic = read_b + write_b
     algo_read, algo_write = acc["read_bytes"], acc["write_bytes"]
     gbps = acc["bytes"] / (avg_ns * 1e-9) / 1e9
-    short = kname.replace("_ZN3ssu17ssu_update_kernelI", "ssu_update_kernel<").split("EEEv")[0]
+    short = readable_kernel_name(kname)
     md = f"""# {short} on {workload}
 
 Kernel: `{kname}`
