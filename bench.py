@@ -188,7 +188,41 @@ def stream_library():
     lib.ssu_stream_write.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.ssu_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                     ctypes.c_void_p]
+    lib.ssu_stream_fanout.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p]
     return lib
+
+
+def pattern_ceiling(w, steps, warmup):
+    """Launch time of the packed call's state traffic alone (each live sequence's
+    tiles read once from the read slot and written to every valid destination,
+    no arithmetic) on the workload's own tensors, or None where the streaming
+    kernel does not apply (one-token calls, separate read and write tables, head
+    tiles not a multiple of 8 KiB)."""
+    import torch
+
+    if w.mode != "packed" or w.src_table is None or w.src_table is not w.dst_table:
+        return None
+    nslots, H, P, N = w.state.shape
+    head_bytes = P * N * w.state.element_size()
+    if H % 4 or head_bytes % 8192:
+        return None
+    table = w.src_table.to(torch.int32).contiguous()
+    nseq = table.shape[0]
+    acc = (w.num_accepted if w.num_accepted is not None
+           else torch.ones(nseq, device=table.device)).to(torch.int32).contiguous()
+    starts = w.cu_seqlens.to(torch.int32).contiguous()
+    lib = stream_library()
+    s = torch.cuda.current_stream().cuda_stream
+    call = lambda: lib.ssu_stream_fanout(w.state.data_ptr(), nslots, H, head_bytes,
+                                         table.data_ptr(), table.shape[1], acc.data_ptr(),
+                                         starts.data_ptr(), nseq, s)
+    if call() != 0:
+        raise RuntimeError("ssu_stream_fanout failed")
+    _, ev = time_calls(call, steps, warmup)
+    return ev * 1e3
 
 
 def ceilings(steps=30, nbytes=2 << 30, kinds=("copy", "read", "write")):
@@ -431,6 +465,12 @@ def run_workload(name, steps, warmup, hpb, lpl=0):
                tokens_per_s=acc["live_rows"] / (wall * 1e-3),
                hbm_gbps=acc["bytes"] / (ev * 1e-3) / 1e9, **acc)
     rec["frac_of_peak"] = rec["hbm_gbps"] / HBM_PEAK_GBPS
+    pattern_us = pattern_ceiling(w, steps, warmup)
+    if pattern_us is not None:
+        # The same state reads and writes with no arithmetic: how close the
+        # kernel comes to pure data movement of its own access pattern.
+        rec["state_traffic_only_us"] = pattern_us
+        rec["frac_of_state_traffic_only"] = pattern_us / rec["kernel_us"]
     del w
     torch.cuda.empty_cache()
     return rec
@@ -478,7 +518,9 @@ def main():
             rec = run_workload(name, max(20, args.steps // 2), max(5, args.warmup // 2),
                                args.heads_per_block, args.loads_per_lane)
             extra[name] = {k: rec[k] for k in ("tokens_per_s", "hbm_gbps", "frac_of_peak",
-                                               "kernel_us", "ms_per_step", "bytes", "live_rows")}
+                                               "kernel_us", "ms_per_step", "bytes", "live_rows",
+                                               "state_traffic_only_us",
+                                               "frac_of_state_traffic_only") if k in rec}
             print(f"[bench] {name}: {rec['kernel_us']:.1f} us/launch, {rec['hbm_gbps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
     ceil = ceilings()

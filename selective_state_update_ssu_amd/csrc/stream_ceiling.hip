@@ -57,6 +57,53 @@ __global__ __launch_bounds__(kThreads) void write_kernel(u32x4* __restrict__ dst
     }
 }
 
+// The state traffic of a packed multi-token call without its arithmetic: for
+// every (sequence, head, block of the head's tile) the block is read once from
+// the sequence's read slot and written to each valid destination slot of the
+// sequence's table row, in the same order of workgroups as the SSU kernel. Four
+// heads per workgroup, two 16-byte vectors per lane, non-temporal: the fastest
+// of the shapes tried for this pattern.
+constexpr int kFanHeads = 4;
+constexpr int kFanLoads = 2;
+constexpr size_t kFanBlock = size_t(kThreads) * kFanLoads * sizeof(u32x4);  // bytes per head
+
+struct FanParams {
+    char* state;
+    size_t slot_bytes, head_bytes;
+    const int* table;    // [nseq, steps]
+    const int* accepted; // [nseq], entries in [1, steps]
+    const int* starts;   // [nseq + 1]
+    int nslots, steps, head_blocks, tile_blocks;
+};
+
+__global__ __launch_bounds__(kThreads* kFanHeads) void fanout_kernel(const FanParams p) {
+    const int tid = threadIdx.x;
+    const int lh = __builtin_amdgcn_readfirstlane(tid / kThreads);
+    const int ht = tid % kThreads;
+    int64_t wg = blockIdx.x;
+    const int tb = static_cast<int>(wg % p.tile_blocks);
+    wg /= p.tile_blocks;
+    const int64_t h = (wg % p.head_blocks) * kFanHeads + lh;
+    const int64_t seq = wg / p.head_blocks;
+    const int len = p.starts[seq + 1] - p.starts[seq];
+    const int k = p.accepted[seq];
+    if (k < 1 || k > p.steps) return;
+    const int r = __builtin_amdgcn_readfirstlane(p.table[seq * p.steps + k - 1]);
+    if (r < 0 || r >= p.nslots) return;
+    const size_t base = h * p.head_bytes + tb * kFanBlock;
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.state + r * p.slot_bytes + base);
+    u32x4 v[kFanLoads];
+#pragma unroll
+    for (int i = 0; i < kFanLoads; ++i) v[i] = __builtin_nontemporal_load(src + ht + i * kThreads);
+    for (int t = 0; t < len && t < p.steps; ++t) {
+        const int w = __builtin_amdgcn_readfirstlane(p.table[seq * p.steps + t]);
+        if (w < 0 || w >= p.nslots) continue;
+        u32x4* dst = reinterpret_cast<u32x4*>(p.state + w * p.slot_bytes + base);
+#pragma unroll
+        for (int i = 0; i < kFanLoads; ++i) __builtin_nontemporal_store(v[i], dst + ht + i * kThreads);
+    }
+}
+
 dim3 grid_for(size_t bytes) { return dim3(static_cast<unsigned>((bytes + kChunk - 1) / kChunk)); }
 
 int finish() { return hipGetLastError() == hipSuccess ? 0 : 1; }
@@ -88,6 +135,33 @@ int ssu_stream_write(void* dst, size_t bytes, void* stream) {
     hipLaunchKernelGGL(write_kernel, grid_for(bytes), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), static_cast<u32x4*>(dst), bytes / 16,
                        0x3F800000u);
+    return finish();
+}
+
+// Packed-call state traffic (fanout_kernel) over a state cache of `nslots` slots
+// of `nheads` heads of `head_bytes` bytes each. Int32 device arrays: table
+// [nseq, steps], accepted [nseq], starts [nseq + 1]. Returns 2 when nheads is
+// not a multiple of 4 or head_bytes not a multiple of 8 KiB (the kernel's
+// blocking), 0 on a successful launch.
+int ssu_stream_fanout(void* state, int64_t nslots, int64_t nheads, size_t head_bytes,
+                      const void* table, int64_t steps, const void* accepted,
+                      const void* starts, int64_t nseq, void* stream) {
+    if (nheads % kFanHeads || head_bytes % kFanBlock || nslots <= 0 || steps <= 0) return 2;
+    if (nseq == 0) return 0;
+    FanParams p;
+    p.state = static_cast<char*>(state);
+    p.slot_bytes = head_bytes * nheads;
+    p.head_bytes = head_bytes;
+    p.table = static_cast<const int*>(table);
+    p.accepted = static_cast<const int*>(accepted);
+    p.starts = static_cast<const int*>(starts);
+    p.nslots = static_cast<int>(nslots);
+    p.steps = static_cast<int>(steps);
+    p.head_blocks = static_cast<int>(nheads / kFanHeads);
+    p.tile_blocks = static_cast<int>(head_bytes / kFanBlock);
+    const dim3 grid(static_cast<unsigned>(nseq * p.head_blocks * p.tile_blocks));
+    hipLaunchKernelGGL(fanout_kernel, grid, dim3(kThreads * kFanHeads), 0,
+                       static_cast<hipStream_t>(stream), p);
     return finish();
 }
 
