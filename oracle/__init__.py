@@ -5,7 +5,9 @@ CPU-baseline leg of ``bench.py`` may import this package. The GPU library never
 calls it, and it shares no code with the GPU library.
 
 The arithmetic lives in ``ssu_oracle.c`` (plain C, fp64, loops in the order
-sequence -> head -> row -> dstate). This module only compiles it with gcc, loads
+sequence -> head -> row -> dstate): the decode-time selective state update, the
+ReplaySSM ring trackers, Philox4x32 and stochastic rounding, and the SSD chunked
+prefill as the token-by-token recurrence it equals. This module only compiles it with gcc, loads
 it with ctypes and widens operands: every fp16/bf16/fp32 value is exactly
 representable in fp64, so the widening loses nothing.
 """
@@ -98,6 +100,11 @@ class Oracle:
                                            _i64, _i64]
         lib.oracle_ring_commit.argtypes = [_ip, _ip, _ip, _i64, _ip, _i64, _i64, _ip, _ip,
                                            _i64, _i64, _i64]
+        _d = ctypes.c_double
+        lib.oracle_ssd_prefill.restype = _int
+        lib.oracle_ssd_prefill.argtypes = [
+            _i64, _i64, _i64, _i64, _i64, _dp, _dp, _dp, _dp, _dp, _dp, _int, _dp, _dp, _int,
+            _d, _d, _i64, _i64, _ip, _ip, _i64, _ip, _dp, _dp, _dp, _dp]
         self.lib = lib
 
     @staticmethod
@@ -264,6 +271,43 @@ def _ring_commit(self, ring_start, prev_num_accepted, prev_query_len, slots, num
 
 Oracle.ring_update = _ring_update
 Oracle.ring_commit = _ring_commit
+
+
+@dataclass
+class SsdResult:
+    out: np.ndarray            # [tokens, nheads, headdim]; rows no chunk covers keep out_init
+    chunk_states: np.ndarray   # [nchunks, nheads, headdim, dstate]: state after each chunk
+    final_states: np.ndarray   # [batch, nheads, headdim, dstate]: chunk_states[last_chunk_indices]
+
+
+def _ssd_prefill(self, x, dt, A, B, C, chunk_size, cu_chunk_seqlens, seq_idx,
+                 last_chunk_indices, *, D=None, z=None, dt_bias=None, dt_softplus=False,
+                 dt_limit=(0.0, float("inf")), initial_states=None,
+                 out_init=None) -> SsdResult:
+    """SSD chunked prefill over packed tokens (x [tokens, heads, dim], dt
+    [tokens, heads], B/C [tokens, groups, dstate]). D is [heads] or [heads, dim]."""
+    x, dt, A, B, C = (_f64(a) for a in (x, dt, A, B, C))
+    D, z, dt_bias, init = (_f64(a) for a in (D, z, dt_bias, initial_states))
+    tokens, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    cc, si, lci = _idx(cu_chunk_seqlens), _idx(seq_idx), _idx(last_chunk_indices)
+    nchunks, batch = cc.shape[0] - 1, lci.shape[0]
+    D_per_dim = 1 if D is not None and D.ndim == 2 else 0
+    out = np.full(x.shape, np.nan) if out_init is None else _f64(out_init).copy()
+    chunk_states = np.empty((nchunks, H, P, N))
+    final_states = np.empty((batch, H, P, N))
+    rc = self.lib.oracle_ssd_prefill(
+        tokens, H, P, N, G, _p(x, _dp), _p(dt, _dp), _p(A, _dp), _p(B, _dp), _p(C, _dp),
+        _p(D, _dp), D_per_dim, _p(z, _dp), _p(dt_bias, _dp), int(bool(dt_softplus)),
+        float(dt_limit[0]), float(dt_limit[1]), int(chunk_size), nchunks, _p(cc, _ip),
+        _p(si, _ip), batch, _p(lci, _ip), _p(init, _dp), _p(out, _dp),
+        _p(chunk_states, _dp), _p(final_states, _dp))
+    if rc != 0:
+        raise ValueError("oracle_ssd_prefill rejected its arguments")
+    return SsdResult(out, chunk_states, final_states)
+
+
+Oracle.ssd_prefill = _ssd_prefill
 
 
 _DEFAULT: Oracle | None = None

@@ -55,6 +55,13 @@
  *    vLLM `ssu_dispatch` module source (the two tracker kernels and their
  *    wrappers `update_replayssm_ring_trackers` and
  *    `commit_replayssm_ring_trackers`), restated per slot below.
+ *  - SSD chunked prefill: the contract of `ssd_combined_fwd_varlen` on the MATE
+ *    page (its docstring and argument checks). The chunked algorithm computes,
+ *    up to rounding order, the same recurrence run token by token over each
+ *    sequence (the structured-state-space duality of the SSD paper, sections 5
+ *    and 6), so the oracle is that plain recurrence with the contract's chunk
+ *    bookkeeping: which tokens a chunk covers, where its entering state comes
+ *    from, and which states are returned.
  */
 #include "ssu_oracle.h"
 
@@ -389,5 +396,94 @@ int oracle_ring_commit(int64_t *ring_start, int64_t *prev_num_accepted,
         }
         prev_query_len[s] = query_start_loc[i + 1] - query_start_loc[i];
     }
+    return 0;
+}
+
+/*
+ * SSD chunked prefill. Chunk c covers tokens [cu_chunk_seqlens[c],
+ * cu_chunk_seqlens[c+1]). It opens a sequence when c == 0 or seq_idx[c] differs
+ * from seq_idx[c-1]; an opening chunk enters with initial_states[seq_idx[c]]
+ * (zeros without initial states), any other chunk with the state the previous
+ * chunk left. Inside a chunk the tokens run in order through the recurrence:
+ *     v  = dt[t, h] (+ dt_bias[h]);  v = softplus(v) when requested;
+ *     v  = min(max(v, dt_min), dt_max)
+ *     s  = s * exp(A[h] v) + v B[t, g] x[t, h, p]
+ *     y  = C[t, g] . s + D x[t, h, p];  y *= z sigmoid(z) when z is given
+ * chunk_states[c] is the state after the chunk's last token and
+ * final_states[b] = chunk_states[last_chunk_indices[b]].
+ */
+static void ssd_step_token(const problem *pb, int D_per_dim, double dt_min, double dt_max,
+                           double *state, int64_t t, double *out) {
+    const int64_t H = pb->nheads, P = pb->headdim, N = pb->dstate;
+    const int64_t ratio = H / pb->ngroups;
+    for (int64_t h = 0; h < H; ++h) {
+        const int64_t grp = h / ratio;
+        const double *Bt = pb->B + (t * pb->ngroups + grp) * N;
+        const double *Ct = pb->C + (t * pb->ngroups + grp) * N;
+        double u = pb->dt[t * H + h];
+        if (pb->dt_bias) u += pb->dt_bias[h];
+        if (pb->dt_softplus) u = softplus(u);
+        u = fmin(fmax(u, dt_min), dt_max);
+        const double decay = exp(pb->A[h] * u);
+        for (int64_t p = 0; p < P; ++p) {
+            const int64_t i = (t * H + h) * P + p;
+            const double xv = pb->x[i];
+            double *st = state + (h * P + p) * N;
+            double dot = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                st[n] = st[n] * decay + u * Bt[n] * xv;
+                dot += st[n] * Ct[n];
+            }
+            double y = dot;
+            if (pb->D) y += (D_per_dim ? pb->D[h * P + p] : pb->D[h]) * xv;
+            if (pb->z) y *= pb->z[i] * sigmoid(pb->z[i]);
+            out[i] = y;
+        }
+    }
+}
+
+int oracle_ssd_prefill(int64_t tokens, int64_t nheads, int64_t headdim, int64_t dstate,
+                       int64_t ngroups, const double *x, const double *dt, const double *A,
+                       const double *B, const double *C, const double *D, int D_per_dim,
+                       const double *z, const double *dt_bias, int dt_softplus,
+                       double dt_min, double dt_max, int64_t chunk_size, int64_t nchunks,
+                       const int64_t *cu_chunk_seqlens, const int64_t *seq_idx, int64_t batch,
+                       const int64_t *last_chunk_indices, const double *initial_states,
+                       double *out, double *chunk_states, double *final_states) {
+    const problem pb = {1,      nheads, headdim, dstate,  ngroups, x, dt, A,
+                        B,      C,      D,       z,       dt_bias, 0, dt_softplus};
+    if (tokens < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+        nheads % ngroups != 0 || chunk_size <= 0 || nchunks < 1 || batch < 0)
+        return -1;
+    if (!cu_chunk_seqlens || !seq_idx || !chunk_states || (batch > 0 && !last_chunk_indices))
+        return -1;
+    if (tokens > 0 && (!x || !dt || !A || !B || !C || !out)) return -1;
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t lo = cu_chunk_seqlens[c], hi = cu_chunk_seqlens[c + 1];
+        if (lo < 0 || hi < lo || hi > tokens || hi - lo > chunk_size) return -1;
+        if (initial_states && (seq_idx[c] < 0 || seq_idx[c] >= batch)) return -1;
+    }
+    for (int64_t b = 0; b < batch; ++b)
+        if (last_chunk_indices[b] < 0 || last_chunk_indices[b] >= nchunks) return -1;
+
+    const int64_t elems = nheads * headdim * dstate;
+    double *s = (double *)calloc((size_t)elems, sizeof(double));
+    if (!s) return -1;
+    for (int64_t c = 0; c < nchunks; ++c) {
+        if (c == 0 || seq_idx[c] != seq_idx[c - 1]) {
+            if (initial_states)
+                memcpy(s, initial_states + seq_idx[c] * elems, (size_t)elems * sizeof(double));
+            else
+                memset(s, 0, (size_t)elems * sizeof(double));
+        }
+        for (int64_t t = cu_chunk_seqlens[c]; t < cu_chunk_seqlens[c + 1]; ++t)
+            ssd_step_token(&pb, D_per_dim, dt_min, dt_max, s, t, out);
+        memcpy(chunk_states + c * elems, s, (size_t)elems * sizeof(double));
+    }
+    if (final_states)
+        for (int64_t b = 0; b < batch; ++b)
+            memcpy(final_states + b * elems, chunk_states + last_chunk_indices[b] * elems,
+                   (size_t)elems * sizeof(double));
+    free(s);
     return 0;
 }

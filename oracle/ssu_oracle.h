@@ -116,6 +116,35 @@ int oracle_ring_commit(int64_t *ring_start, int64_t *prev_num_accepted,
                        int64_t logical_window, int64_t ring_buffer_len,
                        int64_t pad_slot_id);
 
+/*
+ * SSD chunked prefill over packed variable-length sequences.
+ *   x, z, out [tokens, nheads, headdim]; dt [tokens, nheads];
+ *   B, C [tokens, ngroups, dstate]; A, dt_bias [nheads];
+ *   D [nheads] (D_per_dim == 0) or [nheads, headdim] (D_per_dim != 0), or NULL;
+ *   initial_states, final_states [batch, nheads, headdim, dstate] (either NULL);
+ *   chunk_states [nchunks, nheads, headdim, dstate].
+ * Chunk c covers tokens [cu_chunk_seqlens[c], cu_chunk_seqlens[c+1]) (at most
+ * chunk_size of them) and belongs to request seq_idx[c]. A chunk opens a
+ * sequence when c == 0 or seq_idx[c] != seq_idx[c-1]; it then enters with
+ * initial_states[seq_idx[c]] (zeros if NULL), otherwise with the state the
+ * previous chunk left. Inside a chunk the recurrence runs token by token with
+ * v = clamp(softplus?(dt + dt_bias), dt_min, dt_max). chunk_states[c] is the
+ * state after chunk c; final_states[b] = chunk_states[last_chunk_indices[b]].
+ * Rows of `out` no chunk covers are left as they are.
+ * Returns -1 for inconsistent arguments, including chunk ranges outside
+ * [0, tokens], running backwards or longer than chunk_size, a seq_idx outside
+ * [0, batch) when initial states are given, and last_chunk_indices outside
+ * [0, nchunks).
+ */
+int oracle_ssd_prefill(int64_t tokens, int64_t nheads, int64_t headdim, int64_t dstate,
+                       int64_t ngroups, const double *x, const double *dt, const double *A,
+                       const double *B, const double *C, const double *D, int D_per_dim,
+                       const double *z, const double *dt_bias, int dt_softplus,
+                       double dt_min, double dt_max, int64_t chunk_size, int64_t nchunks,
+                       const int64_t *cu_chunk_seqlens, const int64_t *seq_idx, int64_t batch,
+                       const int64_t *last_chunk_indices, const double *initial_states,
+                       double *out, double *chunk_states, double *final_states);
+
 #ifdef __cplusplus
 }
 #endif

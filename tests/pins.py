@@ -633,4 +633,208 @@ def pin_stochastic_rounding_in_the_update(orc):
             assert np.array_equal(sr.state[s], pb["state"][s])
 
 
+# ------------------------------------------------------------ SSD prefill
+
+def _ssd_problem(rng, *, lengths, H, P, N, G, chunk, init=True, runs_ids=None):
+    """Packed sequences of the given lengths cut into chunks of `chunk` tokens
+    (the last chunk of a sequence may be short). Returns the operands and the
+    chunk metadata the contract asks for; request ids default to 0, 1, ..."""
+    cc, seq_idx, lci = [0], [], []
+    ids = list(range(len(lengths))) if runs_ids is None else runs_ids
+    for b, L in enumerate(lengths):
+        pos = 0
+        while True:
+            step = min(chunk, L - pos)
+            cc.append(cc[-1] + step)
+            seq_idx.append(ids[b])
+            pos += step
+            if pos >= L:
+                break
+        lci.append(len(seq_idx) - 1)
+    T = cc[-1]
+    batch = max(ids) + 1
+    return dict(
+        x=rng.standard_normal((T, H, P)), dt=rng.uniform(-3.0, 0.5, (T, H)),
+        A=-np.exp(rng.uniform(0.0, 1.5, H)), B=rng.standard_normal((T, G, N)),
+        C=rng.standard_normal((T, G, N)), D=rng.standard_normal(H),
+        z=rng.standard_normal((T, H, P)), dt_bias=rng.uniform(-1.0, 1.0, H),
+        initial_states=rng.standard_normal((batch, H, P, N)) if init else None,
+        chunk_size=chunk, cu_chunk_seqlens=np.array(cc), seq_idx=np.array(seq_idx),
+        last_chunk_indices=np.array(lci))
+
+
+def _ssd_call(orc, pb, **over):
+    kw = dict(pb)
+    kw.update(over)
+    args = [kw.pop(k) for k in ("x", "dt", "A", "B", "C", "chunk_size", "cu_chunk_seqlens",
+                                "seq_idx", "last_chunk_indices")]
+    return orc.ssd_prefill(*args, **kw)
+
+
+def _ssd_blocked(pb, dt_softplus, dt_limit=(0.0, np.inf)):
+    """The chunked SSD algorithm (the block decomposition of the SSD paper,
+    section 6) with numpy matmuls: per chunk, the diagonal block
+    (C B^T masked by the decay matrix) applied to v x, the chunk's own state
+    from its inputs, the state carried in from the previous chunk of the same
+    request, and that state's contribution C h_in scaled by the decay so far."""
+    x, dt, A, B, C, D, z = (pb[k] for k in ("x", "dt", "A", "B", "C", "D", "z"))
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    ratio = H // G
+    v = dt + pb["dt_bias"]
+    if dt_softplus:
+        v = _softplus(v)
+    v = np.clip(v, dt_limit[0], dt_limit[1])
+    cc, si = pb["cu_chunk_seqlens"], pb["seq_idx"]
+    init = pb["initial_states"]
+    out = np.full(x.shape, np.nan)
+    states = []
+    h_in = None
+    for c in range(len(cc) - 1):
+        if c == 0 or si[c] != si[c - 1]:
+            h_in = init[si[c]].copy() if init is not None else np.zeros((H, P, N))
+        lo, hi = cc[c], cc[c + 1]
+        L = hi - lo
+        if L == 0:
+            states.append(h_in.copy())
+            continue
+        h_out = np.empty_like(h_in)
+        causal = np.tril(np.ones((L, L), dtype=bool))
+        for h in range(H):
+            g = h // ratio
+            cum = np.cumsum(A[h] * v[lo:hi, h])                   # decay exponent to t
+            seg = np.where(causal, cum[:, None] - cum[None, :], -np.inf)
+            Bc, Cc = B[lo:hi, g], C[lo:hi, g]                       # [L, N]
+            Xv = x[lo:hi, h] * v[lo:hi, h][:, None]                 # [L, P]
+            y = ((Cc @ Bc.T) * np.exp(seg)) @ Xv                    # inside the chunk
+            y += np.exp(cum)[:, None] * (Cc @ h_in[h].T)            # from the state in
+            own = (Xv * np.exp(cum[-1] - cum)[:, None]).T @ Bc      # [P, N]
+            h_out[h] = np.exp(cum[-1]) * h_in[h] + own
+            y += D[h] * x[lo:hi, h]
+            y *= z[lo:hi, h] * expit(z[lo:hi, h])
+            out[lo:hi, h] = y
+        h_in = h_out
+        states.append(h_out.copy())
+    return out, np.stack(states)
+
+
+def pin_ssd_chunked_form(orc):
+    """The SSD prefill equals the chunked (block-decomposed) algorithm of the SSD
+    paper, computed with numpy matmuls, for every output and every chunk state:
+    three requests of 37, 16 and 5 tokens in chunks of 16, two groups."""
+    rng = np.random.default_rng(61)
+    pb = _ssd_problem(rng, lengths=[37, 16, 5], H=4, P=3, N=5, G=2, chunk=16)
+    r = _ssd_call(orc, pb, dt_softplus=True)
+    out, states = _ssd_blocked(pb, True)
+    _close(r.out, out, 1e-10, "out")
+    _close(r.chunk_states, states, 1e-10, "chunk states")
+    assert np.array_equal(r.final_states, r.chunk_states[pb["last_chunk_indices"]])
+    # Without initial states every request starts from zero.
+    r0 = _ssd_call(orc, pb, dt_softplus=True, initial_states=None)
+    out0, states0 = _ssd_blocked(dict(pb, initial_states=None), True)
+    _close(r0.out, out0, 1e-10, "out, zero start")
+    _close(r0.chunk_states, states0, 1e-10, "states, zero start")
+
+
+def pin_ssd_equals_decode(orc):
+    """Run token by token, a request is the packed decode form over the same
+    rows: its output rows agree, and the state after each chunk equals the state
+    the decode form stores for that chunk's last token. Requests map to read
+    slots holding their initial states; every token writes its own slot."""
+    rng = np.random.default_rng(62)
+    lengths = [9, 20, 1]
+    pb = _ssd_problem(rng, lengths=lengths, H=2, P=3, N=4, G=1, chunk=8)
+    r = _ssd_call(orc, pb, dt_softplus=True)
+    T = sum(lengths)
+    nreq = len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    steps = max(lengths)
+    dst = np.full((nreq, steps), -1)
+    for b in range(nreq):
+        dst[b, :lengths[b]] = nreq + cu[b] + np.arange(lengths[b])
+    state = np.zeros((nreq + T, 2, 3, 4))
+    state[:nreq] = pb["initial_states"]
+    d = orc.packed_varlen(state, pb["x"], pb["dt"], pb["A"], pb["B"], pb["C"], cu,
+                          src_table=np.arange(nreq)[:, None], dst_table=dst, steps=steps,
+                          D=pb["D"], z=pb["z"], dt_bias=pb["dt_bias"], dt_softplus=True)
+    _close(r.out, d.out, 1e-12, "out")
+    cc = pb["cu_chunk_seqlens"]
+    for c in range(len(cc) - 1):
+        _close(r.chunk_states[c], d.state[nreq + cc[c + 1] - 1], 1e-12, f"chunk {c}")
+
+
+def pin_ssd_seq_idx_decides_entering_state(orc):
+    """A chunk opens a request when its seq_idx differs from the previous
+    chunk's, and then enters with that request's initial state; the returned
+    final states are the chunk states the last-chunk indices name, even when
+    those indices disagree with seq_idx. Each request, run alone, gives the same
+    rows and states bit for bit."""
+    rng = np.random.default_rng(63)
+    # Requests 2, 0, 1 in that order (ids not in chunk order), 3 chunks, 1 chunk, 2 chunks.
+    pb = _ssd_problem(rng, lengths=[20, 7, 12], H=2, P=2, N=3, G=1, chunk=8,
+                      runs_ids=[2, 0, 1])
+    assert list(pb["seq_idx"]) == [2, 2, 2, 0, 1, 1]
+    r = _ssd_call(orc, pb, dt_softplus=True)
+    cc = pb["cu_chunk_seqlens"]
+    for first, last, rid in ((0, 2, 2), (3, 3, 0), (4, 5, 1)):
+        lo, hi = cc[first], cc[last + 1]
+        sub = dict(pb, x=pb["x"][lo:hi], dt=pb["dt"][lo:hi], B=pb["B"][lo:hi],
+                   C=pb["C"][lo:hi], z=pb["z"][lo:hi],
+                   initial_states=pb["initial_states"][rid:rid + 1],
+                   cu_chunk_seqlens=cc[first:last + 2] - lo,
+                   seq_idx=np.zeros(last - first + 1, dtype=np.int64),
+                   last_chunk_indices=np.array([last - first]))
+        alone = _ssd_call(orc, sub, dt_softplus=True)
+        assert np.array_equal(alone.out, r.out[lo:hi]), rid
+        assert np.array_equal(alone.chunk_states, r.chunk_states[first:last + 1]), rid
+    odd = _ssd_call(orc, dict(pb, last_chunk_indices=np.array([0, 4, 3])), dt_softplus=True)
+    assert np.array_equal(odd.chunk_states, r.chunk_states)
+    assert np.array_equal(odd.final_states, r.chunk_states[[0, 4, 3]])
+
+
+def pin_ssd_dt_limit(orc):
+    """The step is clamped to dt_limit after bias and softplus: with softplus off
+    and every dt + bias negative, the default lower limit 0 freezes the state
+    (out = C . h0 + D x); with A = 0, no D, no gate and a zero start, an upper
+    limit u gives out_t = sum_{s<=t} min(v_s, u) (B_s . C_t) x_s over the
+    request, and a lower limit raises small steps the same way."""
+    rng = np.random.default_rng(64)
+    pb = _ssd_problem(rng, lengths=[11, 6], H=2, P=3, N=4, G=1, chunk=4)
+    neg = dict(pb, dt=rng.uniform(-3.0, -1.5, pb["dt"].shape), dt_bias=np.full(2, 0.5))
+    r = _ssd_call(orc, neg, dt_softplus=False, z=None)
+    for b, (first, last) in enumerate(((0, 2), (3, 4))):
+        h0 = pb["initial_states"][b]
+        lo, hi = pb["cu_chunk_seqlens"][first], pb["cu_chunk_seqlens"][last + 1]
+        ref = (np.einsum("tn,hpn->thp", pb["C"][lo:hi, 0], h0)
+               + pb["D"][None, :, None] * pb["x"][lo:hi])
+        _close(r.out[lo:hi], ref, 1e-12, f"frozen request {b}")
+        assert np.array_equal(r.final_states[b], h0)
+    for limit in ((0.0, 0.3), (0.6, np.inf)):
+        flat = dict(pb, A=np.zeros(2), D=None, z=None, initial_states=None)
+        r = _ssd_call(orc, flat, dt_softplus=True, dt_limit=limit)
+        v = np.clip(_softplus(pb["dt"] + pb["dt_bias"]), *limit)
+        for first, last in ((0, 2), (3, 4)):
+            lo, hi = pb["cu_chunk_seqlens"][first], pb["cu_chunk_seqlens"][last + 1]
+            for t in range(lo, hi):
+                s = np.arange(lo, t + 1)
+                bc = pb["B"][s, 0] @ pb["C"][t, 0]                        # [s]
+                ref = np.einsum("s,sh,shp->hp", bc, v[s], pb["x"][s])
+                _close(r.out[t], ref, 1e-12, f"limit {limit} t={t}")
+
+
+def pin_ssd_skip_term_per_dim(orc):
+    """D given per (head, dim) adds D[h, p] x[t, h, p] before the gate; a [H]
+    D equals the [H, P] D with equal columns, bit for bit."""
+    rng = np.random.default_rng(65)
+    pb = _ssd_problem(rng, lengths=[7, 3], H=3, P=4, N=2, G=1, chunk=4)
+    D2 = rng.standard_normal((3, 4))
+    with_d = _ssd_call(orc, pb, dt_softplus=True, D=D2, z=None)
+    without = _ssd_call(orc, pb, dt_softplus=True, D=None, z=None)
+    _close(with_d.out - without.out, D2[None] * pb["x"], 1e-12, "per-dim D")
+    per_head = _ssd_call(orc, pb, dt_softplus=True, z=None)
+    tied = _ssd_call(orc, pb, dt_softplus=True, z=None,
+                     D=np.repeat(pb["D"][:, None], 4, axis=1))
+    assert np.array_equal(per_head.out, tied.out)
+
+
 ALL = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -74,6 +74,28 @@ MUTANTS = [
     ("sr_bf16_half_swapped", "(e % 2) ? (word >> 16) : (word & 0xFFFFu)", "(e % 2) ? (word & 0xFFFFu) : (word >> 16)"),
     ("sr_bf16_group", "const int64_t group = bf16 ? 8 : 4;", "const int64_t group = 4;"),
     ("sr_row_of_token", "store_state(state_out + w * slot_elems, s, slot_elems, begin + t, rounding);", "store_state(state_out + w * slot_elems, s, slot_elems, begin, rounding);"),
+    ("ssd_no_clamp", "        u = fmin(fmax(u, dt_min), dt_max);\n", ""),
+    ("ssd_clamp_before_softplus",
+     "if (pb->dt_softplus) u = softplus(u);\n        u = fmin(fmax(u, dt_min), dt_max);",
+     "u = fmin(fmax(u, dt_min), dt_max);\n        if (pb->dt_softplus) u = softplus(u);"),
+    ("ssd_clamp_upper_only", "u = fmin(fmax(u, dt_min), dt_max);", "u = fmin(u, dt_max);"),
+    ("ssd_decay_uses_raw_dt", "exp(pb->A[h] * u)", "exp(pb->A[h] * pb->dt[t * H + h])"),
+    ("ssd_group_modulo", "const int64_t grp = h / ratio;", "const int64_t grp = h % pb->ngroups;"),
+    ("ssd_D_per_dim_index", "pb->D[h * P + p]", "pb->D[p]"),
+    ("ssd_gate_dropped", "            if (pb->z) y *= pb->z[i] * sigmoid(pb->z[i]);\n", ""),
+    ("ssd_every_chunk_opens", "if (c == 0 || seq_idx[c] != seq_idx[c - 1]) {", "{"),
+    ("ssd_initial_state_by_order",
+     "memcpy(s, initial_states + seq_idx[c] * elems,",
+     "memcpy(s, initial_states + (c == 0 ? 0 : seq_idx[c - 1] + 1) * elems,"),
+    ("ssd_state_before_chunk",
+     "        for (int64_t t = cu_chunk_seqlens[c]; t < cu_chunk_seqlens[c + 1]; ++t)\n            ssd_step_token(&pb, D_per_dim, dt_min, dt_max, s, t, out);\n        memcpy(chunk_states + c * elems, s, (size_t)elems * sizeof(double));",
+     "        memcpy(chunk_states + c * elems, s, (size_t)elems * sizeof(double));\n        for (int64_t t = cu_chunk_seqlens[c]; t < cu_chunk_seqlens[c + 1]; ++t)\n            ssd_step_token(&pb, D_per_dim, dt_min, dt_max, s, t, out);"),
+    ("ssd_final_from_run_end",
+     "memcpy(final_states + b * elems, chunk_states + last_chunk_indices[b] * elems,",
+     "memcpy(final_states + b * elems, chunk_states + (b + 1 < batch ? last_chunk_indices[b + 1] - 1 : nchunks - 1) * elems,"),
+    ("ssd_output_from_old_state",
+     "st[n] = st[n] * decay + u * Bt[n] * xv;\n                dot += st[n] * Ct[n];",
+     "dot += st[n] * Ct[n];\n                st[n] = st[n] * decay + u * Bt[n] * xv;"),
     ("ring_position_not_strided", "const int64_t s = slots[i * slot_stride];\n        if (!slot_valid(s, pad_slot_id, num_states)) continue;\n        if (reset)",
      "const int64_t s = slots[i];\n        if (!slot_valid(s, pad_slot_id, num_states)) continue;\n        if (reset)"),
 ]
