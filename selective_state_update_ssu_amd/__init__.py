@@ -12,6 +12,11 @@ kernel. There is no fallback: without the built library every call raises.
                       num_accepted_tokens, state_batch_indices,
                       dst_state_batch_indices, ...)
 
+    ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens,
+                            cu_chunk_seqlens, last_chunk_indices, seq_idx, out=None, *,
+                            D, z, dt_bias, dt_softplus, dt_limit, initial_states,
+                            return_intermediate_states, state_dtype)
+
 Operand shapes follow the MATE documentation page "Source code for mate.mamba"
 (`selective_state_update`): state [slots, heads, dim, dstate]; x, z, out
 [rows, heads, dim]; dt [rows, heads], [rows, heads, 1] or [rows, heads, dim]
@@ -28,8 +33,8 @@ import torch
 from . import _abi
 
 __all__ = ["ssu_one_token", "ssu_packed_varlen", "update_replayssm_ring_trackers",
-           "reset_replayssm_ring_trackers", "commit_replayssm_ring_trackers", "library_path",
-           "library"]
+           "reset_replayssm_ring_trackers", "commit_replayssm_ring_trackers",
+           "ssd_combined_fwd_varlen", "library_path", "library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBRARY = os.path.join(_HERE, "_lib", "libssu_amd.so")
@@ -404,3 +409,133 @@ def commit_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len
     rc = lib.ssu_ring_commit(ctypes.byref(args), _stream(ring_start.device, stream))
     if rc != _abi.SSU_OK:
         _raise(lib, rc, "ssu_ring_commit")
+
+
+# ------------------------------------------------------------------- prefill
+
+def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seqlens,
+                            last_chunk_indices, seq_idx, out=None, D=None, z=None,
+                            dt_bias=None, dt_softplus=False, dt_limit=(0.0, float("inf")),
+                            initial_states=None, return_intermediate_states=False,
+                            state_dtype=None, checkpoint_token_indices=None,
+                            checkpoint_state_slots=None, checkpoint_states=None, stream=None):
+    """SSD chunked prefill over packed variable-length requests (include/ssd.h).
+
+    The call and its checks follow `ssd_combined_fwd_varlen` on the MATE page
+    "Source code for mate.mamba": x [tokens, heads, dim] and dt [tokens, heads]
+    packed over the batch; B, C [tokens, groups, dstate] in x's dtype (fp16 or
+    bf16); cu_chunk_seqlens alone maps chunks to tokens, seq_idx[c] names the
+    request owning chunk c and decides where each chunk's entering state comes
+    from; `out` is written in place when given. Returns every chunk's final state
+    [nchunks, heads, dim, dstate] with return_intermediate_states, else each
+    request's final state [batch, heads, dim, dstate], in state_dtype (default:
+    initial_states' dtype, else C's). The checkpoint_* arguments are refused.
+    """
+    if any(v is not None for v in (checkpoint_token_indices, checkpoint_state_slots,
+                                   checkpoint_states)):
+        raise NotImplementedError("ssd_combined_fwd_varlen does not support the checkpoint_* "
+                                  "arguments")
+    if x.dim() != 3 or dt.dim() != 2 or B.dim() != 3 or C.dim() != 3:
+        raise ValueError("packed SSD expects x [tokens, heads, dim] and dt [tokens, heads]")
+    tokens, heads, dim = x.shape
+    groups, dstate = B.shape[1], B.shape[2]
+    if dt.shape != (tokens, heads):
+        raise ValueError("dt must be [tokens, heads]")
+    if B.shape != (tokens, groups, dstate) or C.shape != B.shape:
+        raise ValueError("B and C must be [tokens, groups, dstate]")
+    if x.dtype not in (torch.float16, torch.bfloat16) or B.dtype != x.dtype or C.dtype != x.dtype:
+        raise ValueError("x, B and C must share one of fp16/bf16")
+    if dt.dtype not in _IO_DTYPES:
+        raise ValueError("dt must be fp32, fp16 or bf16")
+    if heads % groups:
+        raise ValueError("heads must be divisible by groups")
+    if A.shape != (heads,) or A.dtype != torch.float32:
+        raise ValueError("A must be fp32 [heads]")
+    if dt_bias is not None and (dt_bias.shape != (heads,) or dt_bias.dtype != torch.float32):
+        raise ValueError("dt_bias must be fp32 [heads]")
+    if chunk_size <= 0:
+        raise ValueError("chunk_size must be positive")
+    nchunks = cu_chunk_seqlens.numel() - 1
+    if nchunks < 1:
+        raise ValueError("cu_chunk_seqlens must have at least two entries")
+    if seq_idx.numel() != nchunks:
+        raise ValueError("seq_idx must hold one request id per logical chunk")
+    if cu_seqlens.numel() != last_chunk_indices.numel() + 1:
+        raise ValueError("cu_seqlens and last_chunk_indices must describe the same batch")
+    batch = last_chunk_indices.numel()
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError(f"x must be on a GPU, got {device}")
+    if initial_states is not None:
+        if tuple(initial_states.shape[1:]) != (heads, dim, dstate):
+            raise ValueError("initial_states must be [batch, heads, dim, dstate]")
+        if initial_states.shape[0] != batch:
+            raise ValueError("initial_states must hold one row per sequence in cu_seqlens")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x's shape and dtype")
+    D_per_dim = 0
+    if D is not None:
+        if D.shape == (heads, dim):
+            D_per_dim = 1
+        elif D.shape != (heads,):
+            raise ValueError("D must be [heads, dim] or [heads]")
+        if D.dtype != torch.float32:
+            raise NotImplementedError("D must be fp32")
+    if z is not None and z.shape != x.shape:
+        raise ValueError("z must match x's shape")
+    if z is not None and z.dtype != x.dtype:
+        raise ValueError("z must share x's dtype")
+    if state_dtype is None:
+        state_dtype = initial_states.dtype if initial_states is not None else C.dtype
+    if state_dtype not in _STATE_DTYPES:
+        raise ValueError("state_dtype must be fp16, bf16 or fp32")
+    if initial_states is not None and initial_states.dtype != state_dtype:
+        raise NotImplementedError("initial_states must be in state_dtype")
+    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C),
+                    ("cu_seqlens", cu_seqlens), ("cu_chunk_seqlens", cu_chunk_seqlens),
+                    ("last_chunk_indices", last_chunk_indices), ("seq_idx", seq_idx)):
+        if not t.is_contiguous():
+            raise ValueError("x, dt, A, B, C and the chunk metadata must be contiguous")
+    for name, t in (("out", out), ("z", z), ("D", D), ("dt_bias", dt_bias),
+                    ("initial_states", initial_states)):
+        _contig(name, t)
+    for name, t in (("dt", dt), ("A", A), ("B", B), ("C", C), ("out", out), ("z", z), ("D", D),
+                    ("dt_bias", dt_bias), ("initial_states", initial_states),
+                    ("cu_chunk_seqlens", cu_chunk_seqlens), ("seq_idx", seq_idx),
+                    ("last_chunk_indices", last_chunk_indices)):
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, x is on {device}")
+    meta = {cu_chunk_seqlens.dtype, seq_idx.dtype, last_chunk_indices.dtype}
+    if len(meta) != 1 or cu_chunk_seqlens.dtype not in _INDEX_DTYPES:
+        raise ValueError("cu_chunk_seqlens, seq_idx and last_chunk_indices must share int32 or "
+                         "int64")
+    lib = library()
+    rows = nchunks if return_intermediate_states else batch
+    states = torch.empty((rows, heads, dim, dstate), dtype=state_dtype, device=device)
+    ws_bytes = lib.ssu_ssd_workspace_bytes(nchunks, batch, heads, dim, dstate, groups,
+                                           int(chunk_size))
+    workspace = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=device)
+    ws_ptr = (workspace.data_ptr() + 255) // 256 * 256
+    args = _abi.SsdArgs()
+    args.struct_size = ctypes.sizeof(_abi.SsdArgs)
+    args.tokens, args.nheads, args.headdim, args.dstate, args.ngroups = (tokens, heads, dim,
+                                                                         dstate, groups)
+    args.chunk_size, args.nchunks, args.batch = int(chunk_size), nchunks, batch
+    args.x, args.dt, args.A, args.B, args.C = _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C)
+    args.D, args.z, args.dt_bias = _ptr(D), _ptr(z), _ptr(dt_bias)
+    args.io_dtype, args.dt_dtype = _IO_DTYPES[x.dtype], _IO_DTYPES[dt.dtype]
+    args.D_per_dim, args.dt_softplus = D_per_dim, int(bool(dt_softplus))
+    args.dt_min, args.dt_max = float(dt_limit[0]), float(dt_limit[1])
+    args.cu_chunk_seqlens, args.seq_idx = _ptr(cu_chunk_seqlens), _ptr(seq_idx)
+    args.last_chunk_indices = _ptr(last_chunk_indices)
+    args.meta_dtype = _INDEX_DTYPES[cu_chunk_seqlens.dtype]
+    args.state_dtype = _STATE_DTYPES[state_dtype]
+    args.initial_states, args.out, args.states = _ptr(initial_states), _ptr(out), _ptr(states)
+    args.return_intermediate_states = int(bool(return_intermediate_states))
+    args.workspace, args.workspace_bytes = ws_ptr, ws_bytes
+    rc = lib.ssu_ssd_prefill(ctypes.byref(args), _stream(device, stream))
+    if rc != _abi.SSU_OK:
+        _raise(lib, rc, "ssu_ssd_prefill")
+    return states

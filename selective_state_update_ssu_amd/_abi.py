@@ -1,9 +1,9 @@
-"""ctypes mirror of include/ssu.h. Field order and types must match the header;
+"""ctypes mirror of include/ssu.h and include/ssd.h. Field order and types must match the header;
 the library checks `struct_size` on every call, so a stale mirror fails loudly."""
 import ctypes
 import os
 
-from ctypes import c_int32, c_int64, c_uint32, c_void_p, c_char_p
+from ctypes import c_double, c_int32, c_int64, c_size_t, c_uint32, c_void_p, c_char_p
 
 SSU_F32, SSU_F16, SSU_BF16 = 0, 1, 2
 SSU_I32, SSU_I64 = 0, 1
@@ -11,7 +11,7 @@ SSU_OK, SSU_ERR_INVALID_ARGUMENT, SSU_ERR_UNSUPPORTED, SSU_ERR_LAUNCH = 0, 1, 2,
 ABI_VERSION = 1
 
 EXPORTS = ("ssu_one_token", "ssu_packed_varlen", "ssu_ring_update", "ssu_ring_commit",
-           "ssu_last_error", "ssu_version")
+           "ssu_last_error", "ssu_version", "ssu_ssd_workspace_bytes", "ssu_ssd_prefill")
 
 
 class Operands(ctypes.Structure):
@@ -62,6 +62,22 @@ class RingArgs(ctypes.Structure):
     ]
 
 
+class SsdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_uint32), ("tokens", c_int64),
+        ("nheads", c_int64), ("headdim", c_int64), ("dstate", c_int64), ("ngroups", c_int64),
+        ("chunk_size", c_int64), ("nchunks", c_int64), ("batch", c_int64),
+        ("x", c_void_p), ("dt", c_void_p), ("A", c_void_p), ("B", c_void_p), ("C", c_void_p),
+        ("D", c_void_p), ("z", c_void_p), ("dt_bias", c_void_p),
+        ("io_dtype", c_int32), ("dt_dtype", c_int32), ("D_per_dim", c_int32),
+        ("dt_softplus", c_int32), ("dt_min", c_double), ("dt_max", c_double),
+        ("cu_chunk_seqlens", c_void_p), ("seq_idx", c_void_p), ("last_chunk_indices", c_void_p),
+        ("meta_dtype", c_int32), ("state_dtype", c_int32), ("initial_states", c_void_p),
+        ("out", c_void_p), ("states", c_void_p), ("return_intermediate_states", c_int32),
+        ("reserved", c_int32), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+    ]
+
+
 def load(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(
@@ -76,6 +92,10 @@ def load(path: str) -> ctypes.CDLL:
     for f in (lib.ssu_ring_update, lib.ssu_ring_commit):
         f.restype = c_int32
         f.argtypes = [ctypes.POINTER(RingArgs), c_void_p]
+    lib.ssu_ssd_workspace_bytes.restype = c_size_t
+    lib.ssu_ssd_workspace_bytes.argtypes = [c_int64] * 7
+    lib.ssu_ssd_prefill.restype = c_int32
+    lib.ssu_ssd_prefill.argtypes = [ctypes.POINTER(SsdArgs), c_void_p]
     lib.ssu_last_error.restype = c_char_p
     lib.ssu_last_error.argtypes = []
     lib.ssu_version.restype = c_int32

@@ -1,7 +1,7 @@
 """Compile the HIP sources into the in-tree shared library `_lib/libssu_amd.so`.
 
 Every translation unit is compiled for gfx950 only, in parallel, then linked into
-one shared library that exports the C ABI of include/ssu.h. Packed-fp32 VALU
+one shared library that exports the C ABI of include/ssu.h and include/ssd.h. Packed-fp32 VALU
 instructions are disabled for the device code.
 """
 from __future__ import annotations
@@ -26,7 +26,7 @@ STREAM_SOURCES = ["stream_ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["ssu_api.hip", "ssu_kernels_f32.hip", "ssu_kernels_f16.hip", "ssu_kernels_bf16.hip",
-           "ring_trackers.hip"]
+           "ring_trackers.hip", "ssd_api.hip", "ssd_kernels_bf16.hip", "ssd_kernels_f16.hip"]
 CXXFLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",

@@ -1,0 +1,8 @@
+// SSD prefill kernels with fp16 x, B, C, z and out.
+#include "ssd_kernel.hpp"
+#include "ssd_launch.h"
+
+hipError_t ssd::launch_ssd_f16(const SsdParams& p, int state_dtype, int P, int N, int Q,
+                               hipStream_t stream) {
+    return launch_io<_Float16>(p, state_dtype, P, N, Q, stream);
+}

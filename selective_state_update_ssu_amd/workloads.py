@@ -30,6 +30,16 @@ Named workloads (one GPU each, at their real decode shapes):
   dense_mtp   the Mamba2-2.7B shape in the dense [256, 2, ...] layout (one draft
               token per sequence), slot table [256, 2] of 1024 slots, 5 % pads.
   bf16_state_sr  bf16_state with stochastic rounding of the stored states.
+
+SSD prefill workloads (`SSD_NAMED`, packed prompts cut into chunks):
+  ssd_mamba2_2p7b  16 prompts of U{256..2048} tokens, 80 heads x 64 x 128,
+                   1 group, chunk 256; bf16 x/B/C/z, fp32 states, fresh prompts
+                   (no initial states).
+  ssd_nemotron_h   8 prompts of U{512..4096} tokens, 128 heads x 64 x 128,
+                   8 groups, chunk 128; bf16 io, fp32 states continuing from
+                   initial states; dt ~ U(-4, 0), A = -exp(U(0, 3)).
+  ssd_small        prompts of 1, 255, 256, 257, 700 and 37 tokens, 4 heads x 64
+                   x 128, 2 groups, chunk 256; initial states.
 """
 from __future__ import annotations
 
@@ -269,6 +279,117 @@ def packed_mtp(device, seed=4):
     return packed("packed_mtp", seed, nseq=256, max_len=4, H=80, P=64, N=128, G=1,
                   nslots=2048, device=device, state_dtype="f32", io="bf16",
                   with_z=True, pad_fraction=0.05)
+
+
+@dataclass
+class SsdWorkload:
+    """One SSD prefill call's operands and chunk metadata (int tensors on the
+    workload's device)."""
+    name: str
+    x: torch.Tensor                    # [tokens, H, P] io
+    dt: torch.Tensor                   # [tokens, H]
+    A: torch.Tensor                    # [H] fp32
+    B: torch.Tensor                    # [tokens, G, N] io
+    C: torch.Tensor                    # [tokens, G, N] io
+    chunk_size: int
+    cu_seqlens: torch.Tensor           # [batch + 1]
+    cu_chunk_seqlens: torch.Tensor     # [nchunks + 1]
+    seq_idx: torch.Tensor              # [nchunks]
+    last_chunk_indices: torch.Tensor   # [batch]
+    state_dtype: torch.dtype
+    D: Optional[torch.Tensor] = None   # [H] or [H, P] fp32
+    z: Optional[torch.Tensor] = None
+    dt_bias: Optional[torch.Tensor] = None
+    initial_states: Optional[torch.Tensor] = None  # [batch, H, P, N] state dtype
+    dt_softplus: bool = True
+    dt_limit: tuple = (0.0, float("inf"))
+    return_intermediate_states: bool = False
+    meta: dict = field(default_factory=dict)
+
+    def kwargs(self) -> dict:
+        """Keyword arguments of `ssd_combined_fwd_varlen` for this call."""
+        return dict(D=self.D, z=self.z, dt_bias=self.dt_bias, dt_softplus=self.dt_softplus,
+                    dt_limit=self.dt_limit, initial_states=self.initial_states,
+                    return_intermediate_states=self.return_intermediate_states,
+                    state_dtype=self.state_dtype)
+
+    def args(self) -> tuple:
+        return (self.x, self.dt, self.A, self.B, self.C, self.chunk_size, self.cu_seqlens,
+                self.cu_chunk_seqlens, self.last_chunk_indices, self.seq_idx)
+
+
+def chunk_metadata(lengths, chunk_size, request_ids=None):
+    """Cut packed requests into chunks of chunk_size tokens (a request's last
+    chunk may be shorter): cu_seqlens, cu_chunk_seqlens, seq_idx (the request id
+    of each chunk; 0, 1, ... unless given) and last_chunk_indices, as lists."""
+    ids = list(range(len(lengths))) if request_ids is None else list(request_ids)
+    cu, cc, seq_idx, last = [0], [0], [], []
+    for b, L in enumerate(lengths):
+        cu.append(cu[-1] + L)
+        pos = 0
+        while True:
+            step = min(chunk_size, L - pos)
+            cc.append(cc[-1] + step)
+            seq_idx.append(ids[b])
+            pos += step
+            if pos >= L:
+                break
+        last.append(len(seq_idx) - 1)
+    return cu, cc, seq_idx, last
+
+
+def ssd(name, seed, *, lengths, H, P, N, G, chunk, device, io="bf16", state_dtype="f32",
+        dt_dtype="f32", with_init=False, with_z=True, D_per_dim=False, dt_range=(-3.0, 0.0),
+        a_log_range=(0.0, 2.0), meta_dtype="i32", request_ids=None, **kw) -> SsdWorkload:
+    """A packed prefill: x/B/C/z ~ N(0,1) in the io dtype, dt ~ U(dt_range),
+    dt_bias ~ U(-1, 1), A = -exp(U(a_log_range)), D ~ N(0, 1), initial states
+    ~ N(0, 1) in the state dtype."""
+    lengths = [int(v) for v in lengths]
+    tokens = sum(lengths)
+    ops = operands(seed, tokens, H, P, N, G, device=device, io=io, with_z=with_z,
+                   dt_range=dt_range, a_log_range=a_log_range)
+    ops["dt"] = ops["dt"].to(torch_dtype(dt_dtype))
+    if D_per_dim:
+        ops["D"] = normal((H, P), seed, "D2", device)
+    cu, cc, seq_idx, last = chunk_metadata(lengths, chunk, request_ids)
+    mdt = torch_dtype(meta_dtype)
+    t = lambda v: torch.tensor(v, dtype=mdt, device=device)
+    batch = len(last)
+    init = None
+    if with_init:
+        init = normal((batch, H, P, N), seed, "initial_states", device, torch_dtype(state_dtype))
+    return SsdWorkload(name=name, chunk_size=chunk, cu_seqlens=t(cu), cu_chunk_seqlens=t(cc),
+                       seq_idx=t(seq_idx), last_chunk_indices=t(last),
+                       state_dtype=torch_dtype(state_dtype), initial_states=init,
+                       meta=dict(seed=seed, lengths=lengths, io=io), **ops, **kw)
+
+
+def _lengths(n, lo, hi, seed):
+    g = _generator(seed, "lengths", "cpu")
+    return torch.randint(lo, hi + 1, (n,), generator=g).tolist()
+
+
+def ssd_mamba2_2p7b(device, seed=11):
+    return ssd("ssd_mamba2_2p7b", seed, lengths=_lengths(16, 256, 2048, seed), H=80, P=64,
+               N=128, G=1, chunk=256, device=device)
+
+
+def ssd_nemotron_h(device, seed=12):
+    return ssd("ssd_nemotron_h", seed, lengths=_lengths(8, 512, 4096, seed), H=128, P=64,
+               N=128, G=8, chunk=128, device=device, with_init=True, dt_range=(-4.0, 0.0),
+               a_log_range=(0.0, 3.0))
+
+
+def ssd_small(device, seed=13):
+    return ssd("ssd_small", seed, lengths=[1, 255, 256, 257, 700, 37], H=4, P=64, N=128, G=2,
+               chunk=256, device=device, with_init=True)
+
+
+SSD_NAMED = {
+    "ssd_mamba2_2p7b": ssd_mamba2_2p7b,
+    "ssd_nemotron_h": ssd_nemotron_h,
+    "ssd_small": ssd_small,
+}
 
 
 NAMED = {

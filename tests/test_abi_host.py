@@ -1,4 +1,4 @@
-"""The C ABI on the host: the library loads, exports what include/ssu.h declares,
+"""The C ABI on the host: the library loads, exports what include/*.h declare,
 agrees with the ctypes mirror on struct layout, and rejects every invalid call
 before touching the GPU. No call here reaches a kernel launch: each one either
 fails validation or has no work, so these run on machines without a GPU."""
@@ -14,6 +14,7 @@ import selective_state_update_ssu_amd as ssu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssu.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "ssd.h")]
 
 
 @pytest.fixture(scope="module")
@@ -25,9 +26,11 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssu_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssu_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_function(lib):
@@ -47,10 +50,12 @@ def test_version(lib):
 
 def test_struct_layout_matches_header(tmp_path):
     """Offsets and sizes of every field, as the C compiler lays them out."""
-    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssu.h"', "int main(void){"]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssu.h"', '#include "ssd.h"',
+             "int main(void){"]
     checks = []
     for cname, cls in (("ssu_operands", _abi.Operands), ("ssu_one_token_args", _abi.OneTokenArgs),
-                       ("ssu_packed_args", _abi.PackedArgs), ("ssu_ring_args", _abi.RingArgs)):
+                       ("ssu_packed_args", _abi.PackedArgs), ("ssu_ring_args", _abi.RingArgs),
+                       ("ssu_ssd_args", _abi.SsdArgs)):
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
         checks.append((cname, ctypes.sizeof(cls)))
         for fname, _ in cls._fields_:
@@ -243,3 +248,60 @@ def test_product_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), os.path.join(dirpath, f)
+
+
+# ------------------------------------------------------------------ SSD prefill
+
+def ssd(lib, **kw):
+    a = _abi.SsdArgs(
+        struct_size=ctypes.sizeof(_abi.SsdArgs), tokens=1000, nheads=8, headdim=64, dstate=128,
+        ngroups=2, chunk_size=256, nchunks=6, batch=3, x=addr(1), dt=addr(2), A=addr(3),
+        B=addr(4), C=addr(5), D=addr(6), z=addr(7), dt_bias=addr(8), io_dtype=_abi.SSU_BF16,
+        dt_dtype=_abi.SSU_F32, D_per_dim=0, dt_softplus=1, dt_min=0.0, dt_max=float("inf"),
+        cu_chunk_seqlens=addr(9), seq_idx=addr(10), last_chunk_indices=addr(11),
+        meta_dtype=_abi.SSU_I32, state_dtype=_abi.SSU_F32, initial_states=addr(12),
+        out=addr(13), states=addr(14), return_intermediate_states=0, reserved=0,
+        workspace=addr(15), workspace_bytes=1 << 30)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    rc = lib.ssu_ssd_prefill(ctypes.byref(a), None)
+    return rc, lib.ssu_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(struct_size=8), INV, "struct_size"),
+    (dict(ngroups=3), INV, "divisible"),
+    (dict(nheads=0), INV, "positive"),
+    (dict(chunk_size=0), INV, "chunk_size"),
+    (dict(nchunks=0), INV, "two entries"),
+    (dict(io_dtype=_abi.SSU_F32), INV, "fp16/bf16"),
+    (dict(dt_dtype=9), INV, "dt must be"),
+    (dict(state_dtype=9), INV, "state_dtype"),
+    (dict(meta_dtype=4), INV, "int32 or int64"),
+    (dict(dt_min=1.0, dt_max=0.5), INV, "dt_limit"),
+    (dict(x=0), INV, "required"),
+    (dict(A=0), INV, "A is required"),
+    (dict(seq_idx=0), INV, "required"),
+    (dict(last_chunk_indices=0), INV, "last_chunk_indices"),
+    (dict(states=0), INV, "states is required"),
+    (dict(headdim=80), UNS, "no kernel"),
+    (dict(dstate=256), UNS, "no kernel"),
+    (dict(chunk_size=64), UNS, "no kernel"),
+    (dict(x=addr(1) + 8), UNS, "16-byte aligned"),
+    (dict(workspace_bytes=1024), INV, "workspace"),
+    (dict(workspace=addr(15) + 16), INV, "workspace"),
+    (dict(out=addr(1) + 64), INV, "out overlaps x"),
+    (dict(states=addr(12) + 64), INV, "states overlaps initial_states"),
+    (dict(reserved=1), INV, "reserved"),
+])
+def test_ssd_rejects(lib, kw, code, needle):
+    rc, msg = ssd(lib, **kw)
+    assert rc == code, (rc, msg)
+    assert needle in msg, msg
+
+
+def test_ssd_workspace_bytes(lib):
+    n = lib.ssu_ssd_workspace_bytes(6, 3, 8, 64, 128, 2, 256)
+    need = 6 * 8 * 64 * 128 * 2 + 6 * 2 * 256 * 256 * 4 + 6 * 4 + 3 * 4
+    assert need <= n <= need + 4 * 256 and n % 256 == 0
+    assert lib.ssu_ssd_workspace_bytes(-1, 3, 8, 64, 128, 2, 256) == 0

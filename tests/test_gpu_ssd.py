@@ -1,0 +1,155 @@
+"""SSD chunked prefill on the GPU against the fp64 oracle, element by element,
+within the tolerance derived in ssd_harness.py."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_harness as sh
+from selective_state_update_ssu_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+CASES = {
+    # bf16 io, fp32 states, ragged requests (1, Q-1, Q, Q+1, several chunks), two
+    # groups, initial states, gate.
+    "bf16_f32_ragged": dict(lengths=[1, 255, 256, 257, 700, 37], H=4, P=64, N=128, G=2,
+                            chunk=256, with_init=True),
+    "bf16_f32_all_chunks": dict(lengths=[1, 255, 256, 257, 700, 37], H=4, P=64, N=128, G=2,
+                                chunk=256, with_init=True, return_intermediate_states=True),
+    # fp16 io, bf16 states, dstate 64, chunk 128, no initial states, no gate,
+    # per-dim D, bf16 dt.
+    "f16_bf16_d64": dict(lengths=[130, 5, 128, 300], H=6, P=64, N=64, G=3, chunk=128,
+                         io="f16", state_dtype="bf16", with_z=False, D_per_dim=True,
+                         dt_dtype="bf16"),
+    # fp16 states with a dt limit and softplus off (clamped from below).
+    "bf16_f16_limit": dict(lengths=[77, 400, 129], H=2, P=64, N=128, G=1, chunk=128,
+                           state_dtype="f16", with_init=True, dt_softplus=False,
+                           dt_range=(-1.0, 1.5), dt_limit=(0.05, 0.8)),
+    # one long request: fourteen chunks passed from state to state; int64 metadata.
+    "f16_f32_long": dict(lengths=[3500], H=2, P=64, N=64, G=1, chunk=256, io="f16",
+                         with_init=True, meta_dtype="i64", return_intermediate_states=True),
+    # request ids out of chunk order; fp16 dt.
+    "ids_out_of_order": dict(lengths=[300, 40, 520], H=4, P=64, N=128, G=4, chunk=128,
+                             with_init=True, request_ids=[2, 0, 1], dt_dtype="f16"),
+}
+
+
+def _make(name, seed=5):
+    kw = dict(CASES[name])
+    extra = {k: kw.pop(k) for k in ("return_intermediate_states", "dt_softplus", "dt_limit")
+             if k in kw}
+    return wl.ssd(name, seed, device=DEV, **kw, **extra)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_small_cases(name):
+    w = _make(name)
+    print(f"[ssd] {name}: tokens {w.x.shape[0]}, chunks {w.seq_idx.numel()}", flush=True)
+    out = torch.full_like(w.x, float("nan"))
+    _, states = sh.run_gpu(w, out)
+    torch.cuda.synchronize()
+    ref, mag = sh.oracle_ref(w)
+    r_out, r_st = sh.check_all(w, out, states, ref, mag)
+    print(f"[ssd] {name}: worst err/tol out {r_out:.3f}, states {r_st:.3f}", flush=True)
+
+
+def test_last_chunk_indices_disagreeing_with_seq_idx():
+    """The returned per-request states are the chunk states the last-chunk
+    indices name, even when those disagree with seq_idx; seq_idx alone decides
+    where each chunk's entering state comes from."""
+    w = _make("bf16_f32_ragged")
+    nchunks = w.seq_idx.numel()
+    w.last_chunk_indices = torch.tensor([0, 3, 3, nchunks - 1, 1, 2], dtype=torch.int32,
+                                        device=DEV)
+    out = torch.empty_like(w.x)
+    _, states = sh.run_gpu(w, out)
+    torch.cuda.synchronize()
+    ref, mag = sh.oracle_ref(w)
+    sh.check_all(w, out, states, ref, mag)
+
+
+def test_out_allocated_when_absent_and_written_in_place():
+    import selective_state_update_ssu_amd as ssu
+    w = _make("f16_bf16_d64")
+    states = ssu.ssd_combined_fwd_varlen(*w.args(), **w.kwargs())
+    out = torch.empty_like(w.x)
+    states2 = ssu.ssd_combined_fwd_varlen(*w.args(), out=out, **w.kwargs())
+    torch.cuda.synchronize()
+    assert torch.equal(states, states2)
+    ref, mag = sh.oracle_ref(w)
+    sh.check_out(out, ref.out, mag.out, w.x.dtype)
+
+
+def test_repeatable_bit_for_bit():
+    w = _make("bf16_f32_ragged")
+    a = torch.empty_like(w.x)
+    b = torch.empty_like(w.x)
+    _, sa = sh.run_gpu(w, a)
+    _, sb = sh.run_gpu(w, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(sa, sb)
+
+
+@pytest.mark.parametrize("name", ["ssd_mamba2_2p7b", "ssd_nemotron_h"])
+def test_named_workload_sampled_requests(name):
+    """The full-size prefill, as the benchmark runs it; the oracle checks
+    requests cut out of it -- the shortest, the longest and one more -- on every
+    row and on four heads spread over the groups (rows and final states)."""
+    w = wl.SSD_NAMED[name](DEV)
+    print(f"[ssd] {name}: tokens {w.x.shape[0]}, chunks {w.seq_idx.numel()}", flush=True)
+    out = torch.full_like(w.x, float("nan"))
+    _, states = sh.run_gpu(w, out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(states.float()).all()
+    lengths = w.meta["lengths"]
+    picks = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), len(lengths) // 2})
+    H = w.x.shape[1]
+    heads = [0, H // 3, (2 * H) // 3 + 1, H - 1]
+    for b in picks:
+        cut, (lo, hi), hs = sh.cut_request(w, b, heads)
+        ref, mag = sh.oracle_ref(cut)
+        r_out = sh.check_out(out[lo:hi][:, hs], ref.out, mag.out, w.x.dtype,
+                             what=f"out of request {b}")
+        r_st = sh.check_states(states[b:b + 1][:, hs], ref.final_states, mag.final_states,
+                               w.state_dtype, w.x.dtype, f"state of request {b}")
+        print(f"[ssd] {name} request {b} ({hi - lo} tokens): worst err/tol out {r_out:.3f}, "
+              f"state {r_st:.3f}", flush=True)
+
+
+def test_empty_request_list_and_chunks():
+    """No requests to return (batch 0) and an empty chunk: the call still runs and
+    writes the rows of the chunks it has."""
+    import selective_state_update_ssu_amd as ssu
+    w = _make("bf16_f32_all_chunks")
+    cc = w.cu_chunk_seqlens.cpu().tolist()
+    # Append an empty chunk of a new request 6 (no initial state row for it: the
+    # states come back per chunk, so batch stays as it was).
+    w.cu_chunk_seqlens = torch.tensor(cc + [cc[-1]], dtype=torch.int32, device=DEV)
+    w.seq_idx = torch.cat([w.seq_idx, torch.tensor([5], dtype=torch.int32, device=DEV)])
+    out = torch.empty_like(w.x)
+    _, states = sh.run_gpu(w, out)
+    torch.cuda.synchronize()
+    ref, mag = sh.oracle_ref(w)
+    sh.check_all(w, out, states, ref, mag)
+    # Without initial states and with return_intermediate_states the batch may be 0.
+    states = ssu.ssd_combined_fwd_varlen(
+        w.x, w.dt, w.A, w.B, w.C, w.chunk_size, w.cu_seqlens[:1], w.cu_chunk_seqlens,
+        w.last_chunk_indices[:0], w.seq_idx, out=out, D=w.D, z=w.z, dt_bias=w.dt_bias,
+        dt_softplus=True, return_intermediate_states=True, state_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.default().ssd_prefill(
+        *(sh.np64(t) for t in (w.x, w.dt, w.A, w.B, w.C)), w.chunk_size,
+        sh.npi(w.cu_chunk_seqlens), sh.npi(w.seq_idx), np.zeros(0, dtype=np.int64),
+        D=sh.np64(w.D), z=sh.np64(w.z), dt_bias=sh.np64(w.dt_bias), dt_softplus=True)
+    w.initial_states = None
+    _, mag = sh.oracle_ref(w)
+    sh.check_states(states, ref.chunk_states, mag.chunk_states, torch.float32, w.x.dtype)
