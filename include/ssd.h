@@ -77,7 +77,8 @@ typedef struct ssu_ssd_args {
     int32_t state_dtype;             /* SSU_F32, SSU_F16 or SSU_BF16 */
     const void *initial_states;      /* [batch, nheads, headdim, dstate] state_dtype, or NULL */
     void *out;                       /* [tokens, nheads, headdim] io_dtype, written */
-    void *states;                    /* returned states (see above), state_dtype, written */
+    void *states;                    /* returned states (see above), state_dtype, written;
+                                        16-byte aligned */
     int32_t return_intermediate_states;
     int32_t reserved;                /* 0 */
     /* Scratch owned by the caller, 256-byte aligned, at least
@@ -86,9 +87,9 @@ typedef struct ssu_ssd_args {
     size_t workspace_bytes;
 } ssu_ssd_args;
 
-/* Bytes of workspace ssu_ssd_prefill needs for these sizes (chunk-end states in
- * the io type, the per-chunk C B^T products, and the per-request list of last
- * chunks). */
+/* Bytes of workspace ssu_ssd_prefill needs for these sizes: chunk-end states in
+ * the io type, the per-chunk C B^T products (fp32), each chunk's own state
+ * contribution (fp32) and decay, and the per-request list of last chunks. */
 size_t ssu_ssd_workspace_bytes(int64_t nchunks, int64_t batch, int64_t nheads,
                                int64_t headdim, int64_t dstate, int64_t ngroups,
                                int64_t chunk_size);

@@ -17,7 +17,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t s16, cb, head, next, total;
+    size_t s16, cb, local, cumlast, dummy, head, next, total;
 };
 
 Layout layout(int64_t nchunks, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
@@ -25,7 +25,10 @@ Layout layout(int64_t nchunks, int64_t batch, int64_t nheads, int64_t headdim, i
     Layout l;
     l.s16 = 0;
     l.cb = l.s16 + round_up(static_cast<size_t>(nchunks * nheads * headdim * dstate) * 2);
-    l.head = l.cb + round_up(static_cast<size_t>(nchunks * ngroups * chunk_size * chunk_size) * 4);
+    l.local = l.cb + round_up(static_cast<size_t>(nchunks * ngroups * chunk_size * chunk_size) * 4);
+    l.cumlast = l.local + round_up(static_cast<size_t>(nchunks * nheads * headdim * dstate) * 4);
+    l.dummy = l.cumlast + round_up(static_cast<size_t>(nchunks * nheads) * 4);
+    l.head = l.dummy + round_up(static_cast<size_t>(nheads * headdim * dstate) * 4);
     l.next = l.head + round_up(static_cast<size_t>(nchunks) * 4);
     l.total = l.next + round_up(static_cast<size_t>(batch) * 4);
     return l;
@@ -95,8 +98,10 @@ int check(const ssu_ssd_args& a) {
         if (s.p && !aligned(s.p, 16))
             return report(SSU_ERR_UNSUPPORTED, "%s must be 16-byte aligned", s.name);
     const size_t ssz = dtype_size(a.state_dtype);
-    if ((a.initial_states && !aligned(a.initial_states, ssz)) || (a.states && !aligned(a.states, ssz)))
-        return report(SSU_ERR_UNSUPPORTED, "state tensors must be aligned to their element size");
+    if (a.initial_states && !aligned(a.initial_states, ssz))
+        return report(SSU_ERR_UNSUPPORTED, "initial_states must be aligned to its element size");
+    if (a.states && !aligned(a.states, 16))
+        return report(SSU_ERR_UNSUPPORTED, "states must be 16-byte aligned");
     const Layout l = layout(a.nchunks, a.batch, a.nheads, a.headdim, a.dstate, a.ngroups,
                             a.chunk_size);
     if (!a.workspace || !aligned(a.workspace, kAlign) || a.workspace_bytes < l.total)
@@ -176,6 +181,9 @@ extern "C" int ssu_ssd_prefill(const ssu_ssd_args* args, void* stream) {
     p.states = a.states;
     p.s16 = ws + l.s16;
     p.cb = reinterpret_cast<float*>(ws + l.cb);
+    p.local = reinterpret_cast<float*>(ws + l.local);
+    p.cumlast = reinterpret_cast<float*>(ws + l.cumlast);
+    p.dummy = ws + l.dummy;
     p.list_head = reinterpret_cast<int*>(ws + l.head);
     p.list_next = reinterpret_cast<int*>(ws + l.next);
     p.tokens = a.tokens;

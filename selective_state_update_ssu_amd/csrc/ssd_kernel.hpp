@@ -1,26 +1,25 @@
 // ssd_kernel.hpp -- SSD chunked prefill for gfx950 (CDNA4, wave64, MFMA).
 //
 // The prefill of a Mamba-2 layer over packed variable-length requests, cut into
-// chunks of at most Q tokens (semantics in include/ssd.h). Three contractions
-// per chunk run on the matrix cores, with 16-bit operands and fp32 accumulation:
+// chunks of at most Q tokens (semantics in include/ssd.h), as five launches:
 //
-//   bmm    CB[t, s]  = C_t . B_s                         per (chunk, group)
-//   state  S_c       = exp(cum_last) S_{c-1} + sum_s exp(cum_last - cum_s) v_s x_s B_s^T
-//                                                         per (run of chunks, head)
-//   scan   y_t       = sum_{s<=t} CB[t, s] exp(cum_t - cum_s) v_s x_s
-//                      + exp(cum_t) C_t . S_{c-1} + D x_t, gated by z sigmoid(z)
-//                                                         per (chunk, head)
+//   list      the requests whose last chunk is c, per chunk        (one workgroup)
+//   bmm       CB[t, s] = C_t . B_s                                 per (chunk, group)
+//   chunk     L_c = sum_s exp(cum_last - cum_s) v_s x_s B_s^T      per (chunk, head, block)
+//   passing   S_c = exp(cum_last) S_{c-1} + L_c along each request per 4 state elements
+//   scan      y_t = sum_{s<=t} CB[t, s] exp(cum_t - cum_s) v_s x_s
+//                   + exp(cum_t) C_t . S_{c-1} + D x_t, gated      per (chunk, head)
 //
-// with v the clamped step and cum the running sum of A v inside the chunk. The
-// state kernel walks each request's chunks in order, carrying the state in MFMA
-// accumulators, so chunk states never make a round trip through HBM before they
-// are passed on; it writes each chunk-end state once in the io type for the scan
-// (which consumes it as a 16-bit MFMA operand anyway) and once in the state type
-// where the caller asked for it. The running sums of A v are taken in fp64, so
-// the decay between two tokens is exact to fp32 however far into the chunk they
-// lie. The state kernel feeds the matrix cores v x exp(...) as a sum of two
-// 16-bit values (high part and rounding residual), which makes each product
-// accurate to about 2^-16 instead of 2^-8; the scan rounds its operands once.
+// with v the clamped step and cum the running sum of A v inside the chunk
+// (fp64, so the decay between two tokens is exact to fp32 however far into the
+// chunk they lie). The three contractions run on the matrix cores with 16-bit
+// operands and fp32 accumulation. The chunk kernel feeds exp(.) v x as a high
+// and a low 16-bit part, which makes each product of a state accurate to about
+// 2^-16 instead of 2^-8; the scan rounds its decayed C B^T entries once and uses
+// x exactly. An opening chunk's L already carries the decayed initial state, so
+// the passing walk is a chain of FMAs over loads requested chunks ahead. The
+// passing kernel writes each chunk-end state in the io type (the scan's 16-bit
+// MFMA operand) and in the state type where the caller asked for it.
 //
 // MFMA operand layouts (gfx950, checked on the hardware):
 //   16x16x32: lane l holds A[l % 16][8 (l / 16) + j] and B[8 (l / 16) + j][l % 16],
@@ -28,8 +27,8 @@
 //   32x32x16: lane l holds A[l % 32][8 (l / 32) + j] and B[8 (l / 32) + j][l % 32];
 //             the result D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32], i < 16.
 // Both operands want eight consecutive values of the contracted index per lane.
-// Where that index is the token (state: sum over s; scan: sum over s), the
-// token-major inputs are transposed on their way into LDS.
+// Where that index is the token, the token-major inputs are transposed on their
+// way into LDS.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -72,6 +71,9 @@ struct SsdParams {
     void* states;         // [nchunks or batch, H, P, N] state type
     void* s16;            // workspace [nchunks, H, P, N] io: chunk-end states for the scan
     float* cb;            // workspace [nchunks, G, Q, Q]
+    float* local;         // workspace [nchunks, H, P, N]: each chunk's own state contribution
+    float* cumlast;       // workspace [nchunks, H]: each chunk's decay exponent
+    void* dummy;          // workspace [H, P, N] state type: sink of steps with nothing to return
     int* list_head;       // workspace [nchunks]: first request whose last chunk is c
     int* list_next;       // workspace [batch]
     int64_t tokens, nchunks, batch;
@@ -150,18 +152,25 @@ __device__ __forceinline__ Chunk chunk_of(const SsdParams& p, int64_t c) {
     return {lo, static_cast<int>(hi - lo)};
 }
 
+// The raw step of token `tid` of the chunk for head h (0 past the chunk): the
+// load half of chunk_steps, so that it can be issued ahead of other loads.
+__device__ __forceinline__ float load_step(const SsdParams& p, const Chunk& ch, int h) {
+    const int tid = threadIdx.x;
+    return tid < ch.len ? load_dt(p, (ch.lo + tid) * p.nheads + h) : 0.f;
+}
+
 // Per chunk and head: the clamped step v_s and the inclusive running sum
-// cum_s = sum_{j<=s} A v_j (fp64) for s < len, into LDS; zero past len. Every
-// thread of the workgroup calls it; it ends with a barrier.
-template <int Q>
-__device__ __forceinline__ void chunk_steps(const SsdParams& p, const Chunk& ch, int h, float* sv,
-                                            double* scum, double* swave) {
-    static_assert(Q <= kThreads, "one step per thread");
+// cum_s = sum_{j<=s} A v_j (fp64) for s < len, into LDS; zero past len. `u` is
+// this thread's load_step(). Every thread of the workgroup calls it; it ends
+// with a barrier.
+template <int Q, int THREADS = kThreads>
+__device__ __forceinline__ void chunk_steps(const SsdParams& p, const Chunk& ch, int h, float u,
+                                            float* sv, double* scum, double* swave) {
+    static_assert(Q <= THREADS, "one step per thread");
     const int tid = threadIdx.x, lane = tid & 63;
     float v = 0.f;
     double a = 0.0;
     if (tid < ch.len) {
-        float u = load_dt(p, (ch.lo + tid) * p.nheads + h);
         if (p.dt_bias) u += p.dt_bias[h];
         if (p.dt_softplus) u = softplus_f32(u);
         u = fminf(fmaxf(u, p.dt_min), p.dt_max);
@@ -240,34 +249,57 @@ __global__ __launch_bounds__(kThreads) void ssd_bmm_kernel(const SsdParams p) {
 
 // ------------------------------------------------------------------- state
 
-// Tokens staged per pass of the state kernel, and the LDS row pitch (in 16-bit
-// elements) of the transposed tiles: 16 bytes of padding keeps rows 16-byte
-// aligned for the fragment reads and staggers their banks.
-constexpr int kStateBlock = 64;
-constexpr int kPitch = kStateBlock + 8;
-
-// LDS bytes of the state kernel: sv, scum, swave, sw, then x^T high and low
-// parts [P][kPitch] and B^T [N][kPitch].
-__host__ __device__ constexpr unsigned state_lds_bytes(int P, int N, int Q) {
-    return 4u * Q + 8u * Q + 8u * kWaves + 4u * Q + 2u * (2 * P + N) * kPitch;
+// Transposed tiles in LDS keep the 16-byte chunks of each row permuted by the
+// row's octet: chunk c of row r lives at chunk c ^ ((r / 8) % 8). The
+// transposing stores (eight rows at once) then spread over the banks, and a
+// fragment read (eight consecutive values of one row) stays one 16-byte access.
+// Rows hold a multiple of 64 elements, so the permutation stays inside the row.
+__device__ __forceinline__ int swz(int r, int col) {
+    return (((col >> 3) ^ ((r >> 3) & 7)) << 3) | (col & 7);
 }
 
-// One workgroup per (chunk, head); only the workgroups of chunks that open a
-// request (the first chunk, or seq_idx changes) work: each walks its request's
-// chunks in order with the state in MFMA accumulators. Wave w owns the
-// accumulator tiles of dstate columns [w N/4, (w + 1) N/4) for every row p.
+// The chunk-state kernel: one workgroup per (chunk, head, block of PS rows,
+// block of NS dstate columns) computes the chunk's own contribution to the
+// state, L_c = sum_s exp(cum_last - cum_s) v_s x_s B_s^T (fp32, into the
+// workspace), and for the first block of each (chunk, head) the chunk's decay
+// exponent cum_last. All of the chunk's x and B loads are issued at the start;
+// tokens pass through LDS KB at a time. Wave w owns dstate column tile w of the
+// block, all row tiles.
+constexpr int kStatePS = 32, kStateNS = 64, kStateKB = 128;
+constexpr int kStatePitch = kStateKB + 8;  // LDS row pitch of the transposed tiles
+
+// LDS bytes of the chunk-state kernel: sv, scum, swave, sw; x^T high and low
+// parts [PS][pitch] and B^T [NS][pitch]; the same area later holds the fp32
+// output block [PS][NS + 4].
+__host__ __device__ constexpr unsigned state_lds_bytes(int Q) {
+    return 4u * Q + 8u * Q + 8u * kWaves + 4u * Q + 2u * (2 * kStatePS + kStateNS) * kStatePitch;
+}
+
 template <typename IT, typename ST, int P, int N, int Q>
-__global__ __launch_bounds__(kThreads) void ssd_state_kernel(const SsdParams p) {
+__global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SsdParams p) {
     typedef typename Mfma<IT>::v8 v8;
-    constexpr int PT = P / 16;             // row tiles
-    constexpr int NTW = N / 16 / kWaves;   // column tiles per wave
-    static_assert(NTW >= 1 && P % 16 == 0, "tiles");
-    const int64_t c0 = blockIdx.x / p.nheads;
-    const int h = blockIdx.x % p.nheads;
-    if (c0 > 0 && load_index(p.seq_idx, p.meta_i64, c0) == load_index(p.seq_idx, p.meta_i64, c0 - 1))
-        return;
+    constexpr int PS = kStatePS, NS = kStateNS, KB = kStateKB, XP = kStatePitch;
+    constexpr int PB = P / PS, NB = N / NS;
+    constexpr int PT = PS / 16;                       // row tiles per workgroup
+    static_assert(NS / 16 == kWaves, "one column tile per wave");
+    static_assert(P % PS == 0 && N % NS == 0, "blocks");
+    constexpr int XQ = PS / 8, BQ = NS / 8;           // 16-byte pieces of a token's x / B row
+    constexpr int XPASS = (KB / 2) * XQ / kThreads;   // x loads per thread (two tokens each)
+    constexpr int BPASS = (KB / 2) * BQ / kThreads;   // B loads per thread (two tokens each)
+    static_assert(XPASS >= 1 && BPASS >= 1, "passes");
+    constexpr int OP = NS + 4;                        // output block row pitch (floats)
+    static_assert(PS * OP * 4 <= 2 * (2 * PS + NS) * XP, "output block fits");
+
+    int64_t wg = blockIdx.x;
+    const int nb = static_cast<int>(wg % NB);
+    wg /= NB;
+    const int pb = static_cast<int>(wg % PB);
+    wg /= PB;
+    const int h = static_cast<int>(wg % p.nheads);
+    const int64_t c = wg / p.nheads;
     const int g = h / p.heads_per_group;
     const int H = p.nheads;
+    const int p0 = pb * PS, n0 = nb * NS;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
@@ -278,161 +310,265 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(const SsdParams p) 
     double* swave = scum + Q;
     float* sw = reinterpret_cast<float*>(swave + kWaves);
     unsigned short* xhi = reinterpret_cast<unsigned short*>(sw + Q);
-    unsigned short* xlo = xhi + P * kPitch;
-    unsigned short* bt = xlo + P * kPitch;
-
-    // Accumulator tile (pt, j): rows p = 16 pt + 4 (lane / 16) + i, columns
-    // n = 16 (wave NTW + j) + lane % 16.
-    f32x4 acc[PT][NTW];
-    const int64_t req = uniform64(load_index(p.seq_idx, p.meta_i64, c0));
-    const bool has_init = p.init && req >= 0 && req < p.batch;
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int pr = 16 * pt + 4 * (lane / 16) + i;
-                const int n = 16 * (wave * NTW + j) + lane % 16;
-                acc[pt][j][i] =
-                    has_init ? load_state<ST>(p.init, ((req * H + h) * P + pr) * N + n) : 0.f;
-            }
+    unsigned short* xlo = xhi + PS * XP;
+    unsigned short* bt = xlo + PS * XP;
+    float* oblk = reinterpret_cast<float*>(xhi);
 
     const IT* xp = static_cast<const IT*>(p.x);
     const IT* Bp = static_cast<const IT*>(p.B);
-    for (int64_t c = c0; c < p.nchunks; ++c) {
-        if (c > c0 && load_index(p.seq_idx, p.meta_i64, c) != load_index(p.seq_idx, p.meta_i64, c - 1))
-            break;
-        const Chunk ch = chunk_of<Q>(p, c);
-        lds_barrier();  // the previous chunk is done with sv / scum / the tiles
-        chunk_steps<Q>(p, ch, h, sv, scum, swave);
-        if (ch.len > 0) {
-            const double last = scum[ch.len - 1];
-            if (tid < ch.len) sw[tid] = expf(static_cast<float>(last - scum[tid])) * sv[tid];
-            const float decay = expf(static_cast<float>(last));
+    const Chunk ch = chunk_of<Q>(p, c);
+    // Every block of the chunk is requested at the start: registers of block b
+    // hold KB tokens from token KB b on.
+    constexpr int NSB = Q / KB > 0 ? Q / KB : 1;
+    u16x8 rx[NSB][XPASS][2], rb[NSB][BPASS][2];
+    auto fetch = [&](int b) {
+        const int s0 = KB * b;
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
+        for (int r = 0; r < XPASS; ++r) {
+            const int idx = tid + kThreads * r, q = idx % XQ, s = s0 + 2 * (idx / XQ);
+            const IT* row = xp + ((ch.lo + s) * H + h) * P + p0 + 8 * q;
+            rx[b][r][0] = s < ch.len ? *reinterpret_cast<const u16x8*>(row) : u16x8{};
+            rx[b][r][1] = s + 1 < ch.len ? *reinterpret_cast<const u16x8*>(row + H * P) : u16x8{};
+        }
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) acc[pt][j] *= decay;
+        for (int r = 0; r < BPASS; ++r) {
+            const int idx = tid + kThreads * r, q = idx % BQ, s = s0 + 2 * (idx / BQ);
+            const IT* row = Bp + ((ch.lo + s) * p.ngroups + g) * N + n0 + 8 * q;
+            rb[b][r][0] = s < ch.len ? *reinterpret_cast<const u16x8*>(row) : u16x8{};
+            rb[b][r][1] = s + 1 < ch.len ? *reinterpret_cast<const u16x8*>(row + p.ngroups * N) : u16x8{};
+        }
+    };
 
-            for (int s0 = 0; s0 < ch.len; s0 += kStateBlock) {
-                lds_barrier();  // sw visible; the previous block's tiles consumed
-                // x^T: thread (token pair jp, row octet q) -> rows 8q.., columns 2jp, 2jp+1.
-                for (int idx = tid; idx < (kStateBlock / 2) * (P / 8); idx += kThreads) {
-                    const int jp = idx % (kStateBlock / 2), q = idx / (kStateBlock / 2);
-                    const int s = s0 + 2 * jp;
-                    u16x8 r0 = {}, r1 = {};
-                    float w0 = 0.f, w1 = 0.f;
-                    if (s < ch.len) {
-                        r0 = *reinterpret_cast<const u16x8*>(xp + ((ch.lo + s) * H + h) * P + 8 * q);
-                        w0 = sw[s];
-                    }
-                    if (s + 1 < ch.len) {
-                        r1 = *reinterpret_cast<const u16x8*>(xp + ((ch.lo + s + 1) * H + h) * P + 8 * q);
-                        w1 = sw[s + 1];
-                    }
+    const float u = load_step(p, ch, h);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float a0 = f32_of<IT>(r0[e]) * w0, a1 = f32_of<IT>(r1[e]) * w1;
-                        const unsigned short h0 = bits_of<IT>(a0), h1 = bits_of<IT>(a1);
-                        const unsigned short l0 = bits_of<IT>(a0 - f32_of<IT>(h0));
-                        const unsigned short l1 = bits_of<IT>(a1 - f32_of<IT>(h1));
-                        const int o = (8 * q + e) * kPitch + 2 * jp;
-                        *reinterpret_cast<unsigned*>(xhi + o) = h0 | (static_cast<unsigned>(h1) << 16);
-                        *reinterpret_cast<unsigned*>(xlo + o) = l0 | (static_cast<unsigned>(l1) << 16);
-                    }
-                }
-                // B^T: thread (token pair, dstate octet) -> rows 8q.., columns 2jp, 2jp+1.
-                for (int idx = tid; idx < (kStateBlock / 2) * (N / 8); idx += kThreads) {
-                    const int jp = idx % (kStateBlock / 2), q = idx / (kStateBlock / 2);
-                    const int s = s0 + 2 * jp;
-                    u16x8 r0 = {}, r1 = {};
-                    if (s < ch.len)
-                        r0 = *reinterpret_cast<const u16x8*>(Bp + ((ch.lo + s) * p.ngroups + g) * N + 8 * q);
-                    if (s + 1 < ch.len)
-                        r1 = *reinterpret_cast<const u16x8*>(Bp + ((ch.lo + s + 1) * p.ngroups + g) * N + 8 * q);
+    for (int b = 0; b < NSB; ++b) fetch(b);
+    chunk_steps<Q>(p, ch, h, u, sv, scum, swave);
+    f32x4 acc[PT];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        *reinterpret_cast<unsigned*>(bt + (8 * q + e) * kPitch + 2 * jp) =
-                            r0[e] | (static_cast<unsigned>(r1[e]) << 16);
-                }
-                lds_barrier();
+    for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ch.len > 0) {
+        const double last = scum[ch.len - 1];
+        if (tid < ch.len) sw[tid] = expf(static_cast<float>(last - scum[tid])) * sv[tid];
+        if (pb == 0 && nb == 0 && tid == 0) p.cumlast[c * H + h] = static_cast<float>(last);
+    } else if (pb == 0 && nb == 0 && tid == 0) {
+        p.cumlast[c * H + h] = 0.f;
+    }
 #pragma unroll
-                for (int kk = 0; kk < kStateBlock; kk += 32) {
-                    if (s0 + kk >= ch.len) break;
-                    const int col = kk + 8 * (lane / 16);
-                    v8 bf[NTW];
+    for (int sb = 0; sb < NSB; ++sb) {
+        const int s0 = KB * sb;
+        if (s0 >= ch.len) break;
+        lds_barrier();  // sw visible; the previous block's tiles consumed
+        // x^T (scaled, high and low parts) and B^T into LDS.
 #pragma unroll
-                    for (int j = 0; j < NTW; ++j)
-                        bf[j] = *reinterpret_cast<const v8*>(bt + (16 * (wave * NTW + j) + lane % 16) * kPitch + col);
+        for (int r = 0; r < XPASS; ++r) {
+            const int idx = tid + kThreads * r, q = idx % XQ, j = 2 * (idx / XQ);
+            const float w0 = s0 + j < ch.len ? sw[s0 + j] : 0.f;
+            const float w1 = s0 + j + 1 < ch.len ? sw[s0 + j + 1] : 0.f;
 #pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) {
-                        const int row = (16 * pt + lane % 16) * kPitch + col;
-                        const v8 ah = *reinterpret_cast<const v8*>(xhi + row);
-                        const v8 al = *reinterpret_cast<const v8*>(xlo + row);
-#pragma unroll
-                        for (int j = 0; j < NTW; ++j) {
-                            acc[pt][j] = Mfma<IT>::mma16(ah, bf[j], acc[pt][j]);
-                            acc[pt][j] = Mfma<IT>::mma16(al, bf[j], acc[pt][j]);
-                        }
-                    }
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float a0 = f32_of<IT>(rx[sb][r][0][e]) * w0, a1 = f32_of<IT>(rx[sb][r][1][e]) * w1;
+                const unsigned short h0 = bits_of<IT>(a0), h1 = bits_of<IT>(a1);
+                const unsigned short l0 = bits_of<IT>(a0 - f32_of<IT>(h0));
+                const unsigned short l1 = bits_of<IT>(a1 - f32_of<IT>(h1));
+                const int row = 8 * q + e, o = row * XP + swz(row, j);
+                *reinterpret_cast<unsigned*>(xhi + o) = h0 | (static_cast<unsigned>(h1) << 16);
+                *reinterpret_cast<unsigned*>(xlo + o) = l0 | (static_cast<unsigned>(l1) << 16);
             }
         }
-        // The state after chunk c: in the io type for the scan of chunk c + 1, and
-        // in the state type where the caller asked for it.
-        IT* s16 = static_cast<IT*>(p.s16);
-        const bool feeds_next = c + 1 < p.nchunks &&
-            load_index(p.seq_idx, p.meta_i64, c + 1) == load_index(p.seq_idx, p.meta_i64, c);
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
+        for (int r = 0; r < BPASS; ++r) {
+            const int idx = tid + kThreads * r, q = idx % BQ, j = 2 * (idx / BQ);
 #pragma unroll
-            for (int j = 0; j < NTW; ++j)
+            for (int e = 0; e < 8; ++e) {
+                const int row = 8 * q + e;
+                *reinterpret_cast<unsigned*>(bt + row * XP + swz(row, j)) =
+                    rb[sb][r][0][e] | (static_cast<unsigned>(rb[sb][r][1][e]) << 16);
+            }
+        }
+        lds_barrier();
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int pr = 16 * pt + 4 * (lane / 16) + i;
-                    const int n = 16 * (wave * NTW + j) + lane % 16;
-                    const int64_t e = (static_cast<int64_t>(h) * P + pr) * N + n;
-                    if (feeds_next) s16[c * H * P * N + e] = static_cast<IT>(acc[pt][j][i]);
-                    if (p.return_all) store_state<ST>(p.states, c * H * P * N + e, acc[pt][j][i]);
-                }
-        if (!p.return_all) {
-            int64_t b = uniform64(p.list_head[c]);
-            for (int64_t hops = 0; b >= 0 && b < p.batch && hops < p.batch; ++hops) {
+        for (int kk = 0; kk < KB; kk += 32) {
+            if (s0 + kk >= ch.len) break;
+            const int col = kk + 8 * (lane / 16);
+            const int brow = 16 * wave + lane % 16;
+            const v8 bf = *reinterpret_cast<const v8*>(bt + brow * XP + swz(brow, col));
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
+            for (int pt = 0; pt < PT; ++pt) {
+                const int row = 16 * pt + lane % 16, o = row * XP + swz(row, col);
+                acc[pt] = Mfma<IT>::mma16(*reinterpret_cast<const v8*>(xhi + o), bf, acc[pt]);
+                acc[pt] = Mfma<IT>::mma16(*reinterpret_cast<const v8*>(xlo + o), bf, acc[pt]);
+            }
+        }
+    }
+
+    // L_c through LDS, so that rows leave whole: thread t writes 8 consecutive
+    // columns of row t / (NS / 8). A chunk that opens a request with an initial
+    // state h0 stores exp(cum_last) h0 + L_c instead: the state after it.
+    lds_barrier();
 #pragma unroll
-                    for (int j = 0; j < NTW; ++j)
+    for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int pr = 16 * pt + 4 * (lane / 16) + i;
-                            const int n = 16 * (wave * NTW + j) + lane % 16;
-                            store_state<ST>(p.states, ((b * H + h) * P + pr) * N + n, acc[pt][j][i]);
-                        }
-                b = uniform64(p.list_next[b]);
+        for (int i = 0; i < 4; ++i)
+            oblk[(16 * pt + 4 * (lane / 16) + i) * OP + 16 * wave + lane % 16] = acc[pt][i];
+    lds_barrier();
+    static_assert(PS * NS / 8 == kThreads, "one 8-column piece per thread");
+    const int orow = tid / (NS / 8), ocol = 8 * (tid % (NS / 8));
+    const f32x4* src = reinterpret_cast<const f32x4*>(oblk + orow * OP + ocol);
+    f32x4 v0 = src[0], v1 = src[1];
+    const int64_t req = uniform64(load_index(p.seq_idx, p.meta_i64, c));
+    const bool opens = c == 0 || req != load_index(p.seq_idx, p.meta_i64, c - 1);
+    if (opens && p.init && req >= 0 && req < p.batch) {
+        const float decay = ch.len > 0 ? expf(static_cast<float>(scum[ch.len - 1])) : 1.f;
+        const int64_t base = ((req * H + h) * P + p0 + orow) * static_cast<int64_t>(N) + n0 + ocol;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v0[j] = fmaf(decay, load_state<ST>(p.init, base + j), v0[j]);
+            v1[j] = fmaf(decay, load_state<ST>(p.init, base + 4 + j), v1[j]);
+        }
+    }
+    f32x4* dst = reinterpret_cast<f32x4*>(
+        p.local + ((c * H + h) * P + p0 + orow) * static_cast<int64_t>(N) + n0 + ocol);
+    dst[0] = v0;
+    dst[1] = v1;
+}
+
+// State passing: thread owns four consecutive elements of one head's state and
+// walks all chunks in order: a chunk that opens a request takes its stored
+// value as the state (it already holds the initial state's decayed
+// contribution), every other chunk applies S = exp(cum_last) S + L_c. The chunk
+// values are requested kPassDepth chunks ahead and every step makes the same
+// memory accesses (one load, two stores; a step with nothing to return writes
+// its state to a private dummy slot), so the loads stay in flight across steps.
+// S leaves in the io type for the scan of the next chunk, and in the state type
+// for chunk c (every chunk) or for the first request whose last chunk is c;
+// ssd_fixup_kernel copies it to further requests naming the same chunk.
+constexpr int kPassThreads = 256;
+constexpr int kPassDepth = 8;
+
+template <typename IT, typename ST, int P, int N>
+__global__ __launch_bounds__(kPassThreads) void ssd_state_passing_kernel(const SsdParams p) {
+    constexpr int PER_HEAD = P * N / 4;  // threads per head
+    static_assert(PER_HEAD % kPassThreads == 0, "a workgroup stays in one head");
+    constexpr int W = kPassThreads;      // chunks whose metadata one LDS window holds
+    static_assert(W % kPassDepth == 0, "windows hold whole blocks");
+    typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+    typedef ST st4 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x;
+    const int64_t gt = static_cast<int64_t>(blockIdx.x) * kPassThreads + tid;
+    const int h = __builtin_amdgcn_readfirstlane(static_cast<int>(gt / PER_HEAD));
+    const int64_t e = (gt % PER_HEAD) * 4;        // element within the head's state
+    const int H = p.nheads;
+    const int64_t tile = static_cast<int64_t>(H) * P * N;
+    const int64_t he = static_cast<int64_t>(h) * P * N + e;
+    ST* const dummy = static_cast<ST*>(p.dummy) + he;
+    const int64_t last = p.nchunks - 1;
+
+    // Metadata of a window of W chunks, staged in LDS (LDS reads do not wait on
+    // the vector-memory counter the prefetched loads are tracked by): whether the
+    // chunk opens a request, its decay, and where its state is returned (-1: not).
+    __shared__ int s_open[W];
+    __shared__ float s_decay[W];
+    __shared__ int64_t s_dest[W];
+
+    f32x4 ring[kPassDepth];
+#pragma unroll
+    for (int j = 0; j < kPassDepth; ++j)
+        ring[j] = *reinterpret_cast<const f32x4*>(p.local + min<int64_t>(j, last) * tile + he);
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t w0 = 0; w0 < p.nchunks; w0 += W) {
+        __syncthreads();  // the previous window's metadata is consumed
+        {
+            const int64_t c = w0 + tid;
+            if (c <= last) {
+                const int64_t r = load_index(p.seq_idx, p.meta_i64, c);
+                s_open[tid] = c == 0 || r != load_index(p.seq_idx, p.meta_i64, c - 1);
+                s_decay[tid] = expf(p.cumlast[c * H + h]);
+                const int64_t b = p.return_all ? c : p.list_head[c];
+                s_dest[tid] = (b >= 0 && b < (p.return_all ? p.nchunks : p.batch)) ? b : -1;
+            }
+        }
+        __syncthreads();
+        // Branch-free steps (selects and clamped or dummy addresses), so the
+        // compiler can keep the ring's loads in flight across them.
+        for (int64_t c0 = w0; c0 < w0 + W && c0 <= last; c0 += kPassDepth) {
+#pragma unroll
+            for (int j = 0; j < kPassDepth; ++j) {
+                const int64_t c = c0 + j;
+                const bool valid = c <= last;
+                const int k = valid ? static_cast<int>(c - w0) : 0;
+                const f32x4 local = ring[j];
+                ring[j] = *reinterpret_cast<const f32x4*>(
+                    p.local + min<int64_t>(c + kPassDepth, last) * tile + he);
+                const bool open = s_open[k] != 0;
+                const float d = s_decay[k];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[i] = open ? local[i] : fmaf(d, S[i], local[i]);
+                u16x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = bits_of<IT>(S[i]);
+                IT* s16 = valid ? static_cast<IT*>(p.s16) + c * tile + he
+                                : reinterpret_cast<IT*>(dummy);
+                *reinterpret_cast<u16x4*>(s16) = o;
+                const int64_t b = valid ? s_dest[k] : -1;
+                ST* dst = b >= 0 ? static_cast<ST*>(p.states) + b * tile + he : dummy;
+                st4 q;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q[i] = static_cast<ST>(S[i]);
+                *reinterpret_cast<st4*>(dst) = q;
             }
         }
     }
 }
 
-// -------------------------------------------------------------------- scan
-
-constexpr int scan_pitch(int Q) { return Q + 8; }
-
-// LDS bytes of the scan kernel: sv, cum (fp32), scum (fp64), swave, then
-// (v x)^T [P][Q + 8].
-__host__ __device__ constexpr unsigned scan_lds_bytes(int P, int Q) {
-    return 4u * Q + 4u * Q + 8u * Q + 8u * kWaves + 2u * P * scan_pitch(Q);
+// Requests whose last chunk is also another request's (only an inconsistent
+// caller makes two requests name one chunk) get that request's returned state.
+// One workgroup per request.
+template <typename ST, int P, int N>
+__global__ __launch_bounds__(kPassThreads) void ssd_fixup_kernel(const SsdParams p) {
+    const int64_t b = blockIdx.x;
+    const int64_t c = load_index(p.lci, p.meta_i64, b);
+    if (c < 0 || c >= p.nchunks) return;
+    const int64_t first = p.list_head[c];
+    if (first == b || first < 0 || first >= p.batch) return;
+    const int64_t tile = static_cast<int64_t>(p.nheads) * P * N;
+    const ST* src = static_cast<const ST*>(p.states) + first * tile;
+    ST* dst = static_cast<ST*>(p.states) + b * tile;
+    for (int64_t i = threadIdx.x; i < tile; i += kPassThreads) dst[i] = src[i];
 }
 
-// One workgroup per (chunk, head). Wave w owns the output rows of token tiles
-// w, w + 4, w + 8, ... (16 tokens each) for all P columns.
+// -------------------------------------------------------------------- scan
+
+// The scan runs Q / 32 waves: two 16-token tiles of the chunk per wave.
+__host__ __device__ constexpr int scan_threads(int Q) { return 2 * Q; }
+constexpr int scan_pitch(int Q) { return Q + 8; }       // (v x)^T row pitch, elements
+constexpr int state_pitch(int N) { return N + 8; }      // entering-state row pitch
+
+// LDS bytes of the scan kernel: sv, the log2-scaled running sums (fp32), the
+// fp64 running sums, one fp64 per wave, the entering state [P][N + 8] and
+// (v x)^T [P][Q + 8], both in the io type.
+__host__ __device__ constexpr unsigned scan_lds_bytes(int P, int N, int Q) {
+    return 4u * Q + 4u * Q + 8u * Q + 8u * (scan_threads(Q) / 64) + 2u * P * state_pitch(N) +
+           2u * P * scan_pitch(Q);
+}
+
+// (v x)^T and the entering state are stored permuted by swz().
+
+// One workgroup per (chunk, head); wave w owns token tiles w and w + Q / 32.
+// Independent loads are issued before anything waits: the x tile, the entering
+// state and the first C operands at the start, each product's next operands
+// before its current matrix-core work.
 template <typename IT, typename ST, int P, int N, int Q>
-__global__ __launch_bounds__(kThreads) void ssd_scan_kernel(const SsdParams p) {
+__global__ __launch_bounds__(scan_threads(Q)) void ssd_scan_kernel(const SsdParams p) {
     typedef typename Mfma<IT>::v8 v8;
-    constexpr int PT = P / 16;
-    constexpr int TT = Q / 16 / kWaves;  // token tiles per wave
-    constexpr int XP = scan_pitch(Q);
+    constexpr int NT = scan_threads(Q), NW = NT / 64;
+    constexpr int PT = P / 16, TT = 2, KN = N / 32;
+    constexpr int XP = scan_pitch(Q), SP = state_pitch(N);
+    constexpr int XPASS = (Q / 2) * (P / 8) / NT;   // x loads per thread (token pairs x row octets)
+    constexpr int SPASS = P * (N / 8) / NT;         // entering-state 16-byte chunks per thread
+    static_assert(XPASS * NT == (Q / 2) * (P / 8) && SPASS * NT == P * (N / 8), "passes");
+    static_assert((SP * 2) % 16 == 0 && (XP * 2) % 16 == 0, "16-byte rows");
+    constexpr float kLog2e = 1.4426950408889634f;
+
     const int64_t c = blockIdx.x / p.nheads;
     const int h = blockIdx.x % p.nheads;
     const Chunk ch = chunk_of<Q>(p, c);
@@ -445,136 +581,241 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(const SsdParams p) {
 
     extern __shared__ __align__(16) unsigned char smem[];
     float* sv = reinterpret_cast<float*>(smem);
-    float* cumf = sv + Q;
-    double* scum = reinterpret_cast<double*>(cumf + Q);
+    float* cum2 = sv + Q;
+    double* scum = reinterpret_cast<double*>(cum2 + Q);
     double* swave = scum + Q;
-    unsigned short* xv = reinterpret_cast<unsigned short*>(swave + kWaves);
+    unsigned short* sS = reinterpret_cast<unsigned short*>(swave + NW);
+    unsigned short* xv = sS + P * SP;
 
-    chunk_steps<Q>(p, ch, h, sv, scum, swave);
-    if (tid < Q) cumf[tid] = static_cast<float>(scum[tid]);
-
-    // (v x)^T into LDS, rounded once to the io type.
     const IT* xp = static_cast<const IT*>(p.x);
-    for (int idx = tid; idx < (Q / 2) * (P / 8); idx += kThreads) {
-        const int jp = idx % (Q / 2), q = idx / (Q / 2);
-        const int s = 2 * jp;
-        u16x8 r0 = {}, r1 = {};
-        float v0 = 0.f, v1 = 0.f;
-        if (s < ch.len) {
-            r0 = *reinterpret_cast<const u16x8*>(xp + ((ch.lo + s) * H + h) * P + 8 * q);
-            v0 = sv[s];
-        }
-        if (s + 1 < ch.len) {
-            r1 = *reinterpret_cast<const u16x8*>(xp + ((ch.lo + s + 1) * H + h) * P + 8 * q);
-            v1 = sv[s + 1];
-        }
+    const IT* Cp = static_cast<const IT*>(p.C);
+
+    // ---- loads issued up front: the steps, the x tile, the entering state and
+    // the first C operands.
+    const float u = load_step(p, ch, h);
+    // x: thread handles row octet q of token pair jp (eight threads per token row).
+    u16x8 rx[XPASS][2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            *reinterpret_cast<unsigned*>(xv + (8 * q + e) * XP + s) =
-                bits_of<IT>(f32_of<IT>(r0[e]) * v0) |
-                (static_cast<unsigned>(bits_of<IT>(f32_of<IT>(r1[e]) * v1)) << 16);
+    for (int r = 0; r < XPASS; ++r) {
+        const int idx = tid + NT * r, q = idx % (P / 8), s = 2 * (idx / (P / 8));
+        const IT* row = xp + ((ch.lo + s) * H + h) * P + 8 * q;
+        rx[r][0] = s < ch.len ? *reinterpret_cast<const u16x8*>(row) : u16x8{};
+        rx[r][1] = s + 1 < ch.len ? *reinterpret_cast<const u16x8*>(row + H * P) : u16x8{};
     }
+    // The entering state: the previous chunk's (io type) or the request's initial state.
+    const int64_t req = uniform64(load_index(p.seq_idx, p.meta_i64, c));
+    const bool opens = c == 0 || req != load_index(p.seq_idx, p.meta_i64, c - 1);
+    const bool from_init = opens && p.init && req >= 0 && req < p.batch;
+    const bool has_state = !opens || from_init;
+    u16x8 rs[SPASS];
+#pragma unroll
+    for (int r = 0; r < SPASS; ++r) {
+        const int ci = tid + NT * r, pr = ci / (N / 8), n8 = 8 * (ci % (N / 8));
+        if (!opens) {
+            rs[r] = *reinterpret_cast<const u16x8*>(static_cast<const IT*>(p.s16) +
+                                                    (((c - 1) * H + h) * P + pr) * N + n8);
+        } else if (from_init) {
+            const int64_t base = ((req * H + h) * P + pr) * N + n8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) rs[r][j] = bits_of<IT>(load_state<ST>(p.init, base + j));
+        } else {
+            rs[r] = u16x8{};
+        }
+    }
+    // C operands of the entering-state product, first k step.
+    int trow[TT];
+#pragma unroll
+    for (int k = 0; k < TT; ++k) trow[k] = min(16 * (wave + NW * k) + lane % 16, ch.len - 1);
+    const int kcol = 8 * (lane / 16);
+    auto c_frag = [&](int k, int kk) {
+        return *reinterpret_cast<const v8*>(Cp + ((ch.lo + trow[k]) * p.ngroups + g) * N + kk + kcol);
+    };
+    v8 cf[TT];
+    if (has_state) {
+#pragma unroll
+        for (int k = 0; k < TT; ++k) cf[k] = c_frag(k, 0);
+    }
+
+    chunk_steps<Q, NT>(p, ch, h, u, sv, scum, swave);
+    if (tid < Q) cum2[tid] = static_cast<float>(scum[tid]) * kLog2e;
+
+    // x^T (exact) and the entering state into LDS.
+#pragma unroll
+    for (int r = 0; r < XPASS; ++r) {
+        const int idx = tid + NT * r, q = idx % (P / 8), s = 2 * (idx / (P / 8));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int pr = 8 * q + e;
+            *reinterpret_cast<unsigned*>(xv + pr * XP + swz(pr, s)) =
+                rx[r][0][e] | (static_cast<unsigned>(rx[r][1][e]) << 16);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < SPASS; ++r) {
+        const int ci = tid + NT * r, pr = ci / (N / 8), n8 = 8 * (ci % (N / 8));
+        *reinterpret_cast<u16x8*>(sS + pr * SP + swz(pr, n8)) = rs[r];
+    }
+    lds_barrier();
 
     f32x4 acc[TT][PT];
 #pragma unroll
     for (int k = 0; k < TT; ++k)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // ---- the state entering the chunk: C_t . S_in, then scaled by exp(cum_t)
-    const int64_t req = uniform64(load_index(p.seq_idx, p.meta_i64, c));
-    const bool opens = c == 0 || req != load_index(p.seq_idx, p.meta_i64, c - 1);
-    const bool from_init = opens && p.init && req >= 0 && req < p.batch;
-    const IT* Cp = static_cast<const IT*>(p.C);
-    if (!opens || from_init) {
+    bool live[TT];
 #pragma unroll
-        for (int kk = 0; kk < N; kk += 32) {
-            const int col = kk + 8 * (lane / 16);
+    for (int k = 0; k < TT; ++k) live[k] = 16 * (wave + NW * k) < ch.len;
+
+    // ---- the entering state: C_t . S_in, then scaled by exp(cum_t)
+    if (has_state) {
+#pragma unroll
+        for (int ks = 0; ks < KN; ++ks) {
+            v8 cn[TT];
+            if (ks + 1 < KN) {
+#pragma unroll
+                for (int k = 0; k < TT; ++k) cn[k] = c_frag(k, 32 * (ks + 1));
+            }
             v8 sf[PT];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const int pr = 16 * pt + lane % 16;
-                if (!opens) {
-                    sf[pt] = *reinterpret_cast<const v8*>(static_cast<const IT*>(p.s16) +
-                                                          (((c - 1) * H + h) * P + pr) * N + col);
-                } else {
-                    const int64_t base = ((req * H + h) * P + pr) * N + col;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) sf[pt][j] = static_cast<IT>(load_state<ST>(p.init, base + j));
-                }
+                sf[pt] = *reinterpret_cast<const v8*>(sS + pr * SP + swz(pr, 32 * ks + kcol));
             }
 #pragma unroll
-            for (int k = 0; k < TT; ++k) {
-                const int t0 = 16 * (wave + kWaves * k);
-                if (t0 >= ch.len) continue;
-                const int t = min(t0 + lane % 16, ch.len - 1);
-                const v8 ca = *reinterpret_cast<const v8*>(Cp + ((ch.lo + t) * p.ngroups + g) * N + col);
+            for (int k = 0; k < TT; ++k)
+                if (live[k])
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(ca, sf[pt], acc[k][pt]);
+                    for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(cf[k], sf[pt], acc[k][pt]);
+            if (ks + 1 < KN) {
+#pragma unroll
+                for (int k = 0; k < TT; ++k) cf[k] = cn[k];
             }
         }
 #pragma unroll
         for (int k = 0; k < TT; ++k)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = min(16 * (wave + kWaves * k) + 4 * (lane / 16) + i, Q - 1);
-                const float f = expf(static_cast<float>(scum[t]));
+                const int t = min(16 * (wave + NW * k) + 4 * (lane / 16) + i, Q - 1);
+                const float f = __builtin_amdgcn_exp2f(cum2[t]);
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) acc[k][pt][i] *= f;
             }
     }
-    lds_barrier();  // (v x)^T and cumf complete
 
-    // ---- inside the chunk: (CB masked by the decays) times (v x)
+    // ---- inside the chunk: (C B^T masked, times the decays and the steps v_s)
+    // times x. Tile k needs the s blocks kk <= its last row; the next block's
+    // C B^T entries are requested before the current block's products.
     const float* cbp = p.cb + (c * p.ngroups + g) * Q * Q;
+    f32x4 cb[TT][2];
+    // Tile k's C B^T entries of s block kk, if the tile needs that block.
+    auto cb_load = [&](int k, int kk) {
+        const int t0 = 16 * (wave + NW * k);
+        if (live[k] && t0 + 15 >= kk && kk < ch.len) {
+            const f32x4* r = reinterpret_cast<const f32x4*>(cbp + (t0 + lane % 16) * Q + kk + kcol);
+            cb[k][0] = r[0];
+            cb[k][1] = r[1];
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < TT; ++k) cb_load(k, 0);
     for (int kk = 0; kk < ch.len; kk += 32) {
-        const int col = kk + 8 * (lane / 16);
+        const int col = kk + kcol;
         v8 xf[PT];
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
-            xf[pt] = *reinterpret_cast<const v8*>(xv + (16 * pt + lane % 16) * XP + col);
-        float cs[8];
+        for (int pt = 0; pt < PT; ++pt) {
+            const int pr = 16 * pt + lane % 16;
+            xf[pt] = *reinterpret_cast<const v8*>(xv + pr * XP + swz(pr, col));
+        }
+        float cs[8], vs[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) cs[j] = cumf[col + j];
+        for (int j = 0; j < 8; ++j) {
+            cs[j] = cum2[col + j];
+            vs[j] = sv[col + j];
+        }
 #pragma unroll
         for (int k = 0; k < TT; ++k) {
-            const int t0 = 16 * (wave + kWaves * k);
-            if (t0 >= ch.len || t0 + 15 < kk) continue;
+            const int t0 = 16 * (wave + NW * k);
+            if (!live[k] || t0 + 15 < kk) continue;
             const int t = t0 + lane % 16;
-            const f32x4* cbr = reinterpret_cast<const f32x4*>(cbp + t * Q + col);
-            const f32x4 m0 = cbr[0], m1 = cbr[1];
-            const float ct = cumf[t];
+            const float ct = cum2[t];
             v8 a;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float m = j < 4 ? m0[j] : m1[j - 4];
-                const bool live = col + j <= t && t < ch.len;
-                a[j] = static_cast<IT>(live ? m * expf(ct - cs[j]) : 0.f);
+                const float m = cb[k][j / 4][j % 4];
+                const bool on = col + j <= t && t < ch.len;
+                a[j] = static_cast<IT>(on ? m * vs[j] * __builtin_amdgcn_exp2f(ct - cs[j]) : 0.f);
             }
+            cb_load(k, kk + 32);  // the tile's next block, in flight during the products
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(a, xf[pt], acc[k][pt]);
         }
     }
 
-    // ---- skip term, gate, store
+    // z rows of the epilogue, requested before the skip term: lane l finishes 16
+    // consecutive columns of row l / 4 of each of its tiles.
     const IT* zp = static_cast<const IT*>(p.z);
-    IT* op = static_cast<IT*>(p.out);
+    const int er = lane / 4, ec = (lane % 4) * (P / 4);
+    static_assert(P / 4 == 16, "one lane finishes 16 columns");
+    u16x8 ez[TT][2];
+    if (zp) {
 #pragma unroll
-    for (int k = 0; k < TT; ++k)
+        for (int k = 0; k < TT; ++k) {
+            const int t = min(16 * (wave + NW * k) + er, ch.len - 1);
+            const IT* zr = zp + ((ch.lo + t) * H + h) * P + ec;
+            ez[k][0] = *reinterpret_cast<const u16x8*>(zr);
+            ez[k][1] = *reinterpret_cast<const u16x8*>(zr + 8);
+        }
+    }
+    // ---- skip term from the exact x^T in LDS (row t's four consecutive tokens
+    // are one 8-byte read), then gate and store: each tile goes through a
+    // wave-private LDS scratch spanning the entering-state and x^T areas (free
+    // once every wave is past this point) so that z and out move as whole rows.
+    if (p.D) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * (wave + kWaves * k) + 4 * (lane / 16) + i;
-            if (t >= ch.len) continue;
+        for (int k = 0; k < TT; ++k)
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const int pr = 16 * pt + lane % 16;
-                const int64_t xi = ((ch.lo + t) * H + h) * P + pr;
-                float y = acc[k][pt][i];
-                if (p.D) y += (p.D_per_dim ? p.D[h * P + pr] : p.D[h]) * static_cast<float>(xp[xi]);
-                if (zp) y *= silu_f32(static_cast<float>(zp[xi]));
-                op[xi] = static_cast<IT>(y);
+                const int t = 16 * (wave + NW * k) + 4 * (lane / 16);
+                typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+                const u16x4 xr = *reinterpret_cast<const u16x4*>(xv + pr * XP + swz(pr, t));
+                const float d = p.D_per_dim ? p.D[h * P + pr] : p.D[h];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[k][pt][i] += d * f32_of<IT>(xr[i]);
             }
+    }
+    constexpr int EP = P + 4;  // scratch row pitch in floats (16-byte aligned rows)
+    static_assert(NW * 16 * EP * 4 <= 2 * P * (SP + XP), "epilogue scratch fits");
+    IT* op = static_cast<IT*>(p.out);
+    lds_barrier();
+    float* scratch = reinterpret_cast<float*>(sS) + wave * 16 * EP;
+#pragma unroll
+    for (int k = 0; k < TT; ++k) {
+        if (!live[k]) break;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) scratch[(4 * (lane / 16) + i) * EP + 16 * pt + lane % 16] = acc[k][pt][i];
+        ssu::wave_lds_sync();
+        const int t = 16 * (wave + NW * k) + er;
+        if (t < ch.len) {
+            const int64_t xi = ((ch.lo + t) * H + h) * P + ec;
+            const f32x4* srow = reinterpret_cast<const f32x4*>(scratch + er * EP + ec);
+            u16x8 o0, o1;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float y = srow[e / 4][e % 4];
+                if (zp) y *= silu_f32(f32_of<IT>(ez[k][e / 8][e % 8]));
+                if (e < 8)
+                    o0[e] = bits_of<IT>(y);
+                else
+                    o1[e - 8] = bits_of<IT>(y);
+            }
+            *reinterpret_cast<u16x8*>(op + xi) = o0;
+            *reinterpret_cast<u16x8*>(op + xi + 8) = o1;
         }
+        ssu::wave_lds_sync();  // the next tile reuses the scratch
+    }
 }
 
 }  // namespace ssd
@@ -590,11 +831,19 @@ hipError_t launch_instance(const SsdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL(ssd_list_kernel<0>, dim3(1), dim3(1024), 0, stream, p);
     hipLaunchKernelGGL((ssd_bmm_kernel<IT, N, Q>), dim3(static_cast<unsigned>(p.nchunks * p.ngroups)),
                        dim3(kThreads), 0, stream, p);
-    const dim3 grid(static_cast<unsigned>(p.nchunks * p.nheads));
-    hipLaunchKernelGGL((ssd_state_kernel<IT, ST, P, N, Q>), grid, dim3(kThreads),
-                       state_lds_bytes(P, N, Q), stream, p);
-    hipLaunchKernelGGL((ssd_scan_kernel<IT, ST, P, N, Q>), grid, dim3(kThreads), scan_lds_bytes(P, Q),
-                       stream, p);
+    const unsigned state_grid =
+        static_cast<unsigned>(p.nchunks * p.nheads * (P / kStatePS) * (N / kStateNS));
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<IT, ST, P, N, Q>), dim3(state_grid), dim3(kThreads),
+                       state_lds_bytes(Q), stream, p);
+    hipLaunchKernelGGL((ssd_state_passing_kernel<IT, ST, P, N>),
+                       dim3(static_cast<unsigned>(p.nheads * P * N / 4 / kPassThreads)),
+                       dim3(kPassThreads), 0, stream, p);
+    if (!p.return_all && p.batch > 0)
+        hipLaunchKernelGGL((ssd_fixup_kernel<ST, P, N>), dim3(static_cast<unsigned>(p.batch)),
+                           dim3(kPassThreads), 0, stream, p);
+    hipLaunchKernelGGL((ssd_scan_kernel<IT, ST, P, N, Q>),
+                       dim3(static_cast<unsigned>(p.nchunks * p.nheads)), dim3(scan_threads(Q)),
+                       scan_lds_bytes(P, N, Q), stream, p);
     return hipGetLastError();
 }
 

@@ -288,6 +288,7 @@ def ssd(lib, **kw):
     (dict(dstate=256), UNS, "no kernel"),
     (dict(chunk_size=64), UNS, "no kernel"),
     (dict(x=addr(1) + 8), UNS, "16-byte aligned"),
+    (dict(states=addr(14) + 4), UNS, "states must be 16-byte aligned"),
     (dict(workspace_bytes=1024), INV, "workspace"),
     (dict(workspace=addr(15) + 16), INV, "workspace"),
     (dict(out=addr(1) + 64), INV, "out overlaps x"),
@@ -302,6 +303,10 @@ def test_ssd_rejects(lib, kw, code, needle):
 
 def test_ssd_workspace_bytes(lib):
     n = lib.ssu_ssd_workspace_bytes(6, 3, 8, 64, 128, 2, 256)
-    need = 6 * 8 * 64 * 128 * 2 + 6 * 2 * 256 * 256 * 4 + 6 * 4 + 3 * 4
-    assert need <= n <= need + 4 * 256 and n % 256 == 0
+    # chunk-end states (io type), C B^T per chunk and group, each chunk's own
+    # contribution (fp32), decay exponents, a dummy state tile (fp32 size), the
+    # request list.
+    need = (6 * 8 * 64 * 128 * 2 + 6 * 2 * 256 * 256 * 4 + 6 * 8 * 64 * 128 * 4 + 6 * 8 * 4
+            + 8 * 64 * 128 * 4 + 6 * 4 + 3 * 4)
+    assert need <= n <= need + 7 * 256 and n % 256 == 0
     assert lib.ssu_ssd_workspace_bytes(-1, 3, 8, 64, 128, 2, 256) == 0
