@@ -10,8 +10,10 @@ the launch's average duration from HIP events on the launch stream.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode full|kernel|copy]
 
---mode kernel times only the chosen workload (for profiler runs); --mode copy
-times only the reference copy kernel used to calibrate traffic counters.
+--mode kernel times only the chosen workload (for profiler runs; an ssd_* name
+times the SSD chunked prefill); --mode copy times only the reference copy kernel
+used to calibrate traffic counters. The SSD prefill workloads are reported under
+"workloads" with their own oracle baseline.
 """
 from __future__ import annotations
 
@@ -441,6 +443,176 @@ Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=
     print(md)
 
 
+# ------------------------------------------------------------- SSD prefill
+
+def ssd_accounting(w):
+    """Algorithmic bytes and flops of one SSD prefill call. Bytes: every input
+    read once (x, z, B, C, dt, initial states, per-head parameters, chunk
+    metadata), out and the returned states written once. Flops: the products of
+    the chunked algorithm -- C B^T over each chunk's lower triangle per group,
+    each chunk's own state, the intra-chunk product and the entering-state
+    product -- at 2 flops per multiply-add."""
+    import numpy as np
+    T, H, P = w.x.shape
+    G, N = w.B.shape[1], w.B.shape[2]
+    io = w.x.element_size()
+    ssz = {"torch.float32": 4}.get(str(w.state_dtype), 2)
+    cc = w.cu_chunk_seqlens.cpu().numpy().astype(np.int64)
+    si = w.seq_idx.cpu().numpy().astype(np.int64)
+    L = np.diff(cc)
+    nchunks = L.shape[0]
+    batch = w.last_chunk_indices.numel()
+    opens = np.ones(nchunks, dtype=bool)
+    opens[1:] = si[1:] != si[:-1]
+    entering = ~opens | (w.initial_states is not None)
+    rows_out = nchunks if w.return_intermediate_states else batch
+    meta = (w.cu_chunk_seqlens.numel() + 2 * nchunks + batch) * w.cu_chunk_seqlens.element_size()
+    read = (T * H * P * io * (1 + (w.z is not None)) + 2 * T * G * N * io
+            + T * H * w.dt.element_size() + 3 * 4 * H + meta
+            + (batch * H * P * N * ssz if w.initial_states is not None else 0))
+    write = T * H * P * io + rows_out * H * P * N * ssz
+    pairs = L * (L + 1) // 2
+    flops = float(np.sum(2 * pairs * N * G) + np.sum(2 * L) * H * P * N
+                  + np.sum(2 * pairs) * H * P + np.sum(2 * L[entering]) * H * P * N)
+    return dict(tokens=T, read_bytes=read, write_bytes=write, bytes=read + write, flops=flops,
+                nchunks=nchunks, batch=batch)
+
+
+def ssd_call(w):
+    import torch
+    import selective_state_update_ssu_amd as ssu
+    out = torch.empty_like(w.x)
+    return lambda: ssu.ssd_combined_fwd_varlen(*w.args(), out=out, **w.kwargs())
+
+
+def run_ssd_workload(name, steps, warmup):
+    import torch
+    from selective_state_update_ssu_amd import workloads as wl
+
+    w = wl.SSD_NAMED[name]("cuda")
+    acc = ssd_accounting(w)
+    wall, ev = time_calls(ssd_call(w), steps, warmup)
+    T, H, P = w.x.shape
+    rec = dict(config=dict(workload=name, mode="ssd_prefill", tokens=T,
+                           requests=acc["batch"], chunks=acc["nchunks"], chunk_size=w.chunk_size,
+                           nheads=H, headdim=P, dstate=w.B.shape[2], ngroups=w.B.shape[1],
+                           io_dtype=str(w.x.dtype).replace("torch.", ""),
+                           state_dtype=str(w.state_dtype).replace("torch.", ""),
+                           initial_states=w.initial_states is not None, gate=w.z is not None),
+               us_per_prefill=ev * 1e3, ms_per_step=wall, tokens_per_s=T / (wall * 1e-3),
+               hbm_gbps=acc["bytes"] / (ev * 1e-3) / 1e9,
+               tflops=acc["flops"] / (ev * 1e-3) / 1e12, bytes=acc["bytes"], flops=acc["flops"])
+    rec["frac_of_peak"] = rec["hbm_gbps"] / HBM_PEAK_GBPS
+    del w
+    torch.cuda.empty_cache()
+    return rec
+
+
+def ssd_cpu_baseline(seconds):
+    """The fp64 oracle, single-threaded, on the first request of the
+    Mamba2-2.7B-shaped prefill (all heads), repeated for about `seconds`."""
+    import numpy as np
+    import oracle
+    from selective_state_update_ssu_amd import workloads as wl
+
+    w = wl.ssd_mamba2_2p7b("cpu")
+    cc = w.cu_chunk_seqlens.numpy().astype(np.int64)
+    si = w.seq_idx.numpy().astype(np.int64)
+    chunks = np.nonzero(si == 0)[0]
+    hi = int(cc[chunks[-1] + 1])
+    f = lambda t: t[:hi].double().numpy()
+    args = (f(w.x), f(w.dt), w.A.double().numpy(), f(w.B), f(w.C), w.chunk_size,
+            cc[:chunks[-1] + 2], np.zeros(len(chunks), dtype=np.int64),
+            np.array([len(chunks) - 1]))
+    kw = dict(D=w.D.double().numpy(), z=f(w.z), dt_bias=w.dt_bias.double().numpy(),
+              dt_softplus=True)
+    orc = oracle.default()
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.ssd_prefill(*args, **kw)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": hi * calls / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"request 0 of ssd_mamba2_2p7b ({hi} tokens, all 80 heads), fp64, "
+                      f"{calls} calls in {el:.1f} s, one thread"}
+
+
+def summarize_ssd(prof_dir, workload, cmd):
+    """Per-kernel summary of the SSD prefill under prof_dir: kt/ (kernel trace and
+    stats) and, when present, pmc_FETCH_SIZE/, pmc_WRITE_SIZE/ with the copy
+    calibration cal_FETCH_SIZE/, cal_WRITE_SIZE/. Writes profiles/ssd_prefill_<workload>.md."""
+    import statistics
+    from selective_state_update_ssu_amd import workloads as wl
+
+    stats = [r for r in _csv_rows(os.path.join(prof_dir, "kt", "**", "*kernel_stats.csv"))
+             if "ssd" in r["Name"]]
+    if not stats:
+        raise SystemExit("no SSD kernels in the stats")
+    order = ["ssd_list_kernel", "ssd_bmm_kernel", "ssd_chunk_state_kernel",
+             "ssd_state_passing_kernel", "ssd_fixup_kernel", "ssd_scan_kernel"]
+    short = lambda n: next((k for k in order if k in n), n)
+
+    def counter(sub, name, pred):
+        vals = [float(r["Counter_Value"]) for r in
+                _csv_rows(os.path.join(prof_dir, sub, "**", "*counter_collection.csv"))
+                if r["Counter_Name"] == name and pred(r["Kernel_Name"])]
+        return statistics.median(vals) if vals else None
+
+    have_pmc = os.path.isdir(os.path.join(prof_dir, "pmc_FETCH_SIZE"))
+    if have_pmc:
+        copy = lambda n: "copy_kernel" in n
+        f_fetch = (2 << 30) / (counter("cal_FETCH_SIZE", "FETCH_SIZE", copy) * 1024)
+        f_write = (2 << 30) / (counter("cal_WRITE_SIZE", "WRITE_SIZE", copy) * 1024)
+    w = wl.SSD_NAMED[workload]("cpu")
+    acc = ssd_accounting(w)
+    lines, total = [], 0.0
+    for r in sorted(stats, key=lambda r: order.index(short(r["Name"]))
+                    if short(r["Name"]) in order else 99):
+        k = short(r["Name"])
+        us = float(r["AverageNs"]) / 1e3
+        total += us
+        traffic = ""
+        if have_pmc:
+            pred = lambda n, k=k: k in n
+            fk = counter("pmc_FETCH_SIZE", "FETCH_SIZE", pred)
+            wk = counter("pmc_WRITE_SIZE", "WRITE_SIZE", pred)
+            if fk is not None and wk is not None:
+                rb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
+                traffic = (f"{rb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                           f"{(rb + wb) / (us * 1e-6) / 1e9:.0f}")
+        lines.append(f"| `{k}` | {r['Calls']} | {us:.1f} | {traffic or '- | - | -'} |")
+    T = acc["tokens"]
+    md = f"""# SSD prefill on {workload}
+
+{T} tokens in {acc['nchunks']} chunks of at most {w.chunk_size} ({acc['batch']} requests),
+{w.x.shape[1]} heads x {w.x.shape[2]} x dstate {w.B.shape[2]}, {w.B.shape[1]} groups.
+
+Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):
+```
+{cmd.strip()}
+```
+
+| kernel | calls | average duration (us) | HBM read (MB) | HBM write (MB) | HBM GB/s |
+|---|---|---|---|---|---|
+{chr(10).join(lines)}
+
+| quantity | value |
+|---|---|
+| sum of average kernel durations per prefill | {total:.1f} us |
+| tokens/s at that time | {T / (total * 1e-6) / 1e6:.2f} M |
+| algorithmic bytes per prefill | {acc['bytes'] / 1e6:.1f} MB (read {acc['read_bytes'] / 1e6:.1f}, write {acc['write_bytes'] / 1e6:.1f}) |
+| algorithmic bandwidth | {acc['bytes'] / (total * 1e-6) / 1e9:.0f} GB/s ({acc['bytes'] / (total * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s) |
+| flops of the chunked products per prefill | {acc['flops'] / 1e9:.1f} GFLOP ({acc['flops'] / (total * 1e-6) / 1e12:.1f} TFLOP/s) |
+"""
+    out_md = os.path.join(ROOT, "profiles", f"ssd_prefill_{workload}.md")
+    with open(out_md, "w") as f:
+        f.write(md)
+    print(md)
+
+
 # ---------------------------------------------------------------------- main
 
 def describe(w):
@@ -479,7 +651,10 @@ def run_workload(name, steps, warmup, hpb, lpl=0):
 def main():
     args = parse()
     if args.mode == "summarize":
-        summarize(args.prof_dir, args.workload, args.prof_cmd)
+        if args.workload.startswith("ssd_"):
+            summarize_ssd(args.prof_dir, args.workload, args.prof_cmd)
+        else:
+            summarize(args.prof_dir, args.workload, args.prof_cmd)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -500,6 +675,12 @@ def main():
                           "bytes_each_way": 2 << 30}))
         return
 
+    if args.mode == "kernel" and args.workload.startswith("ssd_"):
+        rec = run_ssd_workload(args.workload, args.steps, args.warmup)
+        print(f"[bench] {args.workload}: {rec['us_per_prefill']:.1f} us/prefill",
+              file=sys.stderr, flush=True)
+        print(json.dumps(rec))
+        return
     head = run_workload(args.workload, args.steps, args.warmup, args.heads_per_block,
                         args.loads_per_lane)
     print(f"[bench] {args.workload}: {head['kernel_us']:.1f} us/launch, "
@@ -523,6 +704,16 @@ def main():
                                                "frac_of_state_traffic_only") if k in rec}
             print(f"[bench] {name}: {rec['kernel_us']:.1f} us/launch, {rec['hbm_gbps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
+        for name in ("ssd_mamba2_2p7b", "ssd_nemotron_h"):
+            rec = run_ssd_workload(name, max(10, args.steps // 10), max(3, args.warmup // 4))
+            extra[name] = {k: rec[k] for k in ("config", "tokens_per_s", "us_per_prefill",
+                                               "ms_per_step", "hbm_gbps", "frac_of_peak",
+                                               "tflops", "bytes", "flops")}
+            print(f"[bench] {name}: {rec['us_per_prefill']:.1f} us/prefill, "
+                  f"{rec['tokens_per_s'] / 1e6:.2f} M tokens/s, {rec['hbm_gbps']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+        if not args.no_cpu_baseline:
+            extra["ssd_cpu_baseline"] = ssd_cpu_baseline(min(5.0, args.cpu_seconds))
     ceil = ceilings()
     copy_gbps = ceil["copy"]
     rings = ring_tracker_times()

@@ -137,6 +137,18 @@ __device__ __forceinline__ float load_dt(const SsdParams& p, int64_t i) {
     return static_cast<float>(static_cast<const __bf16*>(p.dt)[i]);
 }
 
+// Streaming data (x, z, out, the chunk contributions) is read and written
+// non-temporally, so that it does not push the operands every head of a group
+// shares (B, C, C B^T of the chunk) out of L2.
+__device__ __forceinline__ u16x8 stream_load(const void* p) {
+    return __builtin_nontemporal_load(static_cast<const u16x8*>(p));
+}
+
+// Workgroups are dealt round robin to the XCDs, each with its own L2. Renumber
+// them so that each XCD walks a contiguous range of chunk-major tiles: all heads
+// of a chunk then meet the chunk's shared operands in one L2.
+__device__ __forceinline__ int64_t xcd_order(int64_t id, int64_t n) { return ssu::xcd_tile(id, n); }
+
 // Chunk c's first token and length; a range outside [0, tokens], running
 // backwards or longer than Q counts as empty.
 struct Chunk {
@@ -258,48 +270,48 @@ __device__ __forceinline__ int swz(int r, int col) {
     return (((col >> 3) ^ ((r >> 3) & 7)) << 3) | (col & 7);
 }
 
-// The chunk-state kernel: one workgroup per (chunk, head, block of PS rows,
-// block of NS dstate columns) computes the chunk's own contribution to the
-// state, L_c = sum_s exp(cum_last - cum_s) v_s x_s B_s^T (fp32, into the
-// workspace), and for the first block of each (chunk, head) the chunk's decay
-// exponent cum_last. All of the chunk's x and B loads are issued at the start;
-// tokens pass through LDS KB at a time. Wave w owns dstate column tile w of the
-// block, all row tiles.
-constexpr int kStatePS = 32, kStateNS = 64, kStateKB = 128;
+// The chunk-state kernel: one workgroup per (chunk, head, half of the headdim
+// rows) computes the chunk's own contribution to the state,
+// L_c = sum_s exp(cum_last - cum_s) v_s x_s B_s^T (fp32, into the workspace),
+// and the first half of each (chunk, head) the chunk's decay exponent cum_last.
+// It runs N / 16 waves; wave w owns dstate column tile w for the half's rows.
+// All of the chunk's x and B loads are issued at the start; tokens pass through
+// LDS KB at a time.
+constexpr int kStateKB = 128;
+constexpr int kStateRows = 32;             // headdim rows per workgroup
 constexpr int kStatePitch = kStateKB + 8;  // LDS row pitch of the transposed tiles
+__host__ __device__ constexpr int state_threads(int N) { return 4 * N; }
 
 // LDS bytes of the chunk-state kernel: sv, scum, swave, sw; x^T high and low
-// parts [PS][pitch] and B^T [NS][pitch]; the same area later holds the fp32
-// output block [PS][NS + 4].
-__host__ __device__ constexpr unsigned state_lds_bytes(int Q) {
-    return 4u * Q + 8u * Q + 8u * kWaves + 4u * Q + 2u * (2 * kStatePS + kStateNS) * kStatePitch;
+// parts [rows][pitch] and B^T [N][pitch]; the same area later holds the fp32
+// output tile [rows][N + 4].
+__host__ __device__ constexpr unsigned state_lds_bytes(int N, int Q) {
+    return 4u * Q + 8u * Q + 8u * (state_threads(N) / 64) + 4u * Q +
+           2u * (2 * kStateRows + N) * kStatePitch;
 }
 
 template <typename IT, typename ST, int P, int N, int Q>
-__global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SsdParams p) {
+__global__ __launch_bounds__(state_threads(N)) void ssd_chunk_state_kernel(const SsdParams p) {
     typedef typename Mfma<IT>::v8 v8;
-    constexpr int PS = kStatePS, NS = kStateNS, KB = kStateKB, XP = kStatePitch;
-    constexpr int PB = P / PS, NB = N / NS;
-    constexpr int PT = PS / 16;                       // row tiles per workgroup
-    static_assert(NS / 16 == kWaves, "one column tile per wave");
-    static_assert(P % PS == 0 && N % NS == 0, "blocks");
+    constexpr int NT = state_threads(N), NW = NT / 64;
+    constexpr int PS = kStateRows, NS = N, KB = kStateKB, XP = kStatePitch;
+    constexpr int PB = P / PS;                        // row halves
+    constexpr int PT = PS / 16;                       // row tiles
+    static_assert(NS / 16 == NW && P % PS == 0, "one column tile per wave");
     constexpr int XQ = PS / 8, BQ = NS / 8;           // 16-byte pieces of a token's x / B row
-    constexpr int XPASS = (KB / 2) * XQ / kThreads;   // x loads per thread (two tokens each)
-    constexpr int BPASS = (KB / 2) * BQ / kThreads;   // B loads per thread (two tokens each)
-    static_assert(XPASS >= 1 && BPASS >= 1, "passes");
-    constexpr int OP = NS + 4;                        // output block row pitch (floats)
-    static_assert(PS * OP * 4 <= 2 * (2 * PS + NS) * XP, "output block fits");
+    constexpr int XN = (KB / 2) * XQ, BN = (KB / 2) * BQ;  // two-token loads per block
+    constexpr int XPASS = (XN + NT - 1) / NT, BPASS = (BN + NT - 1) / NT;
+    constexpr int OP = NS + 4;                        // output tile row pitch (floats)
+    static_assert(PS * OP * 4 <= 2 * (2 * PS + NS) * XP, "output tile fits");
 
-    int64_t wg = blockIdx.x;
-    const int nb = static_cast<int>(wg % NB);
-    wg /= NB;
+    int64_t wg = xcd_order(blockIdx.x, gridDim.x);
     const int pb = static_cast<int>(wg % PB);
     wg /= PB;
     const int h = static_cast<int>(wg % p.nheads);
     const int64_t c = wg / p.nheads;
+    const int p0 = pb * PS;
     const int g = h / p.heads_per_group;
     const int H = p.nheads;
-    const int p0 = pb * PS, n0 = nb * NS;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
@@ -308,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SsdPara
     float* sv = reinterpret_cast<float*>(smem);
     double* scum = reinterpret_cast<double*>(sv + Q);
     double* swave = scum + Q;
-    float* sw = reinterpret_cast<float*>(swave + kWaves);
+    float* sw = reinterpret_cast<float*>(swave + NW);
     unsigned short* xhi = reinterpret_cast<unsigned short*>(sw + Q);
     unsigned short* xlo = xhi + PS * XP;
     unsigned short* bt = xlo + PS * XP;
@@ -325,32 +337,34 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SsdPara
         const int s0 = KB * b;
 #pragma unroll
         for (int r = 0; r < XPASS; ++r) {
-            const int idx = tid + kThreads * r, q = idx % XQ, s = s0 + 2 * (idx / XQ);
+            const int idx = tid + NT * r, q = idx % XQ, s = s0 + 2 * (idx / XQ);
+            const bool on = idx < XN;
             const IT* row = xp + ((ch.lo + s) * H + h) * P + p0 + 8 * q;
-            rx[b][r][0] = s < ch.len ? *reinterpret_cast<const u16x8*>(row) : u16x8{};
-            rx[b][r][1] = s + 1 < ch.len ? *reinterpret_cast<const u16x8*>(row + H * P) : u16x8{};
+            rx[b][r][0] = on && s < ch.len ? stream_load(row) : u16x8{};
+            rx[b][r][1] = on && s + 1 < ch.len ? stream_load(row + H * P) : u16x8{};
         }
 #pragma unroll
         for (int r = 0; r < BPASS; ++r) {
-            const int idx = tid + kThreads * r, q = idx % BQ, s = s0 + 2 * (idx / BQ);
-            const IT* row = Bp + ((ch.lo + s) * p.ngroups + g) * N + n0 + 8 * q;
-            rb[b][r][0] = s < ch.len ? *reinterpret_cast<const u16x8*>(row) : u16x8{};
-            rb[b][r][1] = s + 1 < ch.len ? *reinterpret_cast<const u16x8*>(row + p.ngroups * N) : u16x8{};
+            const int idx = tid + NT * r, q = idx % BQ, s = s0 + 2 * (idx / BQ);
+            const bool on = idx < BN;
+            const IT* row = Bp + ((ch.lo + s) * p.ngroups + g) * N + 8 * q;
+            rb[b][r][0] = on && s < ch.len ? *reinterpret_cast<const u16x8*>(row) : u16x8{};
+            rb[b][r][1] = on && s + 1 < ch.len ? *reinterpret_cast<const u16x8*>(row + p.ngroups * N) : u16x8{};
         }
     };
 
     const float u = load_step(p, ch, h);
 #pragma unroll
     for (int b = 0; b < NSB; ++b) fetch(b);
-    chunk_steps<Q>(p, ch, h, u, sv, scum, swave);
+    chunk_steps<Q, NT>(p, ch, h, u, sv, scum, swave);
     f32x4 acc[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (ch.len > 0) {
         const double last = scum[ch.len - 1];
         if (tid < ch.len) sw[tid] = expf(static_cast<float>(last - scum[tid])) * sv[tid];
-        if (pb == 0 && nb == 0 && tid == 0) p.cumlast[c * H + h] = static_cast<float>(last);
-    } else if (pb == 0 && nb == 0 && tid == 0) {
+        if (pb == 0 && tid == 0) p.cumlast[c * H + h] = static_cast<float>(last);
+    } else if (pb == 0 && tid == 0) {
         p.cumlast[c * H + h] = 0.f;
     }
 #pragma unroll
@@ -361,7 +375,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SsdPara
         // x^T (scaled, high and low parts) and B^T into LDS.
 #pragma unroll
         for (int r = 0; r < XPASS; ++r) {
-            const int idx = tid + kThreads * r, q = idx % XQ, j = 2 * (idx / XQ);
+            const int idx = tid + NT * r, q = idx % XQ, j = 2 * (idx / XQ);
+            if (idx >= XN) break;
             const float w0 = s0 + j < ch.len ? sw[s0 + j] : 0.f;
             const float w1 = s0 + j + 1 < ch.len ? sw[s0 + j + 1] : 0.f;
 #pragma unroll
@@ -377,7 +392,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SsdPara
         }
 #pragma unroll
         for (int r = 0; r < BPASS; ++r) {
-            const int idx = tid + kThreads * r, q = idx % BQ, j = 2 * (idx / BQ);
+            const int idx = tid + NT * r, q = idx % BQ, j = 2 * (idx / BQ);
+            if (idx >= BN) break;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int row = 8 * q + e;
@@ -401,9 +417,9 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SsdPara
         }
     }
 
-    // L_c through LDS, so that rows leave whole: thread t writes 8 consecutive
-    // columns of row t / (NS / 8). A chunk that opens a request with an initial
-    // state h0 stores exp(cum_last) h0 + L_c instead: the state after it.
+    // L_c through LDS, so that each wave store covers whole rows. A chunk that
+    // opens a request with an initial state h0 stores exp(cum_last) h0 + L_c
+    // instead: the state after it.
     lds_barrier();
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
@@ -411,25 +427,24 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SsdPara
         for (int i = 0; i < 4; ++i)
             oblk[(16 * pt + 4 * (lane / 16) + i) * OP + 16 * wave + lane % 16] = acc[pt][i];
     lds_barrier();
-    static_assert(PS * NS / 8 == kThreads, "one 8-column piece per thread");
-    const int orow = tid / (NS / 8), ocol = 8 * (tid % (NS / 8));
-    const f32x4* src = reinterpret_cast<const f32x4*>(oblk + orow * OP + ocol);
-    f32x4 v0 = src[0], v1 = src[1];
     const int64_t req = uniform64(load_index(p.seq_idx, p.meta_i64, c));
     const bool opens = c == 0 || req != load_index(p.seq_idx, p.meta_i64, c - 1);
-    if (opens && p.init && req >= 0 && req < p.batch) {
-        const float decay = ch.len > 0 ? expf(static_cast<float>(scum[ch.len - 1])) : 1.f;
-        const int64_t base = ((req * H + h) * P + p0 + orow) * static_cast<int64_t>(N) + n0 + ocol;
+    const bool fold = opens && p.init && req >= 0 && req < p.batch;
+    const float decay = ch.len > 0 ? expf(static_cast<float>(scum[ch.len - 1])) : 1.f;
+    constexpr int OPASS = PS * NS / 4 / NT;  // four-float pieces per thread
+    static_assert(OPASS * NT * 4 == PS * NS, "output passes");
+    float* const dst_tile = p.local + ((c * H + h) * P + p0) * static_cast<int64_t>(NS);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v0[j] = fmaf(decay, load_state<ST>(p.init, base + j), v0[j]);
-            v1[j] = fmaf(decay, load_state<ST>(p.init, base + 4 + j), v1[j]);
+    for (int r = 0; r < OPASS; ++r) {
+        const int idx = 4 * (tid + NT * r), orow = idx / NS, ocol = idx % NS;
+        f32x4 v = *reinterpret_cast<const f32x4*>(oblk + orow * OP + ocol);
+        if (fold) {
+            const int64_t base = ((req * H + h) * P + p0 + orow) * static_cast<int64_t>(N) + ocol;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = fmaf(decay, load_state<ST>(p.init, base + j), v[j]);
         }
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst_tile + idx));
     }
-    f32x4* dst = reinterpret_cast<f32x4*>(
-        p.local + ((c * H + h) * P + p0 + orow) * static_cast<int64_t>(N) + n0 + ocol);
-    dst[0] = v0;
-    dst[1] = v1;
 }
 
 // State passing: thread owns four consecutive elements of one head's state and
@@ -569,8 +584,9 @@ __global__ __launch_bounds__(scan_threads(Q)) void ssd_scan_kernel(const SsdPara
     static_assert((SP * 2) % 16 == 0 && (XP * 2) % 16 == 0, "16-byte rows");
     constexpr float kLog2e = 1.4426950408889634f;
 
-    const int64_t c = blockIdx.x / p.nheads;
-    const int h = blockIdx.x % p.nheads;
+    const int64_t wg = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t c = wg / p.nheads;
+    const int h = static_cast<int>(wg % p.nheads);
     const Chunk ch = chunk_of<Q>(p, c);
     if (ch.len == 0) return;
     const int g = h / p.heads_per_group;
@@ -599,8 +615,8 @@ __global__ __launch_bounds__(scan_threads(Q)) void ssd_scan_kernel(const SsdPara
     for (int r = 0; r < XPASS; ++r) {
         const int idx = tid + NT * r, q = idx % (P / 8), s = 2 * (idx / (P / 8));
         const IT* row = xp + ((ch.lo + s) * H + h) * P + 8 * q;
-        rx[r][0] = s < ch.len ? *reinterpret_cast<const u16x8*>(row) : u16x8{};
-        rx[r][1] = s + 1 < ch.len ? *reinterpret_cast<const u16x8*>(row + H * P) : u16x8{};
+        rx[r][0] = s < ch.len ? stream_load(row) : u16x8{};
+        rx[r][1] = s + 1 < ch.len ? stream_load(row + H * P) : u16x8{};
     }
     // The entering state: the previous chunk's (io type) or the request's initial state.
     const int64_t req = uniform64(load_index(p.seq_idx, p.meta_i64, c));
@@ -762,8 +778,8 @@ __global__ __launch_bounds__(scan_threads(Q)) void ssd_scan_kernel(const SsdPara
         for (int k = 0; k < TT; ++k) {
             const int t = min(16 * (wave + NW * k) + er, ch.len - 1);
             const IT* zr = zp + ((ch.lo + t) * H + h) * P + ec;
-            ez[k][0] = *reinterpret_cast<const u16x8*>(zr);
-            ez[k][1] = *reinterpret_cast<const u16x8*>(zr + 8);
+            ez[k][0] = stream_load(zr);
+            ez[k][1] = stream_load(zr + 8);
         }
     }
     // ---- skip term from the exact x^T in LDS (row t's four consecutive tokens
@@ -811,8 +827,8 @@ __global__ __launch_bounds__(scan_threads(Q)) void ssd_scan_kernel(const SsdPara
                 else
                     o1[e - 8] = bits_of<IT>(y);
             }
-            *reinterpret_cast<u16x8*>(op + xi) = o0;
-            *reinterpret_cast<u16x8*>(op + xi + 8) = o1;
+            __builtin_nontemporal_store(o0, reinterpret_cast<u16x8*>(op + xi));
+            __builtin_nontemporal_store(o1, reinterpret_cast<u16x8*>(op + xi + 8));
         }
         ssu::wave_lds_sync();  // the next tile reuses the scratch
     }
@@ -831,10 +847,9 @@ hipError_t launch_instance(const SsdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL(ssd_list_kernel<0>, dim3(1), dim3(1024), 0, stream, p);
     hipLaunchKernelGGL((ssd_bmm_kernel<IT, N, Q>), dim3(static_cast<unsigned>(p.nchunks * p.ngroups)),
                        dim3(kThreads), 0, stream, p);
-    const unsigned state_grid =
-        static_cast<unsigned>(p.nchunks * p.nheads * (P / kStatePS) * (N / kStateNS));
-    hipLaunchKernelGGL((ssd_chunk_state_kernel<IT, ST, P, N, Q>), dim3(state_grid), dim3(kThreads),
-                       state_lds_bytes(Q), stream, p);
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<IT, ST, P, N, Q>),
+                       dim3(static_cast<unsigned>(p.nchunks * p.nheads * (P / kStateRows))),
+                       dim3(state_threads(N)), state_lds_bytes(N, Q), stream, p);
     hipLaunchKernelGGL((ssd_state_passing_kernel<IT, ST, P, N>),
                        dim3(static_cast<unsigned>(p.nheads * P * N / 4 / kPassThreads)),
                        dim3(kPassThreads), 0, stream, p);
