@@ -413,7 +413,7 @@ def summarize(prof_dir, workload, cmd):
         vals = [float(r["Counter_Value"]) for r in
                 _csv_rows(os.path.join(prof_dir, sub, "**", "*counter_collection.csv"))
                 if r["Counter_Name"] == name and kernel_pred(r["Kernel_Name"])]
-        return statistics.median(vals), len(vals)
+        return (statistics.median(vals) if vals else None), len(vals)
 
     is_ssu = lambda n: "ssu_update_kernel" in n
     is_copy = lambda n: "copy_kernel" in n
@@ -453,6 +453,12 @@ Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=
 | calibrated HBM traffic per launch | {traffic / 1e6:.2f} MB (read {read_b / 1e6:.2f}, write {write_b / 1e6:.2f}) |
 | traffic / algorithmic bytes | {traffic / acc['bytes']:.4f} |
 """
+    occ = {n: counter("pmc_OCC", n, is_ssu) for n in ("OccupancyPercent", "MeanOccupancyPerActiveCU")}
+    if all(v[1] for v in occ.values()):
+        md += (f"| occupancy, % of the waves a CU can hold (median of {occ['OccupancyPercent'][1]}) "
+               f"| {occ['OccupancyPercent'][0]:.1f} % |\n"
+               f"| MeanOccupancyPerActiveCU (rocprofv3 derived counter) | "
+               f"{occ['MeanOccupancyPerActiveCU'][0]:.1f} |\n")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     out_md = os.path.join(ROOT, "profiles", f"ssu_update_kernel_{workload}.md")
     with open(out_md, "w") as f:
@@ -613,7 +619,11 @@ def summarize_ssd(prof_dir, workload, cmd):
                 rb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
                 traffic = (f"{rb / 1e6:.1f} | {wb / 1e6:.1f} | "
                            f"{(rb + wb) / (us * 1e-6) / 1e9:.0f}")
-        lines.append(f"| `{k}` | {r['Calls']} | {us:.1f} | {traffic or '- | - | -'} |")
+        util = counter("pmc_MFMA", "MfmaUtil", lambda n, k=k: k in n)
+        occ = counter("pmc_OCC", "OccupancyPercent", lambda n, k=k: k in n)
+        extra = (f" {util:.1f} |" if util is not None else " - |") + \
+                (f" {occ:.1f} |" if occ is not None else " - |")
+        lines.append(f"| `{k}` | {r['Calls']} | {us:.1f} | {traffic or '- | - | -'} |{extra}")
     T = acc["tokens"]
     md = f"""# SSD prefill on {workload}
 
@@ -625,8 +635,8 @@ Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=
 {cmd.strip()}
 ```
 
-| kernel | calls | average duration (us) | HBM read (MB) | HBM write (MB) | HBM GB/s |
-|---|---|---|---|---|---|
+| kernel | calls | average duration (us) | HBM read (MB) | HBM write (MB) | HBM GB/s | MFMA busy % | occupancy % |
+|---|---|---|---|---|---|---|---|
 {chr(10).join(lines)}
 
 | quantity | value |

@@ -111,6 +111,12 @@ struct Mfma<_Float16> {
     }
 };
 
+// Storage of the per-chunk C B^T entries: bf16 when the io type is bf16 (the
+// scan rounds them to bf16 for the matrix cores anyway, after the decay), fp32
+// for fp16 io, whose finer rounding a bf16 copy would spoil.
+template <typename IT> struct CbStore { typedef float type; };
+template <> struct CbStore<__bf16> { typedef __bf16 type; };
+
 // 16-bit io value <-> bits <-> fp32.
 template <typename T>
 __device__ __forceinline__ float f32_of(unsigned short b) {
@@ -237,7 +243,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bmm_kernel(const SsdParams p) {
     const int lane = threadIdx.x % 64;
     const IT* Cp = static_cast<const IT*>(p.C);
     const IT* Bp = static_cast<const IT*>(p.B);
-    float* out = p.cb + (c * p.ngroups + g) * Q * Q;
+    typedef typename CbStore<IT>::type CBT;
+    CBT* out = reinterpret_cast<CBT*>(p.cb) + (c * p.ngroups + g) * Q * Q;
     int tile = 0;
     for (int ti = 0; ti < TQ; ++ti) {
         for (int sj = 0; sj <= ti; ++sj, ++tile) {
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bmm_kernel(const SsdParams p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int row = ti * 32 + 8 * (i / 4) + 4 * (lane / 32) + i % 4;
-                out[row * Q + sj * 32 + lane % 32] = acc[i];
+                out[row * Q + sj * 32 + lane % 32] = static_cast<CBT>(acc[i]);
             }
         }
     }
@@ -719,51 +726,73 @@ __global__ __launch_bounds__(scan_threads(Q)) void ssd_scan_kernel(const SsdPara
     }
 
     // ---- inside the chunk: (C B^T masked, times the decays and the steps v_s)
-    // times x. Tile k needs the s blocks kk <= its last row; the next block's
-    // C B^T entries are requested before the current block's products.
-    const float* cbp = p.cb + (c * p.ngroups + g) * Q * Q;
-    f32x4 cb[TT][2];
-    // Tile k's C B^T entries of s block kk, if the tile needs that block.
-    auto cb_load = [&](int k, int kk) {
+    // times x. Tile k needs the s blocks kk <= its last row; its C B^T entries
+    // are requested two blocks ahead of their products.
+    typedef typename CbStore<IT>::type CBT;
+    const CBT* cbp = reinterpret_cast<const CBT*>(p.cb) + (c * p.ngroups + g) * Q * Q;
+    // Eight C B^T entries of one row: one 16-byte load for bf16, two for fp32.
+    constexpr int CW = sizeof(CBT) == 2 ? 1 : 2;
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    constexpr int DEPTH = 2;  // s blocks of C B^T in flight per tile
+    u32x4v cb[TT][DEPTH][CW];
+    // Tile k's C B^T entries of s block kk into slot d, if the tile needs that block.
+    auto cb_load = [&](int k, int kk, int d) {
         const int t0 = 16 * (wave + NW * k);
         if (live[k] && t0 + 15 >= kk && kk < ch.len) {
-            const f32x4* r = reinterpret_cast<const f32x4*>(cbp + (t0 + lane % 16) * Q + kk + kcol);
-            cb[k][0] = r[0];
-            cb[k][1] = r[1];
+            const u32x4v* r =
+                reinterpret_cast<const u32x4v*>(cbp + (t0 + lane % 16) * Q + kk + kcol);
+#pragma unroll
+            for (int w = 0; w < CW; ++w) cb[k][d][w] = r[w];
+        }
+    };
+    auto cb_value = [&](int k, int d, int j) -> float {
+        if constexpr (CW == 1) {
+            const unsigned word = cb[k][d][0][j / 2];
+            return __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
+        } else {
+            return __uint_as_float(cb[k][d][j / 4][j % 4]);
         }
     };
 #pragma unroll
-    for (int k = 0; k < TT; ++k) cb_load(k, 0);
-    for (int kk = 0; kk < ch.len; kk += 32) {
-        const int col = kk + kcol;
-        v8 xf[PT];
+    for (int k = 0; k < TT; ++k)
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const int pr = 16 * pt + lane % 16;
-            xf[pt] = *reinterpret_cast<const v8*>(xv + pr * XP + swz(pr, col));
-        }
-        float cs[8], vs[8];
+        for (int d = 0; d < DEPTH; ++d) cb_load(k, 32 * d, d);
+    // The loop runs DEPTH s blocks per iteration so that slot indices stay static.
+    for (int kb = 0; kb < ch.len; kb += 32 * DEPTH) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            cs[j] = cum2[col + j];
-            vs[j] = sv[col + j];
-        }
+        for (int d = 0; d < DEPTH; ++d) {
+            const int kk = kb + 32 * d;
+            if (kk >= ch.len) break;
+            const int col = kk + kcol;
+            v8 xf[PT];
 #pragma unroll
-        for (int k = 0; k < TT; ++k) {
-            const int t0 = 16 * (wave + NW * k);
-            if (!live[k] || t0 + 15 < kk) continue;
-            const int t = t0 + lane % 16;
-            const float ct = cum2[t];
-            v8 a;
+            for (int pt = 0; pt < PT; ++pt) {
+                const int pr = 16 * pt + lane % 16;
+                xf[pt] = *reinterpret_cast<const v8*>(xv + pr * XP + swz(pr, col));
+            }
+            float cs[8], vs[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float m = cb[k][j / 4][j % 4];
-                const bool on = col + j <= t && t < ch.len;
-                a[j] = static_cast<IT>(on ? m * vs[j] * __builtin_amdgcn_exp2f(ct - cs[j]) : 0.f);
+                cs[j] = cum2[col + j];
+                vs[j] = sv[col + j];
             }
-            cb_load(k, kk + 32);  // the tile's next block, in flight during the products
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(a, xf[pt], acc[k][pt]);
+            for (int k = 0; k < TT; ++k) {
+                const int t0 = 16 * (wave + NW * k);
+                if (!live[k] || t0 + 15 < kk) continue;
+                const int t = t0 + lane % 16;
+                const float ct = cum2[t];
+                v8 a;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float m = cb_value(k, d, j);
+                    const bool on = col + j <= t && t < ch.len;
+                    a[j] = static_cast<IT>(on ? m * vs[j] * __builtin_amdgcn_exp2f(ct - cs[j]) : 0.f);
+                }
+                cb_load(k, kk + 32 * DEPTH, d);  // in flight during the next blocks
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(a, xf[pt], acc[k][pt]);
+            }
         }
     }
 
