@@ -194,6 +194,7 @@ extern "C" int ssu_ssd_prefill(const ssu_ssd_args* args, void* stream) {
     p.nheads = static_cast<int32_t>(a.nheads);
     p.ngroups = static_cast<int32_t>(a.ngroups);
     p.heads_per_group = static_cast<int32_t>(a.nheads / a.ngroups);
+    p.state_heads = p.heads_per_group % 4 == 0 ? 4 : p.heads_per_group % 2 == 0 ? 2 : 1;
     p.dt_dtype = a.dt_dtype;
     p.meta_i64 = a.meta_dtype == SSU_I64;
     p.D_per_dim = a.D_per_dim != 0;

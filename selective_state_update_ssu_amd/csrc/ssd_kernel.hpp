@@ -83,6 +83,7 @@ struct SsdParams {
     int32_t meta_i64;
     int32_t D_per_dim, dt_softplus;
     int32_t return_all;   // states[c] for every chunk instead of states[b] per request
+    int32_t state_heads;  // heads per chunk-state workgroup: divides heads_per_group, <= 4
 };
 
 // ------------------------------------------------------------------ types
@@ -277,23 +278,25 @@ __device__ __forceinline__ int swz(int r, int col) {
     return (((col >> 3) ^ ((r >> 3) & 7)) << 3) | (col & 7);
 }
 
-// The chunk-state kernel: one workgroup per (chunk, head, half of the headdim
-// rows) computes the chunk's own contribution to the state,
-// L_c = sum_s exp(cum_last - cum_s) v_s x_s B_s^T (fp32, into the workspace),
-// and the first half of each (chunk, head) the chunk's decay exponent cum_last.
-// It runs N / 16 waves; wave w owns dstate column tile w for the half's rows.
-// All of the chunk's x and B loads are issued at the start; tokens pass through
-// LDS KB at a time.
+// The chunk-state kernel: one workgroup per (chunk, block of `state_heads`
+// heads of one group, half of the headdim rows) computes each head's own
+// contribution to the state, L_c = sum_s exp(cum_last - cum_s) v_s x_s B_s^T
+// (fp32, into the workspace), and (first half) the chunk's decay exponent per
+// head. The heads share the chunk's B, staged once per block of KB tokens, and
+// run as a pipeline: the steps of every head are requested together, and the
+// next head's x is in flight while the current head's products run. It runs
+// N / 16 waves; wave w owns dstate column tile w for the half's rows.
 constexpr int kStateKB = 128;
 constexpr int kStateRows = 32;             // headdim rows per workgroup
+constexpr int kStateHeads = 4;             // most heads per workgroup
 constexpr int kStatePitch = kStateKB + 8;  // LDS row pitch of the transposed tiles
 __host__ __device__ constexpr int state_threads(int N) { return 4 * N; }
 
-// LDS bytes of the chunk-state kernel: sv, scum, swave, sw; x^T high and low
-// parts [rows][pitch] and B^T [N][pitch]; the same area later holds the fp32
-// output tile [rows][N + 4].
+// LDS bytes of the chunk-state kernel: sv, scum, swave (the step scan of one
+// head), the weights of every head, x^T high and low parts [rows][pitch] of one
+// head and B^T [N][pitch]; the x^T area later holds one head's fp32 output tile.
 __host__ __device__ constexpr unsigned state_lds_bytes(int N, int Q) {
-    return 4u * Q + 8u * Q + 8u * (state_threads(N) / 64) + 4u * Q +
+    return 4u * Q + 8u * Q + 8u * (state_threads(N) / 64) + 4u * kStateHeads * Q +
            2u * (2 * kStateRows + N) * kStatePitch;
 }
 
@@ -301,24 +304,28 @@ template <typename IT, typename ST, int P, int N, int Q>
 __global__ __launch_bounds__(state_threads(N)) void ssd_chunk_state_kernel(const SsdParams p) {
     typedef typename Mfma<IT>::v8 v8;
     constexpr int NT = state_threads(N), NW = NT / 64;
-    constexpr int PS = kStateRows, NS = N, KB = kStateKB, XP = kStatePitch;
+    constexpr int PS = kStateRows, NS = N, KB = kStateKB, XP = kStatePitch, HM = kStateHeads;
     constexpr int PB = P / PS;                        // row halves
     constexpr int PT = PS / 16;                       // row tiles
     static_assert(NS / 16 == NW && P % PS == 0, "one column tile per wave");
     constexpr int XQ = PS / 8, BQ = NS / 8;           // 16-byte pieces of a token's x / B row
     constexpr int XN = (KB / 2) * XQ, BN = (KB / 2) * BQ;  // two-token loads per block
     constexpr int XPASS = (XN + NT - 1) / NT, BPASS = (BN + NT - 1) / NT;
+    constexpr int NSB = Q / KB > 0 ? Q / KB : 1;      // token blocks per chunk
     constexpr int OP = NS + 4;                        // output tile row pitch (floats)
-    static_assert(PS * OP * 4 <= 2 * (2 * PS + NS) * XP, "output tile fits");
+    static_assert(PS * OP * 4 <= 2 * 2 * PS * XP, "output tile fits the x^T area");
+    static_assert(Q <= NT, "one step per thread");
 
+    const int HB = p.state_heads;
     int64_t wg = xcd_order(blockIdx.x, gridDim.x);
     const int pb = static_cast<int>(wg % PB);
     wg /= PB;
-    const int h = static_cast<int>(wg % p.nheads);
-    const int64_t c = wg / p.nheads;
-    const int p0 = pb * PS;
-    const int g = h / p.heads_per_group;
+    const int hblocks = p.nheads / HB;
+    const int h0 = static_cast<int>(wg % hblocks) * HB;
+    const int64_t c = wg / hblocks;
+    const int g = h0 / p.heads_per_group;
     const int H = p.nheads;
+    const int p0 = pb * PS;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
@@ -327,8 +334,8 @@ __global__ __launch_bounds__(state_threads(N)) void ssd_chunk_state_kernel(const
     float* sv = reinterpret_cast<float*>(smem);
     double* scum = reinterpret_cast<double*>(sv + Q);
     double* swave = scum + Q;
-    float* sw = reinterpret_cast<float*>(swave + NW);
-    unsigned short* xhi = reinterpret_cast<unsigned short*>(sw + Q);
+    float* sw = reinterpret_cast<float*>(swave + NW);   // [HM][Q]
+    unsigned short* xhi = reinterpret_cast<unsigned short*>(sw + HM * Q);
     unsigned short* xlo = xhi + PS * XP;
     unsigned short* bt = xlo + PS * XP;
     float* oblk = reinterpret_cast<float*>(xhi);
@@ -336,67 +343,63 @@ __global__ __launch_bounds__(state_threads(N)) void ssd_chunk_state_kernel(const
     const IT* xp = static_cast<const IT*>(p.x);
     const IT* Bp = static_cast<const IT*>(p.B);
     const Chunk ch = chunk_of<Q>(p, c);
-    // Every block of the chunk is requested at the start: registers of block b
-    // hold KB tokens from token KB b on.
-    constexpr int NSB = Q / KB > 0 ? Q / KB : 1;
-    u16x8 rx[NSB][XPASS][2], rb[NSB][BPASS][2];
-    auto fetch = [&](int b) {
-        const int s0 = KB * b;
+
+    // Staged registers: x of one (head, block), B of one block.
+    u16x8 rx[XPASS][2], rb[BPASS][2];
+    auto fetch_x = [&](int hh, int sb) {
+        const int s0 = KB * sb, h = h0 + hh;
 #pragma unroll
         for (int r = 0; r < XPASS; ++r) {
             const int idx = tid + NT * r, q = idx % XQ, s = s0 + 2 * (idx / XQ);
             const bool on = idx < XN;
             const IT* row = xp + ((ch.lo + s) * H + h) * P + p0 + 8 * q;
-            rx[b][r][0] = on && s < ch.len ? stream_load(row) : u16x8{};
-            rx[b][r][1] = on && s + 1 < ch.len ? stream_load(row + H * P) : u16x8{};
+            rx[r][0] = on && s < ch.len ? stream_load(row) : u16x8{};
+            rx[r][1] = on && s + 1 < ch.len ? stream_load(row + H * P) : u16x8{};
         }
+    };
+    auto fetch_b = [&](int sb) {
+        const int s0 = KB * sb;
 #pragma unroll
         for (int r = 0; r < BPASS; ++r) {
             const int idx = tid + NT * r, q = idx % BQ, s = s0 + 2 * (idx / BQ);
             const bool on = idx < BN;
             const IT* row = Bp + ((ch.lo + s) * p.ngroups + g) * N + 8 * q;
-            rb[b][r][0] = on && s < ch.len ? *reinterpret_cast<const u16x8*>(row) : u16x8{};
-            rb[b][r][1] = on && s + 1 < ch.len ? *reinterpret_cast<const u16x8*>(row + p.ngroups * N) : u16x8{};
+            rb[r][0] = on && s < ch.len ? *reinterpret_cast<const u16x8*>(row) : u16x8{};
+            rb[r][1] = on && s + 1 < ch.len ? *reinterpret_cast<const u16x8*>(row + p.ngroups * N) : u16x8{};
         }
     };
 
-    const float u = load_step(p, ch, h);
+    // The steps of every head first, then the first blocks of B and x.
+    float u[HM];
 #pragma unroll
-    for (int b = 0; b < NSB; ++b) fetch(b);
-    chunk_steps<Q, NT>(p, ch, h, u, sv, scum, swave);
-    f32x4 acc[PT];
+    for (int hh = 0; hh < HM; ++hh) u[hh] = hh < HB ? load_step(p, ch, h0 + hh) : 0.f;
+    fetch_b(0);
+    fetch_x(0, 0);
+
+    float decay[HM];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (ch.len > 0) {
-        const double last = scum[ch.len - 1];
-        if (tid < ch.len) sw[tid] = expf(static_cast<float>(last - scum[tid])) * sv[tid];
-        if (pb == 0 && tid == 0) p.cumlast[c * H + h] = static_cast<float>(last);
-    } else if (pb == 0 && tid == 0) {
-        p.cumlast[c * H + h] = 0.f;
+    for (int hh = 0; hh < HM; ++hh) {
+        if (hh >= HB) break;
+        lds_barrier();  // the previous head's scan is consumed
+        chunk_steps<Q, NT>(p, ch, h0 + hh, u[hh], sv, scum, swave);
+        const double last = ch.len > 0 ? scum[ch.len - 1] : 0.0;
+        if (tid < Q)
+            sw[hh * Q + tid] = tid < ch.len ? expf(static_cast<float>(last - scum[tid])) * sv[tid] : 0.f;
+        if (pb == 0 && tid == 0) p.cumlast[c * H + h0 + hh] = static_cast<float>(last);
+        decay[hh] = expf(static_cast<float>(last));
     }
+
+    f32x4 acc[HM][PT];
+#pragma unroll
+    for (int hh = 0; hh < HM; ++hh)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[hh][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
         const int s0 = KB * sb;
         if (s0 >= ch.len) break;
-        lds_barrier();  // sw visible; the previous block's tiles consumed
-        // x^T (scaled, high and low parts) and B^T into LDS.
-#pragma unroll
-        for (int r = 0; r < XPASS; ++r) {
-            const int idx = tid + NT * r, q = idx % XQ, j = 2 * (idx / XQ);
-            if (idx >= XN) break;
-            const float w0 = s0 + j < ch.len ? sw[s0 + j] : 0.f;
-            const float w1 = s0 + j + 1 < ch.len ? sw[s0 + j + 1] : 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float a0 = f32_of<IT>(rx[sb][r][0][e]) * w0, a1 = f32_of<IT>(rx[sb][r][1][e]) * w1;
-                const unsigned short h0 = bits_of<IT>(a0), h1 = bits_of<IT>(a1);
-                const unsigned short l0 = bits_of<IT>(a0 - f32_of<IT>(h0));
-                const unsigned short l1 = bits_of<IT>(a1 - f32_of<IT>(h1));
-                const int row = 8 * q + e, o = row * XP + swz(row, j);
-                *reinterpret_cast<unsigned*>(xhi + o) = h0 | (static_cast<unsigned>(h1) << 16);
-                *reinterpret_cast<unsigned*>(xlo + o) = l0 | (static_cast<unsigned>(l1) << 16);
-            }
-        }
+        lds_barrier();  // the previous block's B^T is consumed; sw visible
 #pragma unroll
         for (int r = 0; r < BPASS; ++r) {
             const int idx = tid + NT * r, q = idx % BQ, j = 2 * (idx / BQ);
@@ -405,52 +408,87 @@ __global__ __launch_bounds__(state_threads(N)) void ssd_chunk_state_kernel(const
             for (int e = 0; e < 8; ++e) {
                 const int row = 8 * q + e;
                 *reinterpret_cast<unsigned*>(bt + row * XP + swz(row, j)) =
-                    rb[sb][r][0][e] | (static_cast<unsigned>(rb[sb][r][1][e]) << 16);
+                    rb[r][0][e] | (static_cast<unsigned>(rb[r][1][e]) << 16);
             }
         }
-        lds_barrier();
+        if (sb + 1 < NSB && s0 + KB < ch.len) fetch_b(sb + 1);
 #pragma unroll
-        for (int kk = 0; kk < KB; kk += 32) {
-            if (s0 + kk >= ch.len) break;
-            const int col = kk + 8 * (lane / 16);
-            const int brow = 16 * wave + lane % 16;
-            const v8 bf = *reinterpret_cast<const v8*>(bt + brow * XP + swz(brow, col));
+        for (int hh = 0; hh < HM; ++hh) {
+            if (hh >= HB) break;
+            if (hh > 0) lds_barrier();  // the previous head's products are done with x^T
+            // x^T of head hh (scaled by its weights, high and low parts) into LDS.
+            const float* swh = sw + hh * Q + s0;
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const int row = 16 * pt + lane % 16, o = row * XP + swz(row, col);
-                acc[pt] = Mfma<IT>::mma16(*reinterpret_cast<const v8*>(xhi + o), bf, acc[pt]);
-                acc[pt] = Mfma<IT>::mma16(*reinterpret_cast<const v8*>(xlo + o), bf, acc[pt]);
+            for (int r = 0; r < XPASS; ++r) {
+                const int idx = tid + NT * r, q = idx % XQ, j = 2 * (idx / XQ);
+                if (idx >= XN) break;
+                const float w0 = s0 + j < ch.len ? swh[j] : 0.f;
+                const float w1 = s0 + j + 1 < ch.len ? swh[j + 1] : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float a0 = f32_of<IT>(rx[r][0][e]) * w0;
+                    const float a1 = f32_of<IT>(rx[r][1][e]) * w1;
+                    const unsigned short hi0 = bits_of<IT>(a0), hi1 = bits_of<IT>(a1);
+                    const unsigned short lo0 = bits_of<IT>(a0 - f32_of<IT>(hi0));
+                    const unsigned short lo1 = bits_of<IT>(a1 - f32_of<IT>(hi1));
+                    const int row = 8 * q + e, o = row * XP + swz(row, j);
+                    *reinterpret_cast<unsigned*>(xhi + o) = hi0 | (static_cast<unsigned>(hi1) << 16);
+                    *reinterpret_cast<unsigned*>(xlo + o) = lo0 | (static_cast<unsigned>(lo1) << 16);
+                }
+            }
+            // The next head's x (or the next block's first head) is requested now.
+            if (hh + 1 < HB)
+                fetch_x(hh + 1, sb);
+            else if (sb + 1 < NSB && s0 + KB < ch.len)
+                fetch_x(0, sb + 1);
+            lds_barrier();
+#pragma unroll
+            for (int kk = 0; kk < KB; kk += 32) {
+                if (s0 + kk >= ch.len) break;
+                const int col = kk + 8 * (lane / 16);
+                const int brow = 16 * wave + lane % 16;
+                const v8 bf = *reinterpret_cast<const v8*>(bt + brow * XP + swz(brow, col));
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const int row = 16 * pt + lane % 16, o = row * XP + swz(row, col);
+                    acc[hh][pt] = Mfma<IT>::mma16(*reinterpret_cast<const v8*>(xhi + o), bf, acc[hh][pt]);
+                    acc[hh][pt] = Mfma<IT>::mma16(*reinterpret_cast<const v8*>(xlo + o), bf, acc[hh][pt]);
+                }
             }
         }
     }
 
-    // L_c through LDS, so that each wave store covers whole rows. A chunk that
-    // opens a request with an initial state h0 stores exp(cum_last) h0 + L_c
-    // instead: the state after it.
-    lds_barrier();
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            oblk[(16 * pt + 4 * (lane / 16) + i) * OP + 16 * wave + lane % 16] = acc[pt][i];
-    lds_barrier();
+    // Each head's L_c through LDS, so that each wave store covers whole rows. A
+    // chunk that opens a request with an initial state h0 stores
+    // exp(cum_last) h0 + L_c instead: the state after it.
     const int64_t req = uniform64(load_index(p.seq_idx, p.meta_i64, c));
     const bool opens = c == 0 || req != load_index(p.seq_idx, p.meta_i64, c - 1);
     const bool fold = opens && p.init && req >= 0 && req < p.batch;
-    const float decay = ch.len > 0 ? expf(static_cast<float>(scum[ch.len - 1])) : 1.f;
     constexpr int OPASS = PS * NS / 4 / NT;  // four-float pieces per thread
     static_assert(OPASS * NT * 4 == PS * NS, "output passes");
-    float* const dst_tile = p.local + ((c * H + h) * P + p0) * static_cast<int64_t>(NS);
 #pragma unroll
-    for (int r = 0; r < OPASS; ++r) {
-        const int idx = 4 * (tid + NT * r), orow = idx / NS, ocol = idx % NS;
-        f32x4 v = *reinterpret_cast<const f32x4*>(oblk + orow * OP + ocol);
-        if (fold) {
-            const int64_t base = ((req * H + h) * P + p0 + orow) * static_cast<int64_t>(N) + ocol;
+    for (int hh = 0; hh < HM; ++hh) {
+        if (hh >= HB) break;
+        const int h = h0 + hh;
+        lds_barrier();  // x^T (or the previous head's tile) is consumed
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = fmaf(decay, load_state<ST>(p.init, base + j), v[j]);
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                oblk[(16 * pt + 4 * (lane / 16) + i) * OP + 16 * wave + lane % 16] = acc[hh][pt][i];
+        lds_barrier();
+        float* const dst_tile = p.local + ((c * H + h) * P + p0) * static_cast<int64_t>(NS);
+#pragma unroll
+        for (int r = 0; r < OPASS; ++r) {
+            const int idx = 4 * (tid + NT * r), orow = idx / NS, ocol = idx % NS;
+            f32x4 v = *reinterpret_cast<const f32x4*>(oblk + orow * OP + ocol);
+            if (fold) {
+                const int64_t base = ((req * H + h) * P + p0 + orow) * static_cast<int64_t>(N) + ocol;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = fmaf(decay[hh], load_state<ST>(p.init, base + j), v[j]);
+            }
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst_tile + idx));
         }
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst_tile + idx));
     }
 }
 
@@ -877,7 +915,8 @@ hipError_t launch_instance(const SsdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((ssd_bmm_kernel<IT, N, Q>), dim3(static_cast<unsigned>(p.nchunks * p.ngroups)),
                        dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL((ssd_chunk_state_kernel<IT, ST, P, N, Q>),
-                       dim3(static_cast<unsigned>(p.nchunks * p.nheads * (P / kStateRows))),
+                       dim3(static_cast<unsigned>(p.nchunks * (p.nheads / p.state_heads) *
+                                                  (P / kStateRows))),
                        dim3(state_threads(N)), state_lds_bytes(N, Q), stream, p);
     hipLaunchKernelGGL((ssd_state_passing_kernel<IT, ST, P, N>),
                        dim3(static_cast<unsigned>(p.nheads * P * N / 4 / kPassThreads)),
