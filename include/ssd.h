@@ -30,9 +30,10 @@
  *     s  = s * exp(A[h] v) + v * B[t, g] x[t, h, p]        (g = h / (nheads/ngroups))
  *     y  = C[t, g] . s + D x[t, h, p];  y *= z sigmoid(z) if z is given
  *     out[t, h, p] = y
- * The GPU computes it by chunks (intra-chunk products, chunk states, state
- * passing) on the matrix cores with 16-bit operands and fp32 accumulation;
- * results agree with the recurrence within the rounding of those operands.
+ * The GPU computes it by chunks (intra-chunk products, and the state carried
+ * from chunk to chunk along each request) on the matrix cores with 16-bit
+ * operands and fp32 accumulation; results agree with the recurrence within the
+ * rounding of those operands.
  */
 #ifndef SSD_H
 #define SSD_H
@@ -87,9 +88,12 @@ typedef struct ssu_ssd_args {
     size_t workspace_bytes;
 } ssu_ssd_args;
 
-/* Bytes of workspace ssu_ssd_prefill needs for these sizes: chunk-end states in
- * the io type, the per-chunk C B^T products (fp32), each chunk's own state
- * contribution (fp32) and decay, and the per-request list of last chunks. */
+/* Bytes of workspace ssu_ssd_prefill needs for these sizes: each chunk's
+ * entering state in the io type, the per-chunk C B^T products, each chunk's
+ * steps, running sums, weights and decay per head, the chunk descriptors, the
+ * per-request list of last chunks and the runs of chunks that continue one
+ * another. Linear in nchunks; no term grows with the number of tokens beyond
+ * nchunks * chunk_size. */
 size_t ssu_ssd_workspace_bytes(int64_t nchunks, int64_t batch, int64_t nheads,
                                int64_t headdim, int64_t dstate, int64_t ngroups,
                                int64_t chunk_size);

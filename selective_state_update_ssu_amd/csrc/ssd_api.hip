@@ -17,7 +17,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t s16, cb, local, cumlast, dummy, head, next, total;
+    size_t s16, cb, cumlast, head, next, desc, w, cv, runs, wfirst, wlen, winfo, total;
 };
 
 Layout layout(int64_t nchunks, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
@@ -25,12 +25,17 @@ Layout layout(int64_t nchunks, int64_t batch, int64_t nheads, int64_t headdim, i
     Layout l;
     l.s16 = 0;
     l.cb = l.s16 + round_up(static_cast<size_t>(nchunks * nheads * headdim * dstate) * 2);
-    l.local = l.cb + round_up(static_cast<size_t>(nchunks * ngroups * chunk_size * chunk_size) * 4);
-    l.cumlast = l.local + round_up(static_cast<size_t>(nchunks * nheads * headdim * dstate) * 4);
-    l.dummy = l.cumlast + round_up(static_cast<size_t>(nchunks * nheads) * 4);
-    l.head = l.dummy + round_up(static_cast<size_t>(nheads * headdim * dstate) * 4);
+    l.cumlast = l.cb + round_up(static_cast<size_t>(nchunks * ngroups * chunk_size * chunk_size) * 4);
+    l.head = l.cumlast + round_up(static_cast<size_t>(nchunks * nheads) * 4);
     l.next = l.head + round_up(static_cast<size_t>(nchunks) * 4);
-    l.total = l.next + round_up(static_cast<size_t>(batch) * 4);
+    l.desc = l.next + round_up(static_cast<size_t>(batch) * 4);
+    l.w = l.desc + round_up(static_cast<size_t>(nchunks) * sizeof(ssd::ChunkDesc));
+    l.cv = l.w + round_up(static_cast<size_t>(nchunks * nheads * chunk_size) * 4);
+    l.runs = l.cv + round_up(static_cast<size_t>(nchunks * nheads * chunk_size) * 8);
+    l.wfirst = l.runs + round_up(static_cast<size_t>(nchunks) * 4);
+    l.wlen = l.wfirst + round_up(static_cast<size_t>(nchunks) * 4);
+    l.winfo = l.wlen + round_up(static_cast<size_t>(nchunks) * 4);
+    l.total = l.winfo + round_up(4);
     return l;
 }
 
@@ -91,8 +96,12 @@ int check(const ssu_ssd_args& a) {
                       "no kernel for headdim %lld, dstate %lld, chunk_size %lld (built: headdim "
                       "64, dstate 64 or 128, chunk_size 128 or 256)",
                       (long long)a.headdim, (long long)a.dstate, (long long)a.chunk_size);
-    if (a.nchunks * a.nheads > INT32_MAX || a.nchunks * a.ngroups > INT32_MAX)
+    if (a.nchunks * a.nheads > INT32_MAX || a.nchunks * a.ngroups * 16 > INT32_MAX)
         return report(SSU_ERR_UNSUPPORTED, "too many chunks for one launch");
+    // The kernels address a chunk's rows with 32-bit byte offsets.
+    if (a.chunk_size * a.nheads * a.headdim * 2 >= (int64_t(1) << 30) ||
+        a.chunk_size * a.ngroups * a.dstate * 2 >= (int64_t(1) << 30))
+        return report(SSU_ERR_UNSUPPORTED, "a chunk's rows must span less than 1 GiB");
     for (const Span& s : {Span{"x", a.x, 0}, Span{"B", a.B, 0}, Span{"C", a.C, 0},
                           Span{"z", a.z, 0}, Span{"out", a.out, 0}})
         if (s.p && !aligned(s.p, 16))
@@ -181,11 +190,16 @@ extern "C" int ssu_ssd_prefill(const ssu_ssd_args* args, void* stream) {
     p.states = a.states;
     p.s16 = ws + l.s16;
     p.cb = reinterpret_cast<float*>(ws + l.cb);
-    p.local = reinterpret_cast<float*>(ws + l.local);
     p.cumlast = reinterpret_cast<float*>(ws + l.cumlast);
-    p.dummy = ws + l.dummy;
     p.list_head = reinterpret_cast<int*>(ws + l.head);
     p.list_next = reinterpret_cast<int*>(ws + l.next);
+    p.desc = reinterpret_cast<ssd::ChunkDesc*>(ws + l.desc);
+    p.w = reinterpret_cast<float*>(ws + l.w);
+    p.cv = reinterpret_cast<float*>(ws + l.cv);
+    p.run_first = reinterpret_cast<int*>(ws + l.runs);
+    p.walk_first = reinterpret_cast<int*>(ws + l.wfirst);
+    p.walk_len = reinterpret_cast<int*>(ws + l.wlen);
+    p.walk_info = reinterpret_cast<int*>(ws + l.winfo);
     p.tokens = a.tokens;
     p.nchunks = a.nchunks;
     p.batch = a.batch;
@@ -194,7 +208,6 @@ extern "C" int ssu_ssd_prefill(const ssu_ssd_args* args, void* stream) {
     p.nheads = static_cast<int32_t>(a.nheads);
     p.ngroups = static_cast<int32_t>(a.ngroups);
     p.heads_per_group = static_cast<int32_t>(a.nheads / a.ngroups);
-    p.state_heads = p.heads_per_group % 4 == 0 ? 4 : p.heads_per_group % 2 == 0 ? 2 : 1;
     p.dt_dtype = a.dt_dtype;
     p.meta_i64 = a.meta_dtype == SSU_I64;
     p.D_per_dim = a.D_per_dim != 0;
