@@ -47,7 +47,6 @@ namespace ssd {
 
 using ssu::lds_barrier;
 using ssu::load_index;
-using ssu::softplus_f32;
 using ssu::uniform64;
 
 constexpr int kThreads = 256;  // four wave64s per workgroup
@@ -90,7 +89,8 @@ struct SsdParams {
     float* cumlast;       // workspace [nchunks, H]: each chunk's decay exponent
     ChunkDesc* desc;      // workspace [nchunks]
     float* w;             // workspace [nchunks, H, Q]: chunk-state weights exp(cum_last - cum_s) v_s
-    float* cv;            // workspace [nchunks, H, 2, Q]: v_s, then cum_s log2(e), for the scan
+    float* cv;            // workspace [nchunks, H, 2, Q]: cum_s log2(e) - log2(v_s), then
+                          // cum_s log2(e), for the scan
     int* list_head;       // workspace [nchunks]: first request whose last chunk is c
     int* list_next;       // workspace [batch]
     int* run_first;       // workspace [nchunks]: first chunk of each run, in chunk order
@@ -186,6 +186,17 @@ __device__ __forceinline__ float bload_f32(Rsrc r, uint32_t off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+// softplus(v) = max(v, 0) + log1p(exp(-|v|)) with the hardware exp2, log2 and
+// reciprocal; log1p(e) as log(u) e / (u - 1), u = 1 + e rounded, which cancels
+// the rounding of u (a few ulp of fp32 in all).
+__device__ __forceinline__ float softplus_fast(float v) {
+    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * fabsf(v));
+    const float u = 1.f + e;
+    const float l = u == 1.f ? e : 0.6931471805599453f * __builtin_amdgcn_logf(u) * e *
+                                       __builtin_amdgcn_rcpf(u - 1.f);
+    return fmaxf(v, 0.f) + l;
+}
+
 // The gate z sigmoid(z) with the hardware exp2 and reciprocal (about 2 ulp of
 // fp32, far below the 16-bit rounding of the result).
 __device__ __forceinline__ float gate_f32(float z) {
@@ -220,10 +231,17 @@ struct Chunk {
     int len;
 };
 
+// Entry i of a chunk-metadata array (the caller's, read only), one value for
+// the whole wave.
+__device__ __forceinline__ int64_t meta_uniform(const void* ptr, int is64, int64_t i) {
+    return is64 ? ld_uniform(static_cast<const int64_t*>(ptr) + i)
+                : static_cast<int64_t>(ld_uniform(static_cast<const int32_t*>(ptr) + i));
+}
+
 template <int Q>
 __device__ __forceinline__ Chunk chunk_of(const SsdParams& p, int64_t c) {
-    const int64_t lo = uniform64(load_index(p.cu_chunk, p.meta_i64, c));
-    const int64_t hi = uniform64(load_index(p.cu_chunk, p.meta_i64, c + 1));
+    const int64_t lo = meta_uniform(p.cu_chunk, p.meta_i64, c);
+    const int64_t hi = meta_uniform(p.cu_chunk, p.meta_i64, c + 1);
     if (lo < 0 || hi < lo || hi > p.tokens || hi - lo > Q) return {0, 0};
     return {lo, static_cast<int>(hi - lo)};
 }
@@ -313,7 +331,9 @@ __global__ __launch_bounds__(kListThreads) void ssd_list_kernel(const SsdParams 
 
 // One wave per (chunk, head): the clamped steps v_s and the running sums
 // cum_s = sum_{j<=s} A v_j (fp64) of the chunk, handed on as the chunk-state
-// weights w = exp(cum_last - cum_s) v_s, the scan's v_s and cum_s log2(e), and
+// weights w = exp(cum_last - cum_s) v_s, the scan's decay exponents with the
+// step folded in, cum_s log2(e) - log2(v_s) (+inf for a zero step), and
+// cum_s log2(e), and
 // cum_last; zero steps and weights past the chunk's end. The wave of head 0
 // writes the chunk's descriptor. Lane l owns tokens l + 64 r.
 constexpr int kPrepThreads = 256;
@@ -331,8 +351,8 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(const SsdParams 
     if (h >= H) return;
     const Chunk ch = chunk_of<Q>(p, c);
     if (h == 0 && lane == 0) {
-        const int64_t req = load_index(p.seq_idx, p.meta_i64, c);
-        const bool opens = c == 0 || req != load_index(p.seq_idx, p.meta_i64, c - 1);
+        const int64_t req = meta_uniform(p.seq_idx, p.meta_i64, c);
+        const bool opens = c == 0 || req != meta_uniform(p.seq_idx, p.meta_i64, c - 1);
         int32_t enter = kEnterCarry;
         if (opens) enter = p.init && req >= 0 && req < p.batch ? static_cast<int32_t>(req) : kEnterZero;
         p.desc[c] = ChunkDesc{ch.lo, ch.len, enter};
@@ -356,7 +376,7 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(const SsdParams 
             for (int r = 0; r < R; ++r) u[r] = static_cast<float>(static_cast<const __bf16*>(p.dt)[idx[r]]);
         }
     }
-    const double A = static_cast<double>(p.A[h]);
+    const double A = static_cast<double>(ld_uniform(p.A + h));
     float v[R];
     double cum[R];
     double carry = 0.0;
@@ -364,8 +384,8 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(const SsdParams 
     for (int r = 0; r < R; ++r) {
         const int s = 64 * r + lane;
         float x = u[r];
-        if (p.dt_bias) x += p.dt_bias[h];
-        if (p.dt_softplus) x = softplus_f32(x);
+        if (p.dt_bias) x += ld_uniform(p.dt_bias + h);
+        if (p.dt_softplus) x = softplus_fast(x);
         x = fminf(fmaxf(x, p.dt_min), p.dt_max);
         v[r] = s < ch.len ? x : 0.f;
         double a = A * static_cast<double>(v[r]);
@@ -382,8 +402,9 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(const SsdParams 
     for (int r = 0; r < R; ++r) {
         const int s = 64 * r + lane;
         p.w[base + s] = s < ch.len ? expf(static_cast<float>(carry - cum[r])) * v[r] : 0.f;
-        p.cv[2 * base + s] = v[r];
-        p.cv[2 * base + Q + s] = static_cast<float>(cum[r]) * kLog2e;
+        const float c2 = static_cast<float>(cum[r]) * kLog2e;
+        p.cv[2 * base + s] = c2 - __builtin_amdgcn_logf(v[r]);
+        p.cv[2 * base + Q + s] = c2;
     }
     if (lane == 0) p.cumlast[c * H + h] = static_cast<float>(carry);
 }
@@ -701,8 +722,8 @@ __host__ __device__ constexpr int scan_threads(int Q) { return 2 * Q; }
 constexpr int scan_pitch(int Q) { return Q + 8; }       // (v x)^T row pitch, elements
 constexpr int state_pitch(int N) { return N + 8; }      // entering-state row pitch
 
-// LDS bytes of the scan kernel: the steps and the log2-scaled running sums
-// (fp32), the skip coefficients, the entering state [P][N + 8] and x^T
+// LDS bytes of the scan kernel: the decay exponents with the steps folded in
+// and the log2-scaled running sums (fp32), the skip coefficients, the entering state [P][N + 8] and x^T
 // [P][Q + 8], both in the io type.
 __host__ __device__ constexpr unsigned scan_lds_bytes(int P, int N, int Q) {
     return 4u * Q + 4u * Q + 4u * P + 2u * P * state_pitch(N) + 2u * P * scan_pitch(Q);
@@ -738,9 +759,9 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
     const int lane = tid % 64;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    float* sv = reinterpret_cast<float*>(smem);
-    float* cum2 = sv + Q;
-    static_assert(NT == 2 * Q, "one step value per thread");
+    float* sl = reinterpret_cast<float*>(smem);  // [Q] cum_s log2(e) - log2(v_s)
+    float* cum2 = sl + Q;                          // [Q] cum_s log2(e)
+    static_assert(NT == 2 * Q, "one value per thread");
     float* sd = cum2 + Q;  // [P] skip coefficients
     unsigned short* sS = reinterpret_cast<unsigned short*>(sd + P);
     unsigned short* xv = sS + P * SP;
@@ -750,7 +771,8 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
     const int64_t xoff = (d.lo * H + h) * P;  // the chunk's first x / z / out row of head h
 
     // ---- loads issued up front.
-    const float step = p.cv[(c * H + h) * 2 * Q + tid];  // v_s (tid < Q), then cum_s log2(e)
+    // cum_s log2(e) - log2(v_s) (tid < Q), then cum_s log2(e).
+    const float step = p.cv[(c * H + h) * 2 * Q + tid];
     // x: thread handles row octet q of token pair s (eight threads per token row).
     const Rsrc xr = make_rsrc(static_cast<const IT*>(p.x) + xoff, len * xrow);
     u16x8 rx[XPASS][2];
@@ -784,7 +806,7 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
     const float dcoef = bload_f32(dr, 4u * (p.D_per_dim ? h * P + min(tid, P - 1) : h));
 
     // Steps, x^T (exact) and the entering state into LDS.
-    sv[tid] = step;  // cum2 follows sv
+    sl[tid] = step;  // cum2 follows sl
     if (tid < P) sd[tid] = dcoef;
 #pragma unroll
     for (int r = 0; r < XPASS; ++r) {
@@ -859,12 +881,13 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
     typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
     constexpr int DEPTH = 2;  // s blocks of C B^T in flight per tile
     u32x4v cb[TT][DEPTH][CW];
+    const Rsrc cbr = make_rsrc(cbp, Q * Q * sizeof(CBT));
     auto cb_load = [&](int k, int kk, int dd) {
         const int t0 = 16 * (wave + NW * k);
-        const u32x4v* r =
-            reinterpret_cast<const u32x4v*>(cbp + (t0 + lane % 16) * Q + min(kk, Q - 32) + kcol);
+        const uint32_t off = ((t0 + lane % 16) * Q + min(kk, Q - 32) + kcol) * sizeof(CBT);
 #pragma unroll
-        for (int w = 0; w < CW; ++w) cb[k][dd][w] = r[w];
+        for (int w = 0; w < CW; ++w)
+            cb[k][dd][w] = __builtin_amdgcn_raw_buffer_load_b128(cbr, off + 16 * w, 0, 0);
     };
     auto cb_value = [&](int k, int dd, int j) -> float {
         if constexpr (CW == 1) {
@@ -894,12 +917,10 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
                 const int pr = 16 * pt + lane % 16;
                 xf[pt] = *reinterpret_cast<const v8*>(xv + pr * XP + swz(pr, col));
             }
-            float cs[8], vs[8];
+            // v_s exp2(ct - cs) = exp2(ct - (cs - log2 v_s)).
+            float ls[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                cs[j] = cum2[col + j];
-                vs[j] = sv[col + j];
-            }
+            for (int j = 0; j < 8; ++j) ls[j] = sl[col + j];
 #pragma unroll
             for (int k = 0; k < TT; ++k) {
                 const int t0 = 16 * (wave + NW * k);
@@ -914,13 +935,13 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
                     if (kk + 31 > t0) {
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
-                            const float ex = col + j <= t ? ct - cs[j] : -__builtin_huge_valf();
-                            a[j] = static_cast<IT>(cb_value(k, dd, j) * vs[j] * __builtin_amdgcn_exp2f(ex));
+                            const float ex = col + j <= t ? ct - ls[j] : -__builtin_huge_valf();
+                            a[j] = static_cast<IT>(cb_value(k, dd, j) * __builtin_amdgcn_exp2f(ex));
                         }
                     } else {
 #pragma unroll
                         for (int j = 0; j < 8; ++j)
-                            a[j] = static_cast<IT>(cb_value(k, dd, j) * vs[j] * __builtin_amdgcn_exp2f(ct - cs[j]));
+                            a[j] = static_cast<IT>(cb_value(k, dd, j) * __builtin_amdgcn_exp2f(ct - ls[j]));
                     }
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(a, xf[pt], acc[k][pt]);
