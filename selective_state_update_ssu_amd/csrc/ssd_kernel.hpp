@@ -725,8 +725,14 @@ constexpr int state_pitch(int N) { return N + 8; }      // entering-state row pi
 // LDS bytes of the scan kernel: the decay exponents with the steps folded in
 // and the log2-scaled running sums (fp32), the skip coefficients, the entering state [P][N + 8] and x^T
 // [P][Q + 8], both in the io type.
+// The epilogue's fp32 scratch (16 rows per wave) then takes the x^T area and
+// what follows it.
+__host__ __device__ constexpr int scan_epilogue_pitch(int P) { return P + 4; }
 __host__ __device__ constexpr unsigned scan_lds_bytes(int P, int N, int Q) {
-    return 4u * Q + 4u * Q + 4u * P + 2u * P * state_pitch(N) + 2u * P * scan_pitch(Q);
+    return 4u * Q + 4u * Q + 4u * P + 2u * P * state_pitch(N) +
+           (2u * P * scan_pitch(Q) > 4u * 16 * scan_epilogue_pitch(P) * (scan_threads(Q) / 64)
+                ? 2u * P * scan_pitch(Q)
+                : 4u * 16 * scan_epilogue_pitch(P) * (scan_threads(Q) / 64));
 }
 
 // x^T and the entering state are stored permuted by swz().
@@ -805,6 +811,25 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
     const Rsrc dr = make_rsrc(p.D, p.D ? static_cast<uint32_t>((p.D_per_dim ? H * P : H) * 4) : 0u);
     const float dcoef = bload_f32(dr, 4u * (p.D_per_dim ? h * P + min(tid, P - 1) : h));
 
+    // z rows of the epilogue (zeros without z): lane l finishes 16 consecutive
+    // columns of row l / 4 of each of its tiles. Where every wave's tiles fit the
+    // entering-state area they are requested now and parked there once the
+    // entering-state product is done with it; otherwise they are requested
+    // after the products inside the chunk.
+    const int er = lane / 4, ec = (lane % 4) * (P / 4);
+    static_assert(P / 4 == 16, "one lane finishes 16 columns");
+    constexpr int ZL = NW * TT * 2048 <= 2 * P * SP ? TT : 0;
+    const Rsrc zr = make_rsrc(p.z ? static_cast<const IT*>(p.z) + xoff : nullptr, p.z ? len * xrow : 0u);
+    u16x8 ez[TT][2];
+    auto z_load = [&](int k) {
+        const uint32_t off = (16 * (wave + NW * k) + er) * xrow + 2 * ec;
+        ez[k][0] = bload_nt(zr, off);
+        ez[k][1] = bload_nt(zr, off + 16);
+    };
+#pragma unroll
+    for (int k = 0; k < ZL; ++k) z_load(k);
+    u16x8* const zslot = reinterpret_cast<u16x8*>(sS) + 2 * (wave * 64 + lane);  // + 2 * 64 * NW * k
+
     // Steps, x^T (exact) and the entering state into LDS.
     sl[tid] = step;  // cum2 follows sl
     if (tid < P) sd[tid] = dcoef;
@@ -868,6 +893,15 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) acc[k][pt][i] *= f;
             }
+    }
+
+    if constexpr (ZL > 0) {
+        lds_barrier();  // every wave is done with the entering state
+#pragma unroll
+        for (int k = 0; k < ZL; ++k) {
+            zslot[2 * 64 * NW * k] = ez[k][0];
+            zslot[2 * 64 * NW * k + 1] = ez[k][1];
+        }
     }
 
     // ---- inside the chunk: (C B^T masked, times the decays and the steps v_s)
@@ -951,18 +985,8 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
         }
     }
 
-    // z rows of the epilogue, requested before the skip term (zeros without z): lane l finishes 16
-    // consecutive columns of row l / 4 of each of its tiles.
-    const int er = lane / 4, ec = (lane % 4) * (P / 4);
-    static_assert(P / 4 == 16, "one lane finishes 16 columns");
-    const Rsrc zr = make_rsrc(p.z ? static_cast<const IT*>(p.z) + xoff : nullptr, p.z ? len * xrow : 0u);
-    u16x8 ez[TT][2];
 #pragma unroll
-    for (int k = 0; k < TT; ++k) {
-        const uint32_t off = (16 * (wave + NW * k) + er) * xrow + 2 * ec;
-        ez[k][0] = bload_nt(zr, off);
-        ez[k][1] = bload_nt(zr, off + 16);
-    }
+    for (int k = ZL; k < TT; ++k) z_load(k);
 
     // ---- skip term from the exact x^T in LDS (row t's four consecutive tokens
     // are one 8-byte read), then gate and store: each tile goes through a
@@ -979,12 +1003,11 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[k][pt][i] += sd[pr] * f32_of<IT>(xr4[i]);
         }
-    constexpr int EP = P + 4;  // scratch row pitch in floats (16-byte aligned rows)
-    static_assert(NW * 16 * EP * 4 <= 2 * P * (SP + XP), "epilogue scratch fits");
+    constexpr int EP = scan_epilogue_pitch(P);
     IT* op = static_cast<IT*>(p.out);
     const bool gate = p.z != nullptr;
-    lds_barrier();
-    float* scratch = reinterpret_cast<float*>(sS) + wave * 16 * EP;
+    lds_barrier();  // every wave is done with x^T
+    float* scratch = reinterpret_cast<float*>(xv) + wave * 16 * EP;
 #pragma unroll
     for (int k = 0; k < TT; ++k) {
         if (!live[k]) break;
@@ -997,11 +1020,13 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
         if (t < len) {
             const int64_t xi = xoff + static_cast<int64_t>(t) * H * P + ec;
             const f32x4* srow = reinterpret_cast<const f32x4*>(scratch + er * EP + ec);
+            const u16x8 z0 = k < ZL ? zslot[2 * 64 * NW * k] : ez[k][0];
+            const u16x8 z1 = k < ZL ? zslot[2 * 64 * NW * k + 1] : ez[k][1];
             u16x8 o0, o1;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 float y = srow[e / 4][e % 4];
-                if (gate) y *= gate_f32(f32_of<IT>(ez[k][e / 8][e % 8]));
+                if (gate) y *= gate_f32(f32_of<IT>(e < 8 ? z0[e] : z1[e - 8]));
                 if (e < 8)
                     o0[e] = bits_of<IT>(y);
                 else
