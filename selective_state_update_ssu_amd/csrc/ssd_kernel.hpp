@@ -519,8 +519,15 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
     const int64_t tile = static_cast<int64_t>(H) * P * N;
     const bool lists = !p.return_all && p.batch > 0;
 
+    // Workgroups are dealt to the XCDs round robin, so with a grid of a multiple
+    // of the XCD count each XCD always sees the same residue of item % XCDs.
+    // Heads are permuted so that residue x means the contiguous heads
+    // [x H / XCDs, (x + 1) H / XCDs): every XCD works on every run, and the
+    // heads sharing B rows (a group, or part of one) share one L2.
+    const bool by_xcd = H % ssu::kXcds == 0 && gridDim.x % ssu::kXcds == 0;
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
-        const int r = static_cast<int>(item / H), h = static_cast<int>(item % H);
+        const int r = static_cast<int>(item / H), u = static_cast<int>(item % H);
+        const int h = by_xcd ? (u % ssu::kXcds) * (H / ssu::kXcds) + u / ssu::kXcds : u;
         const int c0 = ld_uniform(p.walk_first + r), nc = ld_uniform(p.walk_len + r);
         const int g = h / p.heads_per_group;
         const IT* xh = static_cast<const IT*>(p.x) + h * P;
@@ -811,20 +818,21 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
     const Rsrc dr = make_rsrc(p.D, p.D ? static_cast<uint32_t>((p.D_per_dim ? H * P : H) * 4) : 0u);
     const float dcoef = bload_f32(dr, 4u * (p.D_per_dim ? h * P + min(tid, P - 1) : h));
 
-    // z rows of the epilogue (zeros without z): lane l finishes 16 consecutive
-    // columns of row l / 4 of each of its tiles. Where every wave's tiles fit the
+    // z rows of the epilogue (zeros without z): lane l finishes 8 consecutive
+    // columns of rows l / 8 and l / 8 + 8 of each of its tiles, so every store
+    // instruction writes eight whole rows. Where every wave's tiles fit the
     // entering-state area they are requested now and parked there once the
     // entering-state product is done with it; otherwise they are requested
     // after the products inside the chunk.
-    const int er = lane / 4, ec = (lane % 4) * (P / 4);
-    static_assert(P / 4 == 16, "one lane finishes 16 columns");
+    const int er = lane / 8, ec = (lane % 8) * (P / 8);
+    static_assert(P / 8 == 8, "eight lanes per row, 16 bytes each");
     constexpr int ZL = NW * TT * 2048 <= 2 * P * SP ? TT : 0;
     const Rsrc zr = make_rsrc(p.z ? static_cast<const IT*>(p.z) + xoff : nullptr, p.z ? len * xrow : 0u);
     u16x8 ez[TT][2];
     auto z_load = [&](int k) {
         const uint32_t off = (16 * (wave + NW * k) + er) * xrow + 2 * ec;
         ez[k][0] = bload_nt(zr, off);
-        ez[k][1] = bload_nt(zr, off + 16);
+        ez[k][1] = bload_nt(zr, off + 8 * xrow);
     };
 #pragma unroll
     for (int k = 0; k < ZL; ++k) z_load(k);
@@ -1016,24 +1024,23 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
 #pragma unroll
             for (int i = 0; i < 4; ++i) scratch[(4 * (lane / 16) + i) * EP + 16 * pt + lane % 16] = acc[k][pt][i];
         ssu::wave_lds_sync();
-        const int t = 16 * (wave + NW * k) + er;
-        if (t < len) {
-            const int64_t xi = xoff + static_cast<int64_t>(t) * H * P + ec;
-            const f32x4* srow = reinterpret_cast<const f32x4*>(scratch + er * EP + ec);
-            const u16x8 z0 = k < ZL ? zslot[2 * 64 * NW * k] : ez[k][0];
-            const u16x8 z1 = k < ZL ? zslot[2 * 64 * NW * k + 1] : ez[k][1];
-            u16x8 o0, o1;
+        const u16x8 zz[2] = {k < ZL ? zslot[2 * 64 * NW * k] : ez[k][0],
+                             k < ZL ? zslot[2 * 64 * NW * k + 1] : ez[k][1]};
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float y = srow[e / 4][e % 4];
-                if (gate) y *= gate_f32(f32_of<IT>(e < 8 ? z0[e] : z1[e - 8]));
-                if (e < 8)
-                    o0[e] = bits_of<IT>(y);
-                else
-                    o1[e - 8] = bits_of<IT>(y);
+        for (int half = 0; half < 2; ++half) {
+            const int row = er + 8 * half, t = 16 * (wave + NW * k) + row;
+            if (t < len) {
+                const f32x4* srow = reinterpret_cast<const f32x4*>(scratch + row * EP + ec);
+                u16x8 o;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float y = srow[e / 4][e % 4];
+                    if (gate) y *= gate_f32(f32_of<IT>(zz[half][e]));
+                    o[e] = bits_of<IT>(y);
+                }
+                __builtin_nontemporal_store(
+                    o, reinterpret_cast<u16x8*>(op + xoff + static_cast<int64_t>(t) * H * P + ec));
             }
-            __builtin_nontemporal_store(o0, reinterpret_cast<u16x8*>(op + xi));
-            __builtin_nontemporal_store(o1, reinterpret_cast<u16x8*>(op + xi + 8));
         }
         ssu::wave_lds_sync();  // the next tile reuses the scratch
     }
