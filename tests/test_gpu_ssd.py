@@ -40,6 +40,11 @@ CASES = {
     # request ids out of chunk order; fp16 dt.
     "ids_out_of_order": dict(lengths=[300, 40, 520], H=4, P=64, N=128, G=4, chunk=128,
                              with_init=True, request_ids=[2, 0, 1], dt_dtype="f16"),
+    # more runs of chunks than the state walk ranks by length (2048): they are
+    # walked in chunk order; a few multi-chunk requests among 2100.
+    "more_runs_than_ranked": dict(lengths=[1 + (7 * i) % 5 for i in range(2096)]
+                                  + [300, 700, 129, 257], H=2, P=64, N=64, G=1, chunk=128,
+                                  with_init=True),
 }
 
 
