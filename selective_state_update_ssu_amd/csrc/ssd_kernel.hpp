@@ -12,9 +12,12 @@
 //   scan      y_t = sum_{s<=t} CB[t, s] exp(cum_t - cum_s) v_s x_s
 //                   + exp(cum_t) C_t . S_{c-1} + D x_t, gated      per (chunk, head)
 //
-// with v the clamped step and cum the running sum of A v inside the chunk
-// (fp64, so the decay between two tokens is exact to fp32 however far into the
-// chunk they lie). The three contractions run on the matrix cores with 16-bit
+// with v the clamped step and cum the running sum of A v inside the chunk, in
+// fp64. The walk's weights take exp of fp64 differences, exact to fp32 however
+// far into the chunk; the scan's decays exp2 the difference of two fp32-rounded
+// running sums (an absolute error of about one ulp of |cum| log2(e) in the
+// exponent, far below the 16-bit rounding of the decayed entry for the
+// magnitudes a chunk reaches). The three contractions run on the matrix cores with 16-bit
 // operands and fp32 accumulation. The walk feeds w_s x_s as a high and a low
 // 16-bit part, which makes each product of a state accurate to about 2^-16
 // instead of 2^-8, and keeps the state in its fp32 accumulators from chunk to
