@@ -348,8 +348,10 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(const SsdParams 
     constexpr float kLog2e = 1.4426950408889634f;
     const int H = p.nheads;
     const int hq = (H + HW - 1) / HW;
-    const int64_t c = blockIdx.x / hq;
-    const int h = static_cast<int>(blockIdx.x % hq) * HW + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    // XCD-contiguous numbering: the workgroups of a chunk share its dt rows in one L2.
+    const int64_t wg = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t c = wg / hq;
+    const int h = static_cast<int>(wg % hq) * HW + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int lane = threadIdx.x % 64;
     if (h >= H) return;
     const Chunk ch = chunk_of<Q>(p, c);
@@ -425,8 +427,11 @@ template <int Q> __host__ __device__ constexpr int bmm_blocks() { return (bmm_ti
 template <typename IT, int N, int Q>
 __global__ __launch_bounds__(kThreads) void ssd_bmm_kernel(const SsdParams p) {
     typedef typename Mfma<IT>::v8 v8;
-    const int64_t cg = blockIdx.x / bmm_blocks<Q>();
-    const int tile = static_cast<int>(blockIdx.x % bmm_blocks<Q>()) * kWaves +
+    // XCD-contiguous numbering: the workgroups of a (chunk, group) share its C and
+    // B rows in one L2.
+    const int64_t wg = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t cg = wg / bmm_blocks<Q>();
+    const int tile = static_cast<int>(wg % bmm_blocks<Q>()) * kWaves +
                      __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     if (tile >= bmm_tiles<Q>()) return;
     const int64_t c = cg / p.ngroups;
