@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "ssu_kernel.hpp"
 
@@ -1073,18 +1074,21 @@ hipError_t launch_instance(const SsdParams& p, hipStream_t stream) {
                        dim3(kThreads), 0, stream, p);
     // The walk runs as many workgroups as fit on the device at once (each loops
     // over work items), never more than there can be items.
-    static int resident[64];
+    // (Cached per device and instance; concurrent first calls store the same value.)
+    static std::atomic<int> resident[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (resident[dev] == 0) {
+    int fit = resident[dev].load(std::memory_order_relaxed);
+    if (fit == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ssd_state_walk_kernel<IT, ST, P, N, Q>,
                                                          walk_threads(N), walk_lds_bytes(P, N)) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return hipErrorInvalidValue;
-        resident[dev] = per_cu * cus > 0 ? per_cu * cus : 1;
+        fit = per_cu * cus > 0 ? per_cu * cus : 1;
+        resident[dev].store(fit, std::memory_order_relaxed);
     }
-    const int64_t walkers = std::min<int64_t>(resident[dev], p.nchunks * p.nheads);
+    const int64_t walkers = std::min<int64_t>(fit, p.nchunks * p.nheads);
     hipLaunchKernelGGL((ssd_state_walk_kernel<IT, ST, P, N, Q>), dim3(static_cast<unsigned>(walkers)),
                        dim3(walk_threads(N)), walk_lds_bytes(P, N), stream, p);
     hipLaunchKernelGGL((ssd_scan_kernel<IT, ST, P, N, Q>),
