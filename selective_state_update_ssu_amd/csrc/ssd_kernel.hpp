@@ -534,7 +534,16 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
     // [x H / XCDs, (x + 1) H / XCDs): every XCD works on every run, and the
     // heads sharing B rows (a group, or part of one) share one L2.
     const bool by_xcd = H % ssu::kXcds == 0 && gridDim.x % ssu::kXcds == 0;
-    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+    // Items are dealt in rounds of one per workgroup, every other round in
+    // reverse ("snake" order): with the runs longest first, a workgroup that
+    // got one of the longest walks gets one of the shortest next.
+    const int64_t G = gridDim.x;
+    for (int64_t round = 0;; ++round) {
+        const int64_t item = round * G + ((round & 1) ? G - 1 - blockIdx.x : blockIdx.x);
+        if (item >= nitems) {
+            if (round * G >= nitems) break;
+            continue;  // this round's tail is short; a reversed round may still hold an item
+        }
         const int r = static_cast<int>(item / H), u = static_cast<int>(item % H);
         const int h = by_xcd ? (u % ssu::kXcds) * (H / ssu::kXcds) + u / ssu::kXcds : u;
         const int c0 = ld_uniform(p.walk_first + r), nc = ld_uniform(p.walk_len + r);
