@@ -51,7 +51,6 @@ namespace ssd {
 
 using ssu::lds_barrier;
 using ssu::load_index;
-using ssu::uniform64;
 
 constexpr int kThreads = 256;  // four wave64s per workgroup
 constexpr int kWaves = kThreads / 64;
@@ -228,19 +227,20 @@ __device__ __forceinline__ ChunkDesc load_desc(const SsdParams& p, int64_t c) {
 // of a chunk then meet the chunk's shared operands in one L2.
 __device__ __forceinline__ int64_t xcd_order(int64_t id, int64_t n) { return ssu::xcd_tile(id, n); }
 
-// Chunk c's first token and length; a range outside [0, tokens], running
-// backwards or longer than Q counts as empty.
-struct Chunk {
-    int64_t lo;
-    int len;
-};
-
 // Entry i of a chunk-metadata array (the caller's, read only), one value for
 // the whole wave.
 __device__ __forceinline__ int64_t meta_uniform(const void* ptr, int is64, int64_t i) {
     return is64 ? ld_uniform(static_cast<const int64_t*>(ptr) + i)
                 : static_cast<int64_t>(ld_uniform(static_cast<const int32_t*>(ptr) + i));
 }
+
+// Chunk c's first token and length from the caller's cu_chunk_seqlens (read by
+// the prep kernel, which hands them on in the chunk descriptor); a range
+// outside [0, tokens], running backwards or longer than Q counts as empty.
+struct Chunk {
+    int64_t lo;
+    int len;
+};
 
 template <int Q>
 __device__ __forceinline__ Chunk chunk_of(const SsdParams& p, int64_t c) {
