@@ -44,6 +44,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "ssu_kernel.hpp"
 
@@ -605,49 +606,59 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
                 for (int qt = 0; qt < 2; ++qt) acc[nt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        // The state after chunk c: the next chunk's entering state (io type) if the
-        // run goes on, and the returned states (state type).
-        auto emit = [&](int c, bool next, int first_req) {
-            if (next) {
-                IT* const e16 = static_cast<IT*>(p.s16) + static_cast<int64_t>(c + 1) * tile;
+        // A state tile [P][N] of type T to dst (row-major, this head's block of
+        // a state tile), through the B^T area of LDS so that every store writes
+        // whole 16-byte pieces of whole rows: each wave drops its part of S^T into
+        // LDS (16-byte chunks of row p permuted by p, which spreads the writes of
+        // sixteen rows over the banks), then the workgroup copies the rows out.
+        // The caller makes sure every wave is done with the B^T area; the next
+        // use of LDS is behind a barrier.
+        auto store_tile = [&](auto* dst) {
+            typedef typename std::remove_pointer<decltype(dst)>::type T;
+            typedef T t4 __attribute__((ext_vector_type(4)));
+            constexpr int CPR = N * static_cast<int>(sizeof(T)) / 16;  // 16-byte chunks per row
+            static_assert(P * N * sizeof(T) <= 2u * N * XP, "the tile fits the B^T area");
+            unsigned char* lt = reinterpret_cast<unsigned char*>(bt);
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                    for (int qt = 0; qt < 2; ++qt) {
-                        u16x4 o;
+                for (int qt = 0; qt < 2; ++qt) {
+                    const int pr = q0 + 16 * qt + lane % 16, n = n0 + 16 * nt + 4 * (lane / 16);
+                    const int byte = n * static_cast<int>(sizeof(T));
+                    t4 v;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) o[i] = bits_of<IT>(acc[nt][qt][i]);
-                        *reinterpret_cast<u16x4*>(e16 + elem(nt, qt)) = o;
-                    }
-            }
-            auto put = [&](int64_t row) {
-                ST* const dst = static_cast<ST*>(p.states) + row * tile;
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int qt = 0; qt < 2; ++qt) {
-                        st4 v;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) v[i] = static_cast<ST>(acc[nt][qt][i]);
-                        *reinterpret_cast<st4*>(dst + elem(nt, qt)) = v;
-                    }
-            };
-            if (p.return_all) {
-                put(c);
-            } else {
-                int b = first_req;
-                for (int64_t guard = 0; guard < p.batch && b >= 0 && b < p.batch; ++guard) {
-                    put(b);
-                    b = ld_uniform(p.list_next + b);
+                    for (int i = 0; i < 4; ++i) v[i] = static_cast<T>(acc[nt][qt][i]);
+                    *reinterpret_cast<t4*>(lt + pr * N * sizeof(T) + (((byte / 16) ^ (pr % CPR)) * 16) +
+                                           byte % 16) = v;
                 }
+            lds_barrier();
+            constexpr int PIECES = P * CPR / NT;
+            static_assert(PIECES * NT == P * CPR, "whole pieces");
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) {
+                const int idx = tid + NT * i, pr = idx / CPR, ch = idx % CPR;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(lt + pr * N * sizeof(T) + ((ch ^ (pr % CPR)) * 16));
+                *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(dst + static_cast<int64_t>(pr) * N) +
+                                          ch * 16) = v;
             }
         };
+        // The returned states, written from the accumulators directly (each
+        // chunk's with return_intermediate_states, else only the requests'
+        // last chunks').
+        auto put = [&](int64_t row) {
+            ST* const dst = static_cast<ST*>(p.states) + row * tile;
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    st4 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = static_cast<ST>(acc[nt][qt][i]);
+                    *reinterpret_cast<st4*>(dst + elem(nt, qt)) = v;
+                }
+        };
 
-        // Chunk c's first block emits the state after chunk c - 1 right after its
-        // operands arrive and before the next loads are requested, so that waiting
-        // for those loads never waits for stores issued after them.
         // Per-chunk scalars are requested a chunk ahead of their use.
-        int prev_req = -1;
         ChunkDesc dn = load_desc(p, (nc > 1 ? c0 + 1 : c0));
         float cl = ld_uniform(p.cumlast + static_cast<int64_t>(c0) * H + h);
         int rq = lists ? ld_uniform(p.list_head + c0) : -1;
@@ -689,7 +700,6 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
                     }
                 }
                 if (sb == 0) {
-                    if (k > 0) emit(c - 1, true, prev_req);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -729,13 +739,26 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
                         }
                 }
             }
-            prev_req = first_req;
+            // The state after chunk c: the next chunk's entering state (io type)
+            // if the run goes on, and the returned states (state type).
+            if (more) {
+                lds_barrier();  // every wave is done with this block's operands
+                store_tile(static_cast<IT*>(p.s16) + static_cast<int64_t>(c + 1) * tile + hs);
+            }
+            if (p.return_all) {
+                put(c);
+            } else {
+                int b = first_req;
+                for (int64_t guard = 0; guard < p.batch && b >= 0 && b < p.batch; ++guard) {
+                    put(b);
+                    b = ld_uniform(p.list_next + b);
+                }
+            }
             d = dn;
             dn = dnn;
             cl = cln;
             rq = rqn;
         }
-        emit(c0 + nc - 1, false, prev_req);
         __syncthreads();  // every wave is done with LDS before the next item stages
     }
 }
