@@ -158,19 +158,21 @@ int check_operands(const ssu_operands& op, int64_t rows, bool work, bool packed)
 // 128, headdim 64): a read+write one-token call streams best in small tiles
 // (2 loads per lane, 2 heads per workgroup with an fp32 state, 1 with a 16-bit
 // one); a read-only call and the packed call, which writes several states per
-// state read, in larger ones (4 loads per lane, 2 heads per workgroup). One-token
-// calls gain from each XCD walking a contiguous range of tiles; packed calls do
-// not (their per-sequence work varies with the token count).
+// state read, in larger ones (4 loads per lane, 2 heads per workgroup). Calls
+// whose sequences all have the same number of tokens (one-token calls, packed
+// calls without cu_seqlens) gain from each XCD walking a contiguous range of
+// tiles; varlen packed calls do not, since a contiguous range of sequences can
+// hold more tokens than another, so their tiles go round robin.
 struct Shape {
     int heads_per_block, loads_per_lane, xcd_order;
 };
 
-Shape default_shape(const ssu_operands& op, bool packed) {
+Shape default_shape(const ssu_operands& op, bool packed, bool equal_lengths) {
     const bool read_only = op.disable_state_update != 0;
     Shape s;
     const bool sr = op.rand_seed && op.state_dtype != SSU_F32 && !read_only;
     if (packed)
-        s = {2, 4, 0};
+        s = {2, 4, equal_lengths ? 1 : 0};
     else if (read_only)
         s = {2, 4, 1};
     else if (sr)  // the Philox work of stochastic rounding wants bigger tiles
@@ -184,7 +186,8 @@ Shape default_shape(const ssu_operands& op, bool packed) {
     return s;
 }
 
-void fill_common(ssu::KernelParams& k, const ssu_operands& op, bool packed) {
+void fill_common(ssu::KernelParams& k, const ssu_operands& op, bool packed,
+                 bool equal_lengths) {
     k.state = op.state;
     k.x = op.x;
     k.B = op.B;
@@ -204,7 +207,7 @@ void fill_common(ssu::KernelParams& k, const ssu_operands& op, bool packed) {
     k.headdim = static_cast<int32_t>(op.headdim);
     k.ngroups = static_cast<int32_t>(op.ngroups);
     k.heads_per_group = static_cast<int32_t>(op.nheads / op.ngroups);
-    const Shape dflt = default_shape(op, packed);
+    const Shape dflt = default_shape(op, packed, equal_lengths);
     k.heads_per_block = op.heads_per_block ? op.heads_per_block : dflt.heads_per_block;
     k.loads_per_lane = op.loads_per_lane ? op.loads_per_lane : dflt.loads_per_lane;
     k.xcd_order = op.tile_order ? op.tile_order == 1 : dflt.xcd_order;
@@ -260,7 +263,7 @@ int ssu_one_token(const ssu_one_token_args* a, void* stream) {
     if (a->batch == 0) return ok();
 
     ssu::KernelParams k{};
-    fill_common(k, op, false);
+    fill_common(k, op, false, true);
     k.src = a->src_slots;
     k.dst = a->dst_slots;
     k.src_i64 = a->src_dtype == SSU_I64;
@@ -308,7 +311,7 @@ int ssu_packed_varlen(const ssu_packed_args* a, void* stream) {
                     (long long)a->rows, (long long)a->nseq, (long long)a->seq_len);
 
     ssu::KernelParams k{};
-    fill_common(k, op, true);
+    fill_common(k, op, true, a->cu_seqlens == nullptr);
     k.src = a->src_table;
     k.dst = a->dst_table;
     k.cu = a->cu_seqlens;
