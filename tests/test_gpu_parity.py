@@ -167,6 +167,35 @@ def test_packed_small(case):
     compare_full(_case_id(case), w, out, after, before, ref)
 
 
+@pytest.mark.parametrize("case", [
+    dict(state_dtype="f32", io="bf16", N=128, P=64, H=4, G=1),
+    dict(state_dtype="bf16", io="f16", N=64, P=80, H=4, G=2, hpb=2),
+    dict(state_dtype="f16", io="f32", N=256, P=64, H=2, G=1),
+    dict(state_dtype="f32", io="bf16", N=16, P=64, H=4, G=4, accepted=False),
+], ids=_case_id)
+def test_packed_sequences_longer_than_a_staged_chunk(case):
+    """Sequences of 8, 9, 16, 17 and 23 tokens: the kernel stages the per-token
+    operands eight tokens at a time, so these cross one, two and three restaging
+    points with the state still in registers; every token's destination is
+    checked."""
+    c = dict(case)
+    hpb = c.pop("hpb", 0)
+    lengths = [9, 1, 17, 8, 0, 23, 16, 2]
+    w = wl.packed("long", 212, nseq=len(lengths), max_len=24, nslots=200, device=DEV,
+                  lengths=lengths, pad_fraction=0.12, **c)
+    out, after, before = hz.gpu_run(w, heads_per_block=hpb)
+    compare_full(_case_id(case), w, out, after, before, hz.oracle_full(w))
+
+
+def test_dense_sequences_longer_than_a_staged_chunk():
+    """A dense [batch, 11, heads, dim] call: every sequence restages its operands
+    once, at token 8."""
+    w = wl.packed("denselong", 213, nseq=5, max_len=11, H=4, P=64, N=128, G=1, nslots=64,
+                  device=DEV, dense=True, pad_fraction=0.2)
+    out, after, before = hz.gpu_run(w)
+    compare_full("dense-long", w, out, after, before, hz.oracle_full(w))
+
+
 # ------------------------------------------------------------- packed edges
 
 def _packed_base(seed=303, **kw):
