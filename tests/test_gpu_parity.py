@@ -196,6 +196,33 @@ def test_dense_sequences_longer_than_a_staged_chunk():
     compare_full("dense-long", w, out, after, before, hz.oracle_full(w))
 
 
+def test_pad_slot_id_inside_the_cache_and_wide_slot_ids():
+    """pad_slot_id may name a real slot: a sequence reading it is inert and a
+    write to it is dropped, while -1 and int64 ids beyond the cache (2^40,
+    -2^40) are out of range and act as pads too."""
+    w = wl.one_token("padid", 121, batch=12, H=4, P=64, N=64, G=1, nslots=30, device=DEV,
+                     index_dtype="i64", dst_mode="distinct")
+    pad = int(w.src[3])
+    w.pad_slot_id = pad
+    w.dst[5] = pad
+    w.src[7] = -1
+    w.src[8] = 1 << 40
+    w.dst[9] = -(1 << 40)
+    out, after, before = hz.gpu_run(w)
+    compare_full("pad-id one-token", w, out, after, before, hz.oracle_full(w))
+    assert torch.equal(hz.bits(after[pad]), hz.bits(before[pad]))
+
+    p = wl.packed("padid", 122, nseq=6, max_len=4, H=4, P=64, N=64, G=1, nslots=40,
+                  device=DEV, index_dtype="i64", lengths=[3, 4, 1, 2, 4, 2])
+    pad = int(p.src_table[1, 0])
+    p.pad_slot_id = pad
+    p.src_table[4, 2] = 1 << 40
+    p.src_table[5, 1] = -1
+    out, after, before = hz.gpu_run(p)
+    compare_full("pad-id packed", p, out, after, before, hz.oracle_full(p))
+    assert torch.equal(hz.bits(after[pad]), hz.bits(before[pad]))
+
+
 # ------------------------------------------------------------- packed edges
 
 def _packed_base(seed=303, **kw):
