@@ -310,3 +310,37 @@ def test_ssd_workspace_bytes(lib):
             + 6 * 8 * 256 * 4 + 6 * 8 * 256 * 8 + 3 * 6 * 4 + 4)
     assert need <= n <= need + 12 * 256 and n % 256 == 0
     assert lib.ssu_ssd_workspace_bytes(-1, 3, 8, 64, 128, 2, 256) == 0
+
+
+def test_error_text_is_per_thread(lib):
+    """Two host threads fail with different messages at the same time; each
+    reads back its own, and a later successful (empty) call clears only the
+    caller's text."""
+    import threading
+
+    both_failed = threading.Barrier(2)
+    a_cleared = threading.Event()
+    seen = {}
+
+    def worker(name, kw):
+        rc, _ = one_token(lib, **kw)
+        both_failed.wait()
+        seen[name, "rc"] = rc
+        seen[name, "after both"] = lib.ssu_last_error().decode()
+        if name == "a":
+            seen["a", "empty rc"], seen["a", "after empty"] = one_token(lib, batch=0)
+            a_cleared.set()
+        else:
+            a_cleared.wait()
+            seen["b", "after a cleared"] = lib.ssu_last_error().decode()
+
+    threads = [threading.Thread(target=worker, args=("a", dict(ngroups=3))),
+               threading.Thread(target=worker, args=("b", dict(dstate=48)))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=30)
+    assert seen["a", "rc"] == INV and "multiple of ngroups" in seen["a", "after both"]
+    assert seen["b", "rc"] == UNS and "dstate 48" in seen["b", "after both"]
+    assert seen["a", "empty rc"] == _abi.SSU_OK and seen["a", "after empty"] == ""
+    assert "dstate 48" in seen["b", "after a cleared"]
