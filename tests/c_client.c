@@ -1,0 +1,301 @@
+/*
+ * c_client.c -- drives the SSU C ABI from plain C, as a serving engine written
+ * in C or C++ would: device buffers from hipMalloc, a HIP stream of its own, no
+ * Python and no torch. One one-token call and one packed call, each checked
+ * against the fp64 oracle (test infrastructure, linked here only):
+ *   - out and the written states within max |gpu - ref| <= 1e-5 max(1, max |ref|)
+ *     (fp32 state and io);
+ *   - placement exact: slots the oracle leaves alone keep their bytes, and rows
+ *     of inert sequences keep a NaN sentinel bit for bit.
+ * Prints "c client ok" and exits 0 on success, 1 on a mismatch, 2 on a HIP or
+ * library error.
+ */
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "ssu.h"
+#include "ssu_oracle.h"
+
+#define CHECK_HIP(call)                                                              \
+    do {                                                                             \
+        hipError_t e_ = (call);                                                      \
+        if (e_ != hipSuccess) {                                                      \
+            fprintf(stderr, "%s failed: %s\n", #call, hipGetErrorString(e_));        \
+            exit(2);                                                                 \
+        }                                                                            \
+    } while (0)
+
+enum { NSLOTS = 12, H = 4, P = 64, N = 128, G = 2 };
+#define SLOT (H * P * N)
+static const uint32_t kSentinel = 0x7FC0DEADu; /* a NaN no computation produces */
+
+/* Seeded 64-bit LCG (Knuth's MMIX constants), top 53 bits as a uniform. */
+static uint64_t rng_state = 0x243F6A8885A308D3ull;
+static float uniform(float lo, float hi) {
+    rng_state = rng_state * 6364136223846793005ull + 1442695040888963407ull;
+    return (float)(lo + (hi - lo) * ((double)(rng_state >> 11) * 0x1.0p-53));
+}
+static void fill(float* v, size_t n, float lo, float hi) {
+    for (size_t i = 0; i < n; ++i) v[i] = uniform(lo, hi);
+}
+static double* widen(const float* v, size_t n) {
+    double* d = malloc(n * sizeof(double));
+    for (size_t i = 0; i < n; ++i) d[i] = v[i];
+    return d;
+}
+static void* to_device(const void* host, size_t bytes) {
+    void* d = NULL;
+    CHECK_HIP(hipMalloc(&d, bytes));
+    CHECK_HIP(hipMemcpy(d, host, bytes, hipMemcpyHostToDevice));
+    return d;
+}
+
+/* Per-head parameters shared by both calls. */
+static float A[H], D[H], dt_bias[H];
+
+/* Compare a GPU result with the oracle's. Returns the number of failures. */
+static int compare(const char* what, int rows, const float* state0, const float* state_gpu,
+                   const double* state_ref, const float* out_gpu, const double* out_ref,
+                   const int* row_live) {
+    int bad = 0;
+    double scale = 1.0, err = 0.0;
+    for (int s = 0; s < NSLOTS; ++s) {
+        const size_t o = (size_t)s * SLOT;
+        int touched = 0;
+        for (size_t i = 0; i < SLOT && !touched; ++i) touched = state_ref[o + i] != (double)state0[o + i];
+        if (!touched) {
+            if (memcmp(state_gpu + o, state0 + o, SLOT * sizeof(float)) != 0) {
+                fprintf(stderr, "%s: slot %d changed but the oracle leaves it alone\n", what, s);
+                ++bad;
+            }
+            continue;
+        }
+        for (size_t i = 0; i < SLOT; ++i) {
+            scale = fmax(scale, fabs(state_ref[o + i]));
+            err = fmax(err, fabs((double)state_gpu[o + i] - state_ref[o + i]));
+        }
+    }
+    if (err > 1e-5 * scale) {
+        fprintf(stderr, "%s: state error %.3e at scale %.3e\n", what, err, scale);
+        ++bad;
+    }
+    scale = 1.0;
+    err = 0.0;
+    for (int r = 0; r < rows; ++r) {
+        const size_t o = (size_t)r * H * P;
+        if (!row_live[r]) {
+            for (size_t i = 0; i < H * P; ++i) {
+                uint32_t bits;
+                memcpy(&bits, out_gpu + o + i, sizeof bits);
+                if (bits != kSentinel) {
+                    fprintf(stderr, "%s: row %d of an inert sequence was written\n", what, r);
+                    ++bad;
+                    break;
+                }
+            }
+            continue;
+        }
+        for (size_t i = 0; i < H * P; ++i) {
+            scale = fmax(scale, fabs(out_ref[o + i]));
+            err = fmax(err, fabs((double)out_gpu[o + i] - out_ref[o + i]));
+        }
+    }
+    if (err > 1e-5 * scale) {
+        fprintf(stderr, "%s: out error %.3e at scale %.3e\n", what, err, scale);
+        ++bad;
+    }
+    printf("%s: %s\n", what, bad ? "MISMATCH" : "matches the oracle");
+    return bad;
+}
+
+/* One call's operands on host and device; rows tokens. */
+typedef struct {
+    int rows;
+    float *x, *z, *dt, *B, *C, *out;
+    void *dx, *dz, *ddt, *dB, *dC, *dout;
+} Tokens;
+
+static Tokens make_tokens(int rows) {
+    Tokens t;
+    t.rows = rows;
+    const size_t hp = (size_t)rows * H * P, gn = (size_t)rows * G * N;
+    t.x = malloc(hp * sizeof(float));
+    t.z = malloc(hp * sizeof(float));
+    t.dt = malloc((size_t)rows * H * sizeof(float));
+    t.B = malloc(gn * sizeof(float));
+    t.C = malloc(gn * sizeof(float));
+    t.out = malloc(hp * sizeof(float));
+    fill(t.x, hp, -1.f, 1.f);
+    fill(t.z, hp, -2.f, 2.f);
+    fill(t.dt, (size_t)rows * H, -3.f, 0.f);
+    fill(t.B, gn, -1.f, 1.f);
+    fill(t.C, gn, -1.f, 1.f);
+    for (size_t i = 0; i < hp; ++i) memcpy(&t.out[i], &kSentinel, sizeof(float));
+    t.dx = to_device(t.x, hp * sizeof(float));
+    t.dz = to_device(t.z, hp * sizeof(float));
+    t.ddt = to_device(t.dt, (size_t)rows * H * sizeof(float));
+    t.dB = to_device(t.B, gn * sizeof(float));
+    t.dC = to_device(t.C, gn * sizeof(float));
+    t.dout = to_device(t.out, hp * sizeof(float));
+    return t;
+}
+
+static ssu_operands operands(void* dstate, const Tokens* t, const void* dA, const void* dD,
+                             const void* dbias) {
+    ssu_operands op;
+    memset(&op, 0, sizeof op);
+    op.state = dstate;
+    op.state_dtype = SSU_F32;
+    op.nslots = NSLOTS;
+    op.nheads = H;
+    op.headdim = P;
+    op.dstate = N;
+    op.ngroups = G;
+    op.x = t->dx;
+    op.B = t->dB;
+    op.C = t->dC;
+    op.z = t->dz;
+    op.out = t->dout;
+    op.io_dtype = SSU_F32;
+    op.dt = t->ddt;
+    op.A = dA;
+    op.D = dD;
+    op.dt_bias = dbias;
+    op.dt_softplus = 1;
+    op.pad_slot_id = -1;
+    return op;
+}
+
+int main(void) {
+    if (ssu_version() != SSU_ABI_VERSION) {
+        fprintf(stderr, "library ABI %d, header %d\n", ssu_version(), SSU_ABI_VERSION);
+        return 2;
+    }
+    hipStream_t stream;
+    CHECK_HIP(hipStreamCreate(&stream));
+
+    for (int h = 0; h < H; ++h) {
+        A[h] = -expf(uniform(0.f, 2.f));
+        D[h] = uniform(-1.f, 1.f);
+        dt_bias[h] = uniform(-1.f, 1.f);
+    }
+    void* dA = to_device(A, sizeof A);
+    void* dD = to_device(D, sizeof D);
+    void* dbias = to_device(dt_bias, sizeof dt_bias);
+    double *A64 = widen(A, H), *D64 = widen(D, H), *bias64 = widen(dt_bias, H);
+
+    float* state0 = malloc((size_t)NSLOTS * SLOT * sizeof(float));
+    fill(state0, (size_t)NSLOTS * SLOT, -1.f, 1.f);
+    float* state_gpu = malloc((size_t)NSLOTS * SLOT * sizeof(float));
+    double* state_ref = malloc((size_t)NSLOTS * SLOT * sizeof(double));
+    double* state0_64 = widen(state0, (size_t)NSLOTS * SLOT);
+    int failures = 0;
+
+    /* ---- one token per sequence: sequence 2 reads a pad slot (inert); every
+       sequence writes a slot no sequence reads. */
+    {
+        enum { BATCH = 5 };
+        const int32_t src[BATCH] = {3, 7, -1, 0, 9};
+        const int32_t dst[BATCH] = {4, 8, 5, 1, 10};
+        const int live[BATCH] = {1, 1, 0, 1, 1};
+        Tokens t = make_tokens(BATCH);
+        void* dstate = to_device(state0, (size_t)NSLOTS * SLOT * sizeof(float));
+        void* dsrc = to_device(src, sizeof src);
+        void* ddst = to_device(dst, sizeof dst);
+        ssu_one_token_args a;
+        memset(&a, 0, sizeof a);
+        a.struct_size = sizeof a;
+        a.op = operands(dstate, &t, dA, dD, dbias);
+        a.batch = BATCH;
+        a.src_slots = dsrc;
+        a.src_dtype = SSU_I32;
+        a.dst_slots = ddst;
+        a.dst_dtype = SSU_I32;
+        if (ssu_one_token(&a, stream) != SSU_OK) {
+            fprintf(stderr, "ssu_one_token: %s\n", ssu_last_error());
+            return 2;
+        }
+        CHECK_HIP(hipStreamSynchronize(stream));
+        CHECK_HIP(hipMemcpy(state_gpu, dstate, (size_t)NSLOTS * SLOT * sizeof(float), hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(t.out, t.dout, (size_t)BATCH * H * P * sizeof(float), hipMemcpyDeviceToHost));
+
+        int64_t src64[BATCH], dst64[BATCH];
+        for (int b = 0; b < BATCH; ++b) src64[b] = src[b], dst64[b] = dst[b];
+        double* out_ref = malloc((size_t)BATCH * H * P * sizeof(double));
+        double *x64 = widen(t.x, (size_t)BATCH * H * P), *z64 = widen(t.z, (size_t)BATCH * H * P);
+        double *dt64 = widen(t.dt, (size_t)BATCH * H), *B64 = widen(t.B, (size_t)BATCH * G * N);
+        double* C64 = widen(t.C, (size_t)BATCH * G * N);
+        if (oracle_ssu_one_token(state0_64, state_ref, NSLOTS, H, P, N, G, BATCH, x64, dt64, 0, A64,
+                                 B64, C64, D64, z64, bias64, 1, src64, dst64, -1, 0, NULL, out_ref) != 0) {
+            fprintf(stderr, "oracle_ssu_one_token refused its arguments\n");
+            return 2;
+        }
+        failures += compare("one-token", BATCH, state0, state_gpu, state_ref, t.out, out_ref, live);
+    }
+
+    /* ---- packed: three sequences of 3, 0 and 4 tokens; the acceptance count
+       picks the read entry of a shared [3, 4] table, every token writes its own
+       entry (-1 entries drop the write). */
+    {
+        enum { NSEQ = 3, STEPS = 4, ROWS = 7 };
+        const int32_t cu[NSEQ + 1] = {0, 3, 3, 7};
+        const int32_t accepted[NSEQ] = {2, 1, 3};
+        const int32_t table[NSEQ * STEPS] = {2, 6, 11, -1, 1, 3, 4, 5, 0, 8, 9, 10};
+        const int live[ROWS] = {1, 1, 1, 1, 1, 1, 1};
+        Tokens t = make_tokens(ROWS);
+        void* dstate = to_device(state0, (size_t)NSLOTS * SLOT * sizeof(float));
+        void* dcu = to_device(cu, sizeof cu);
+        void* dacc = to_device(accepted, sizeof accepted);
+        void* dtab = to_device(table, sizeof table);
+        ssu_packed_args a;
+        memset(&a, 0, sizeof a);
+        a.struct_size = sizeof a;
+        a.op = operands(dstate, &t, dA, dD, dbias);
+        a.rows = ROWS;
+        a.nseq = NSEQ;
+        a.cu_seqlens = dcu;
+        a.num_accepted = dacc;
+        a.meta_dtype = SSU_I32;
+        a.src_table = dtab;
+        a.src_dtype = SSU_I32;
+        a.src_seq_stride = STEPS;
+        a.src_step_stride = 1;
+        a.dst_table = dtab;
+        a.dst_dtype = SSU_I32;
+        a.dst_seq_stride = STEPS;
+        a.dst_step_stride = 1;
+        a.steps = STEPS;
+        if (ssu_packed_varlen(&a, stream) != SSU_OK) {
+            fprintf(stderr, "ssu_packed_varlen: %s\n", ssu_last_error());
+            return 2;
+        }
+        CHECK_HIP(hipStreamSynchronize(stream));
+        CHECK_HIP(hipMemcpy(state_gpu, dstate, (size_t)NSLOTS * SLOT * sizeof(float), hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(t.out, t.dout, (size_t)ROWS * H * P * sizeof(float), hipMemcpyDeviceToHost));
+
+        int64_t cu64[NSEQ + 1], acc64[NSEQ], tab64[NSEQ * STEPS];
+        for (int i = 0; i <= NSEQ; ++i) cu64[i] = cu[i];
+        for (int i = 0; i < NSEQ; ++i) acc64[i] = accepted[i];
+        for (int i = 0; i < NSEQ * STEPS; ++i) tab64[i] = table[i];
+        double* out_ref = malloc((size_t)ROWS * H * P * sizeof(double));
+        double *x64 = widen(t.x, (size_t)ROWS * H * P), *z64 = widen(t.z, (size_t)ROWS * H * P);
+        double *dt64 = widen(t.dt, (size_t)ROWS * H), *B64 = widen(t.B, (size_t)ROWS * G * N);
+        double* C64 = widen(t.C, (size_t)ROWS * G * N);
+        if (oracle_ssu_packed_varlen(state0_64, state_ref, NSLOTS, H, P, N, G, ROWS, NSEQ, cu64, acc64,
+                                     tab64, STEPS, 1, tab64, STEPS, 1, STEPS, x64, dt64, 0, A64, B64,
+                                     C64, D64, z64, bias64, 1, -1, 0, NULL, out_ref) != 0) {
+            fprintf(stderr, "oracle_ssu_packed_varlen refused its arguments\n");
+            return 2;
+        }
+        failures += compare("packed", ROWS, state0, state_gpu, state_ref, t.out, out_ref, live);
+    }
+
+    CHECK_HIP(hipStreamDestroy(stream));
+    if (failures) return 1;
+    printf("c client ok\n");
+    return 0;
+}
