@@ -587,8 +587,7 @@ def summarize_ssd(prof_dir, workload, cmd):
              if "ssd" in r["Name"]]
     if not stats:
         raise SystemExit("no SSD kernels in the stats")
-    order = ["ssd_prep_kernel", "ssd_list_kernel", "ssd_bmm_kernel", "ssd_state_walk_kernel",
-             "ssd_scan_kernel"]
+    order = ["ssd_front_kernel", "ssd_state_walk_kernel", "ssd_scan_kernel"]
     short = lambda n: next((k for k in order if k in n), n)
 
     def counter(sub, name, pred):

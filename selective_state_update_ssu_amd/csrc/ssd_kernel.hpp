@@ -1,13 +1,14 @@
 // ssd_kernel.hpp -- SSD chunked prefill for gfx950 (CDNA4, wave64, MFMA).
 //
 // The prefill of a Mamba-2 layer over packed variable-length requests, cut into
-// chunks of at most Q tokens (semantics in include/ssd.h), as these launches:
+// chunks of at most Q tokens (semantics in include/ssd.h), as three launches:
 //
-//   prep      the chunk's descriptor; per (chunk, head) the clamped steps v_s,
-//             the running sums cum_s and the weights exp(cum_last - cum_s) v_s
-//   list      the requests whose last chunk is c, per chunk; the runs of chunks
+//   front     three independent parts in one launch:
+//     list    the requests whose last chunk is c, per chunk; the runs of chunks
 //             that continue one another, longest first           (one workgroup)
-//   bmm       CB[t, s] = C_t . B_s                                 per (chunk, group, tile)
+//     prep    the chunk's descriptor; per (chunk, head) the clamped steps v_s,
+//             the running sums cum_s and the weights exp(cum_last - cum_s) v_s
+//     bmm     CB[t, s] = C_t . B_s                                 per (chunk, group, tile)
 //   walk      S_c = exp(cum_last) S_{c-1} + sum_s w_s x_s B_s^T   per (run, head), in order
 //   scan      y_t = sum_{s<=t} CB[t, s] exp(cum_t - cum_s) v_s x_s
 //                   + exp(cum_t) C_t . S_{c-1} + D x_t, gated      per (chunk, head)
@@ -64,7 +65,7 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 // dtype codes of include/ssu.h.
 enum { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
-// Per chunk, written by the prep kernel for every later launch.
+// Per chunk, written by prep (in the front launch) for the later launches.
 struct ChunkDesc {
     int64_t lo;     // first token
     int32_t len;    // tokens; 0 for an empty chunk or a range that is not valid
@@ -236,7 +237,7 @@ __device__ __forceinline__ int64_t meta_uniform(const void* ptr, int is64, int64
 }
 
 // Chunk c's first token and length from the caller's cu_chunk_seqlens (read by
-// the prep kernel, which hands them on in the chunk descriptor); a range
+// prep, which hands them on in the chunk descriptor, and by bmm); a range
 // outside [0, tokens], running backwards or longer than Q counts as empty.
 struct Chunk {
     int64_t lo;
@@ -253,19 +254,20 @@ __device__ __forceinline__ Chunk chunk_of(const SsdParams& p, int64_t c) {
 
 // ------------------------------------------------------------ request list
 
-// One workgroup, after prep:
+// One workgroup of the front launch:
 //  - list_head[c] / list_next[b]: the requests b whose last chunk index is c, as
 //    a linked list per chunk (order unspecified; each b appears once), when final
 //    states are returned per request;
 //  - the runs: maximal ranges of chunks each continuing the one before (a run
-//    starts at every chunk that opens a request), as (first chunk, length) sorted
-//    by length, longest first (up to kSortRuns runs; more stay in chunk order),
-//    for the state walk.
-constexpr int kListThreads = 1024;
+//    starts at every chunk that opens a request: the first chunk, and every
+//    chunk whose seq_idx differs from the previous chunk's), as (first chunk,
+//    length) sorted by length, longest first (up to kSortRuns runs; more stay in
+//    chunk order), for the state walk.
+// It reads only the caller's metadata, so it needs nothing from prep.
+constexpr int kListThreads = kThreads;
 constexpr int kSortRuns = 2048;
 
-template <int kUnused = 0>
-__global__ __launch_bounds__(kListThreads) void ssd_list_kernel(const SsdParams p) {
+__device__ void list_body(const SsdParams& p) {
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     constexpr int NW = kListThreads / 64;
     if (!p.return_all && p.batch > 0) {
@@ -281,7 +283,9 @@ __global__ __launch_bounds__(kListThreads) void ssd_list_kernel(const SsdParams 
     int base = 0;
     for (int64_t c0 = 0; c0 < p.nchunks; c0 += kListThreads) {
         const int64_t c = c0 + tid;
-        const bool start = c < p.nchunks && p.desc[c].enter != kEnterCarry;
+        const bool start = c < p.nchunks &&
+                           (c == 0 || load_index(p.seq_idx, p.meta_i64, c) !=
+                                          load_index(p.seq_idx, p.meta_i64, c - 1));
         const unsigned long long m = __ballot(start);
         if (lane == 0) s_count[wave] = __popcll(m);
         __syncthreads();
@@ -340,18 +344,23 @@ __global__ __launch_bounds__(kListThreads) void ssd_list_kernel(const SsdParams 
 // step folded in, cum_s log2(e) - log2(v_s) (+inf for a zero step), and
 // cum_s log2(e), and
 // cum_last; zero steps and weights past the chunk's end. The wave of head 0
-// writes the chunk's descriptor. Lane l owns tokens l + 64 r.
-constexpr int kPrepThreads = 256;
+// writes the chunk's descriptor. Lane l owns tokens l + 64 r. Workgroup `id` of
+// `count` (chunk x groups of four heads).
+constexpr int kPrepThreads = kThreads;
+
+__host__ __device__ constexpr int64_t prep_blocks(int64_t nchunks, int64_t nheads) {
+    return nchunks * ((nheads + kPrepThreads / 64 - 1) / (kPrepThreads / 64));
+}
 
 template <int Q>
-__global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(const SsdParams p) {
+__device__ void prep_body(const SsdParams& p, int64_t id, int64_t count) {
     constexpr int R = Q / 64;
     constexpr int HW = kPrepThreads / 64;  // heads per workgroup
     constexpr float kLog2e = 1.4426950408889634f;
     const int H = p.nheads;
     const int hq = (H + HW - 1) / HW;
     // XCD-contiguous numbering: the workgroups of a chunk share its dt rows in one L2.
-    const int64_t wg = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t wg = xcd_order(id, count);
     const int64_t c = wg / hq;
     const int h = static_cast<int>(wg % hq) * HW + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int lane = threadIdx.x % 64;
@@ -422,23 +431,25 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(const SsdParams 
 // (s <= t needs no more): one wave per tile, 32x32x16 MFMA with both operands
 // straight from memory (eight consecutive dstate values per lane are
 // contiguous), every operand load issued before the first product. Rows past
-// the chunk's length read its last token and are never used.
+// the chunk's length read its last token and are never used. The chunk's token
+// range comes from the caller's cu_chunk_seqlens, so this needs nothing from
+// prep. Workgroup `id` of `count` (chunk x group x tile blocks).
 template <int Q> __host__ __device__ constexpr int bmm_tiles() { return (Q / 32) * (Q / 32 + 1) / 2; }
 template <int Q> __host__ __device__ constexpr int bmm_blocks() { return (bmm_tiles<Q>() + kWaves - 1) / kWaves; }
 
 template <typename IT, int N, int Q>
-__global__ __launch_bounds__(kThreads) void ssd_bmm_kernel(const SsdParams p) {
+__device__ void bmm_body(const SsdParams& p, int64_t id, int64_t count) {
     typedef typename Mfma<IT>::v8 v8;
     // XCD-contiguous numbering: the workgroups of a (chunk, group) share its C and
     // B rows in one L2.
-    const int64_t wg = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t wg = xcd_order(id, count);
     const int64_t cg = wg / bmm_blocks<Q>();
     const int tile = static_cast<int>(wg % bmm_blocks<Q>()) * kWaves +
                      __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     if (tile >= bmm_tiles<Q>()) return;
     const int64_t c = cg / p.ngroups;
     const int g = static_cast<int>(cg % p.ngroups);
-    const ChunkDesc d = load_desc(p, c);
+    const Chunk d = chunk_of<Q>(p, c);
     int ti = 0;
     while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
     const int sj = tile - ti * (ti + 1) / 2;
@@ -466,6 +477,41 @@ __global__ __launch_bounds__(kThreads) void ssd_bmm_kernel(const SsdParams p) {
         const int row = ti * 32 + 8 * (i / 4) + 4 * (lane / 32) + i % 4;
         out[row * Q + sj * 32 + lane % 32] = static_cast<CBT>(acc[i]);
     }
+}
+
+// ------------------------------------------------------------------ front
+
+// The three short stages before the state walk share one launch: none reads
+// what another writes (each derives chunk ranges and request openings from the
+// caller's metadata), and the walk and the scan, which read all three, come in
+// later launches. Workgroup ranges, each starting at a multiple of the XCD
+// count so that the XCD-contiguous numbering inside a range holds: the list
+// (first, so that its serial work starts at once; the other workgroups of its
+// range return at once), then prep, then the C B^T tiles.
+__host__ __device__ constexpr int64_t round_to_xcds(int64_t n) {
+    return (n + ssu::kXcds - 1) / ssu::kXcds * ssu::kXcds;
+}
+
+template <int Q>
+__host__ __device__ constexpr int64_t front_blocks(int64_t nchunks, int64_t nheads, int64_t ngroups) {
+    return ssu::kXcds + round_to_xcds(prep_blocks(nchunks, nheads)) + nchunks * ngroups * bmm_blocks<Q>();
+}
+
+template <typename IT, int N, int Q>
+__global__ __launch_bounds__(kThreads) void ssd_front_kernel(const SsdParams p) {
+    int64_t b = blockIdx.x;
+    if (b < ssu::kXcds) {
+        if (b == 0) list_body(p);
+        return;
+    }
+    b -= ssu::kXcds;
+    const int64_t np = prep_blocks(p.nchunks, p.nheads);
+    if (b < round_to_xcds(np)) {
+        if (b < np) prep_body<Q>(p, b, np);
+        return;
+    }
+    b -= round_to_xcds(np);
+    bmm_body<IT, N, Q>(p, b, p.nchunks * p.ngroups * bmm_blocks<Q>());
 }
 
 // ----------------------------------------------------------- LDS layout
@@ -1091,18 +1137,14 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
 
 namespace ssd {
 
-// The launches of one prefill, on `stream`: the request list (when final
-// states are gathered per request), prep, bmm, chunk state, passing, the
-// duplicate fix-up (with the list), scan. Dispatches on the state type and the
+// The launches of one prefill, on `stream`: the front (request list, prep and
+// C B^T), the state walk, the scan. Dispatches on the state type and the
 // (headdim, dstate, chunk) instance.
 template <typename IT, typename ST, int P, int N, int Q>
 hipError_t launch_instance(const SsdParams& p, hipStream_t stream) {
-    const int64_t prep_blocks = p.nchunks * ((p.nheads + kPrepThreads / 64 - 1) / (kPrepThreads / 64));
-    hipLaunchKernelGGL((ssd_prep_kernel<Q>), dim3(static_cast<unsigned>(prep_blocks)),
-                       dim3(kPrepThreads), 0, stream, p);
-    hipLaunchKernelGGL(ssd_list_kernel<0>, dim3(1), dim3(kListThreads), 0, stream, p);
-    hipLaunchKernelGGL((ssd_bmm_kernel<IT, N, Q>),
-                       dim3(static_cast<unsigned>(p.nchunks * p.ngroups * bmm_blocks<Q>())),
+    const int64_t front = front_blocks<Q>(p.nchunks, p.nheads, p.ngroups);
+    if (front > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((ssd_front_kernel<IT, N, Q>), dim3(static_cast<unsigned>(front)),
                        dim3(kThreads), 0, stream, p);
     // The walk runs as many workgroups as fit on the device at once (each loops
     // over work items), never more than there can be items.

@@ -5,7 +5,8 @@ Each translation unit is compiled to AMD assembly with the library's own flags
   - no scratch memory and no VGPR spills in any kernel;
   - every SSU update kernel moves the state with non-temporal vector loads and
     stores, reduces over dstate with DPP lane moves, and uses no matrix core;
-  - the SSD bmm, state-walk and scan kernels run on the matrix cores."""
+  - the SSD front (whose C B^T tiles are a product), state-walk and scan
+    kernels run on the matrix cores."""
 import os
 import re
 import subprocess
@@ -72,7 +73,7 @@ def test_ssu_kernels_stream_state_and_reduce_across_lanes(asm, unit):
 
 def test_ssd_products_on_matrix_cores(asm):
     ks = kernels(asm["ssd_kernels_bf16.hip"])
-    for kind in ("ssd_bmm_kernel", "ssd_state_walk_kernel", "ssd_scan_kernel"):
+    for kind in ("ssd_front_kernel", "ssd_state_walk_kernel", "ssd_scan_kernel"):
         bodies = [b for k, b in ks.items() if kind in k]
         assert bodies, kind
         for b in bodies:
