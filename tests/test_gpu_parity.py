@@ -380,7 +380,8 @@ def test_tied_parameter_views_bit_identical():
 @pytest.mark.parametrize("state_dtype,mode,rounds", [("bf16", "one_token", 10),
                                                       ("f16", "one_token", 10),
                                                       ("bf16", "packed", 7),
-                                                      ("f16", "packed", 10)])
+                                                      ("f16", "packed", 10),
+                                                      ("bf16", "packed_long", 10)])
 def test_stochastic_rounding(state_dtype, mode, rounds):
     """Stored 16-bit states equal the oracle's stochastic rounding with the same
     Philox words (up to rare threshold flips between the fp32 and fp64 states);
@@ -389,10 +390,13 @@ def test_stochastic_rounding(state_dtype, mode, rounds):
         w = wl.one_token("sr", 1001, batch=9, H=8, P=64, N=128, G=2, nslots=24, device=DEV,
                          state_dtype=state_dtype, io="bf16", pad_fraction=0.2,
                          dst_mode="distinct")
-    else:
+    elif mode == "packed":
         w = wl.packed("sr", 1002, nseq=7, max_len=4, H=4, P=64, N=64, G=1, nslots=40,
                       device=DEV, state_dtype=state_dtype, lengths=[3, 1, 4, 0, 2, 4, 1],
                       pad_fraction=0.15)
+    else:  # sequences past the eight-token operand stage; rows number the draws
+        w = wl.packed("srlong", 1004, nseq=4, max_len=19, H=4, P=64, N=128, G=1, nslots=90,
+                      device=DEV, state_dtype=state_dtype, lengths=[9, 2, 19, 16])
     w.rand_seed = torch.tensor([0x0123_4567_89AB_CDEF], dtype=torch.int64, device=DEV)
     w.philox_rounds = rounds
     out, after, before = hz.gpu_run(w)
