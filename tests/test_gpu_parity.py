@@ -441,3 +441,67 @@ def test_stochastic_rounding_is_unbiased_on_average():
     mean_err = (acc / 64 - exact[dst]).abs().mean().item()
     rne_err = (rne[dst].float() - exact[dst]).abs().mean().item()
     assert mean_err < 0.5 * rne_err, (mean_err, rne_err)
+
+
+# ------------------------------------------------------------- concurrency
+
+def test_threads_and_streams_match_a_single_thread():
+    """Two host threads, each on its own HIP stream (default priority), each
+    running a chain of in-place one-token and packed steps on a state cache of
+    its own: every result equals the same chain run on one thread, bit for
+    bit. The library keeps no state between calls (its error text is per
+    thread), so concurrent callers cannot disturb each other."""
+    import threading
+
+    steps = 6
+    works = [wl.one_token("conc1", 1101, batch=48, H=8, P=64, N=128, G=2, nslots=64,
+                          device=DEV, pad_fraction=0.1),
+             wl.packed("conc2", 1102, nseq=24, max_len=4, H=8, P=64, N=128, G=1,
+                       nslots=128, device=DEV, pad_fraction=0.1)]
+
+    import selective_state_update_ssu_amd as ssu
+
+    def chain(w, state, out, stream=None):
+        common = dict(D=w.D, z=w.z, dt_bias=w.dt_bias, dt_softplus=w.dt_softplus,
+                      pad_slot_id=w.pad_slot_id, stream=stream)
+        for _ in range(steps):
+            if w.mode == "one_token":
+                ssu.ssu_one_token(state, w.x, w.dt, w.A, w.B, w.C, out,
+                                  state_batch_indices=w.src, dst_state_batch_indices=w.dst,
+                                  **common)
+            else:
+                ssu.ssu_packed_varlen(state, w.x, w.dt, w.A, w.B, w.C, w.cu_seqlens, out,
+                                      num_accepted_tokens=w.num_accepted,
+                                      state_batch_indices=w.src_table,
+                                      dst_state_batch_indices=w.dst_table, **common)
+
+    ref = []
+    for w in works:
+        state, out = w.state.clone(), w.out_sentinel()
+        chain(w, state, out)
+        ref.append((state, out))
+    torch.cuda.synchronize()
+
+    got = [(w.state.clone(), w.out_sentinel()) for w in works]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in works]
+    errors = []
+
+    def run(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                chain(works[i], *got[i], stream=streams[i])
+            streams[i].synchronize()
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(works))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for (s_ref, o_ref), (s_got, o_got) in zip(ref, got):
+        assert torch.equal(hz.bits(s_ref), hz.bits(s_got))
+        assert torch.equal(hz.bits(o_ref), hz.bits(o_got))
