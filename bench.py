@@ -12,7 +12,9 @@ the launch's average duration from HIP events on the launch stream.
 
 --mode kernel times only the chosen workload (for profiler runs; an ssd_* name
 times the SSD chunked prefill); --mode copy times only the reference copy kernel
-used to calibrate traffic counters. The SSD prefill workloads are reported under
+used to calibrate traffic counters; --mode sweep times the one-token step over
+decode batch sizes (back to back and replayed from a HIP graph) and over dstate
+and state widths, one JSON line per point. The SSD prefill workloads are reported under
 "workloads" with their own oracle baseline.
 """
 from __future__ import annotations
@@ -40,7 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--mode", choices=["full", "kernel", "copy", "summarize"], default="full")
+    ap.add_argument("--mode", choices=["full", "kernel", "copy", "summarize", "sweep"],
+                    default="full")
     ap.add_argument("--prof-dir", help="summarize: directory holding the rocprofv3 passes")
     ap.add_argument("--prof-cmd", default="", help="summarize: the command lines that made them")
     ap.add_argument("--heads-per-block", type=int, default=0)
@@ -687,6 +690,64 @@ def run_workload(name, steps, warmup, hpb, lpl=0):
     return rec
 
 
+def sweep(steps, warmup):
+    """One-token calls of the Mamba2-2.7B head shape (80 heads x 64 rows, bf16 io
+    with gate, default launch shape): (1) fp32 state, dstate 128, batch 1 ..
+    1024, timed back to back and as `steps` calls captured in one HIP graph
+    (the graph shows the device time where the host bounds the eager rate);
+    (2) dstate 16 .. 256 with fp32 and bf16 state, batch chosen for ~1.35 GB
+    per call. Prints one JSON line per point."""
+    import statistics
+    import torch
+    from selective_state_update_ssu_amd import workloads as wl
+
+    def med(call):
+        return statistics.median(time_calls(call, steps, warmup)[1] * 1e3 for _ in range(3))
+
+    for batch in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
+        w = wl.one_token("sweep", 1, batch=batch, H=80, P=64, N=128, G=1, nslots=2 * batch,
+                         device="cuda", state_dtype="f32", io="bf16", with_z=True)
+        call = make_call(w, 0)
+        eager = med(call)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()  # warm the binding on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / steps)
+        nbytes = accounting(w)["bytes"]
+        replayed = statistics.median(ts)
+        print(json.dumps({"sweep": "batch", "batch": batch, "eager_us": eager,
+                          "graph_us": replayed, "graph_gbps": nbytes / replayed / 1e3}),
+              flush=True)
+        del graph, w, call
+        torch.cuda.empty_cache()
+    for sd, esz in (("f32", 4), ("bf16", 2)):
+        for N in (16, 32, 64, 128, 256):
+            batch = int(round(1.35e9 / (2 * 80 * 64 * N * esz)))
+            w = wl.one_token("sweep_ds", 7, batch=batch, H=80, P=64, N=N, G=1,
+                             nslots=2 * batch, device="cuda", state_dtype=sd, io="bf16",
+                             with_z=True)
+            t = med(make_call(w, 0))
+            print(json.dumps({"sweep": "dstate", "state": sd, "dstate": N, "batch": batch,
+                              "us": t, "gbps": accounting(w)["bytes"] / t / 1e3}), flush=True)
+            del w
+            torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.mode == "summarize":
@@ -712,6 +773,9 @@ def main():
     if args.mode == "copy":
         print(json.dumps({"ceilings_gbps": ceilings(steps=args.steps, kinds=("copy",)),
                           "bytes_each_way": 2 << 30}))
+        return
+    if args.mode == "sweep":
+        sweep(min(args.steps, 100), args.warmup)
         return
 
     if args.mode == "kernel" and args.workload.startswith("ssd_"):
