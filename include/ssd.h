@@ -32,8 +32,14 @@
  *     out[t, h, p] = y
  * The GPU computes it by chunks (intra-chunk products, and the state carried
  * from chunk to chunk along each request) on the matrix cores with 16-bit
- * operands and fp32 accumulation; results agree with the recurrence within the
- * rounding of those operands.
+ * operands and fp32 accumulation. x, B and C enter those products exactly; every
+ * derived operand (the decayed C B^T entries, the weighted x, the state handed
+ * from one chunk to the next) enters as a high and a low 16-bit part, so each
+ * product is accurate to about 2^-16 of itself and the results agree with the
+ * recurrence to within the final rounding of out and of the states (tolerances:
+ * 16-bit |err| <= 1e-2 + 2e-2 |ref|, fp32 states max |err| <= 1e-5 max(1,
+ * max |ref|)). With fp16 io the decayed C B^T entries and the states must stay
+ * within fp16's range.
  */
 #ifndef SSD_H
 #define SSD_H
@@ -89,7 +95,8 @@ typedef struct ssu_ssd_args {
 } ssu_ssd_args;
 
 /* Bytes of workspace ssu_ssd_prefill needs for these sizes: each chunk's
- * entering state in the io type, the per-chunk C B^T products, each chunk's
+ * entering state as high and low io-type parts, the per-chunk C B^T products
+ * (fp32), each chunk's
  * steps, running sums, weights and decay per head, the chunk descriptors, the
  * per-request list of last chunks and the runs of chunks that continue one
  * another. Linear in nchunks; no term grows with the number of tokens beyond

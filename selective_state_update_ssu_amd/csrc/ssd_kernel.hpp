@@ -19,12 +19,12 @@
 // running sums (an absolute error of about one ulp of |cum| log2(e) in the
 // exponent, far below the 16-bit rounding of the decayed entry for the
 // magnitudes a chunk reaches). The three contractions run on the matrix cores with 16-bit
-// operands and fp32 accumulation. The walk feeds w_s x_s as a high and a low
-// 16-bit part, which makes each product of a state accurate to about 2^-16
-// instead of 2^-8, and keeps the state in its fp32 accumulators from chunk to
-// chunk; the scan rounds its decayed C B^T entries once and uses x exactly.
-// Each chunk's entering state reaches the scan in the io type (its 16-bit MFMA
-// operand), written by the walk.
+// operands and fp32 accumulation. Every operand that is not an input (the
+// walk's w_s x_s, the scan's decayed C B^T entries and entering states) goes in
+// as a high and a low 16-bit part, which makes each product accurate to about
+// 2^-16 (bf16) or 2^-22 (fp16) instead of 2^-9 / 2^-12; x, B and C go in
+// exactly. The walk keeps the state in its fp32 accumulators from chunk to
+// chunk and hands each chunk's entering state to the scan as the two parts.
 //
 // Tiles are read through raw buffer descriptors whose range ends where the
 // chunk's rows end: the hardware returns zeros past the range, so rows past a
@@ -89,7 +89,8 @@ struct SsdParams {
     const void* init;     // [batch, H, P, N] state type, may be null
     void* out;            // [tokens, H, P] io
     void* states;         // [nchunks or batch, H, P, N] state type
-    void* s16;            // workspace [nchunks, H, P, N] io: each chunk's entering state
+    void* s16;            // workspace [nchunks, H, 2, P, N] io: each chunk's entering state
+                          // as high and low parts
     float* cb;            // workspace [nchunks, G, Q, Q]
     float* cumlast;       // workspace [nchunks, H]: each chunk's decay exponent
     ChunkDesc* desc;      // workspace [nchunks]
@@ -137,11 +138,21 @@ struct Mfma<_Float16> {
     }
 };
 
-// Storage of the per-chunk C B^T entries: bf16 when the io type is bf16 (the
-// scan rounds them to bf16 for the matrix cores anyway, after the decay), fp32
-// for fp16 io, whose finer rounding a bf16 copy would spoil.
-template <typename IT> struct CbStore { typedef float type; };
-template <> struct CbStore<__bf16> { typedef __bf16 type; };
+// A 16-bit operand of the matrix cores that stands for an fp32 value v is the
+// pair hi = io(v), lo = io(v - hi): the two products hi * b + lo * b, summed in
+// fp32, carry v to about 2^-16 (bf16) or 2^-22 (fp16) of itself instead of the
+// 2^-9 / 2^-12 of one rounding. The scan feeds its decayed C B^T entries and
+// the entering states this way, the walk its weighted x; x, B and C are exact
+// in the io type and go in whole. (The per-chunk C B^T entries are kept in
+// fp32 for the same reason.)
+template <typename IT>
+__device__ __forceinline__ void split16(float v, IT& hi, IT& lo) {
+    hi = static_cast<IT>(v);
+    lo = static_cast<IT>(v - static_cast<float>(hi));
+}
+// Each chunk's entering state reaches the scan as these two planes, [2][P][N]
+// per (chunk, head).
+constexpr int kEnterPlanes = 2;
 
 // 16-bit io value <-> bits <-> fp32.
 template <typename T>
@@ -189,6 +200,34 @@ __device__ __forceinline__ u16x8 bload_nt(Rsrc r, uint32_t off) {
 }
 __device__ __forceinline__ float bload_f32(Rsrc r, uint32_t off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Four consecutive state-type elements at byte offset `off` of a buffer
+// descriptor, as fp32 (one 16-byte load for fp32, one 8-byte load otherwise),
+// and back.
+template <typename ST>
+__device__ __forceinline__ f32x4 bload_state4(Rsrc r, uint32_t off) {
+    if constexpr (sizeof(ST) == 4) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    } else {
+        typedef ST st4 __attribute__((ext_vector_type(4)));
+        const st4 v = __builtin_bit_cast(st4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+        return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+                     static_cast<float>(v[3])};
+    }
+}
+template <typename ST>
+__device__ __forceinline__ void bstore_state4(Rsrc r, uint32_t off, f32x4 v) {
+    typedef ST st4 __attribute__((ext_vector_type(4)));
+    st4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = static_cast<ST>(v[i]);
+    if constexpr (sizeof(ST) == 4) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), r, off, 0, 0);
+    } else {
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), r, off, 0, 0);
+    }
 }
 
 // softplus(v) = max(v, 0) + log1p(exp(-|v|)) with the hardware exp2, log2 and
@@ -470,12 +509,11 @@ __device__ void bmm_body(const SsdParams& p, int64_t id, int64_t count) {
     f32x16 acc = {};
 #pragma unroll
     for (int k = 0; k < N / 16; ++k) acc = Mfma<IT>::mma32(ra[k], rb[k], acc);
-    typedef typename CbStore<IT>::type CBT;
-    CBT* out = reinterpret_cast<CBT*>(p.cb) + (c * p.ngroups + g) * Q * Q;
+    float* out = p.cb + (c * p.ngroups + g) * Q * Q;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int row = ti * 32 + 8 * (i / 4) + 4 * (lane / 32) + i % 4;
-        out[row * Q + sj * 32 + lane % 32] = static_cast<CBT>(acc[i]);
+        out[row * Q + sj * 32 + lane % 32] = acc[i];
     }
 }
 
@@ -533,10 +571,10 @@ __device__ __forceinline__ int swz(int r, int col) {
 // and headdim columns [32 (w % 2), +32) of S^T). A chunk's tokens are staged in
 // blocks of KB: B^T [N][KB] and the weighted x^T [P][KB] as high and low 16-bit
 // parts; the next block's operands are requested before the current block's
-// products. After each chunk the state leaves in the io type as the next
-// chunk's entering state, and in the state type where it is returned. The run's
-// entering state is the request's initial state (also handed to the scan in the
-// io type) or zeros. Workgroup i takes items i, i + grid, ...; the items come
+// products. After each chunk the state leaves as the next chunk's entering
+// state (high and low io-type planes, for the scan) and in the state type where
+// it is returned. The run's entering state is the request's initial state (also
+// handed to the scan as the two planes) or zeros. Workgroup i takes items i, i + grid, ...; the items come
 // longest run first, so the long walks start at once.
 constexpr int kWalkKB = 128;
 constexpr int kWalkPitch = kWalkKB + 8;
@@ -548,8 +586,6 @@ __host__ __device__ constexpr unsigned walk_lds_bytes(int P, int N) {
 template <typename IT, typename ST, int P, int N, int Q>
 __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_walk_kernel(const SsdParams p) {
     typedef typename Mfma<IT>::v8 v8;
-    typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
-    typedef ST st4 __attribute__((ext_vector_type(4)));
     constexpr int NT = walk_threads(N), NW = NT / 64;
     constexpr int KB = Q < kWalkKB ? Q : kWalkKB, XP = kWalkPitch;
     constexpr int NSB = Q / KB;                          // blocks per chunk
@@ -574,6 +610,8 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
     const uint32_t xrow = static_cast<uint32_t>(H * P * 2), brow = static_cast<uint32_t>(p.ngroups * N * 2);
     const int64_t tile = static_cast<int64_t>(H) * P * N;
     const bool lists = !p.return_all && p.batch > 0;
+    // First element of chunk c's entering state for head h (both planes).
+    auto enter_tile = [&](int64_t c, int h) { return (c * H + h) * (kEnterPlanes * P * N); };
 
     // Workgroups are dealt to the XCDs round robin, so with a grid of a multiple
     // of the XCD count each XCD always sees the same residue of item % XCDs.
@@ -598,9 +636,10 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
         const IT* xh = static_cast<const IT*>(p.x) + h * P;
         const IT* bg = static_cast<const IT*>(p.B) + g * N;
         const int64_t hs = static_cast<int64_t>(h) * P * N;
-        // Offset of this lane's four consecutive state elements of tile (nt, qt).
-        auto elem = [&](int nt, int qt) {
-            return hs + static_cast<int64_t>(q0 + 16 * qt + lane % 16) * N + n0 + 16 * nt + 4 * (lane / 16);
+        // Offset of this lane's four consecutive state elements of tile (nt, qt)
+        // inside the head's [P][N] block.
+        auto local = [&](int nt, int qt) {
+            return static_cast<uint32_t>((q0 + 16 * qt + lane % 16) * N + n0 + 16 * nt + 4 * (lane / 16));
         };
 
         // The operands of one block: x and B rows of tokens [s0, s0 + KB) of chunk c
@@ -610,13 +649,14 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
         auto fetch = [&](const ChunkDesc& d, int c, int s0) {
             const Rsrc xr = make_rsrc(xh + d.lo * H * P, d.len * xrow);
             const Rsrc br = make_rsrc(bg + d.lo * p.ngroups * N, d.len * brow);
+            const Rsrc wr = make_rsrc(p.w + (static_cast<int64_t>(c) * H + h) * Q, 4u * Q);
 #pragma unroll
             for (int i = 0; i < XPASS; ++i) {
                 const int idx = tid + NT * i, q = idx % XQ, s = s0 + 2 * (idx / XQ);
                 const uint32_t off = s * xrow + 16 * q;
                 rx[i][0] = bload_nt(xr, off);
                 rx[i][1] = bload_nt(xr, off + xrow);
-                rw[i] = *reinterpret_cast<const float2*>(p.w + (static_cast<int64_t>(c) * H + h) * Q + s);
+                rw[i] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(wr, 4u * s, 0, 0));
             }
 #pragma unroll
             for (int i = 0; i < BPASS; ++i) {
@@ -630,21 +670,14 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
         ChunkDesc d = load_desc(p, c0);
         fetch(d, c0, 0);
         f32x4 acc[2][2];
-        if (d.enter >= 0 && d.enter < p.batch) {
-            const int64_t base = static_cast<int64_t>(d.enter) * tile;
-            IT* const e16 = static_cast<IT*>(p.s16) + static_cast<int64_t>(c0) * tile;
+        const bool init = d.enter >= 0 && d.enter < p.batch;
+        if (init) {
+            const Rsrc ir = make_rsrc(static_cast<const ST*>(p.init) + d.enter * tile + hs,
+                                      P * N * sizeof(ST));
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
-                    u16x4 o;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[nt][qt][i] = load_state<ST>(p.init, base + elem(nt, qt) + i);
-                        o[i] = bits_of<IT>(acc[nt][qt][i]);
-                    }
-                    *reinterpret_cast<u16x4*>(e16 + elem(nt, qt)) = o;
-                }
+                for (int qt = 0; qt < 2; ++qt) acc[nt][qt] = bload_state4<ST>(ir, sizeof(ST) * local(nt, qt));
         } else {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
@@ -652,56 +685,62 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
                 for (int qt = 0; qt < 2; ++qt) acc[nt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        // A state tile [P][N] of type T to dst (row-major, this head's block of
-        // a state tile), through the B^T area of LDS so that every store writes
-        // whole 16-byte pieces of whole rows: each wave drops its part of S^T into
-        // LDS (16-byte chunks of row p permuted by p, which spreads the writes of
-        // sixteen rows over the banks), then the workgroup copies the rows out.
-        // The caller makes sure every wave is done with the B^T area; the next
-        // use of LDS is behind a barrier.
-        auto store_tile = [&](auto* dst) {
-            typedef typename std::remove_pointer<decltype(dst)>::type T;
-            typedef T t4 __attribute__((ext_vector_type(4)));
-            constexpr int CPR = N * static_cast<int>(sizeof(T)) / 16;  // 16-byte chunks per row
-            static_assert(P * N * sizeof(T) <= 2u * N * XP, "the tile fits the B^T area");
+        // The state as the next chunk's entering state: the high and the low
+        // planes [2][P][N] (io type) at dst, through the B^T area of LDS so that
+        // every store writes whole 16-byte pieces of whole rows: each wave drops
+        // its part of S^T into LDS (16-byte chunks of row p permuted by p, which
+        // spreads the writes of sixteen rows over the banks), then the workgroup
+        // copies the rows out. The caller makes sure every wave is done with the
+        // B^T area; the next use of LDS is behind a barrier.
+        auto store_enter = [&](IT* dst) {
+            typedef unsigned short t4 __attribute__((ext_vector_type(4)));
+            constexpr int CPR = N * 2 / 16;  // 16-byte chunks per row
+            constexpr unsigned PLANE = P * N * 2;
+            static_assert(kEnterPlanes * PLANE <= 2u * N * XP, "both planes fit the B^T area");
             unsigned char* lt = reinterpret_cast<unsigned char*>(bt);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
                     const int pr = q0 + 16 * qt + lane % 16, n = n0 + 16 * nt + 4 * (lane / 16);
-                    const int byte = n * static_cast<int>(sizeof(T));
+                    const int byte = n * 2;
+                    const unsigned o = pr * N * 2 + (((byte / 16) ^ (pr % CPR)) * 16) + byte % 16;
                     t4 v;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = static_cast<T>(acc[nt][qt][i]);
-                    *reinterpret_cast<t4*>(lt + pr * N * sizeof(T) + (((byte / 16) ^ (pr % CPR)) * 16) +
-                                           byte % 16) = v;
+                    for (int i = 0; i < 4; ++i) v[i] = bits_of<IT>(acc[nt][qt][i]);
+                    *reinterpret_cast<t4*>(lt + o) = v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = bits_of<IT>(acc[nt][qt][i] - f32_of<IT>(v[i]));
+                    *reinterpret_cast<t4*>(lt + PLANE + o) = v;
                 }
             lds_barrier();
-            constexpr int PIECES = P * CPR / NT;
+            constexpr int PIECES = P * CPR / NT;  // per plane
             static_assert(PIECES * NT == P * CPR, "whole pieces");
+            // One plane at a time, which bounds the registers the copy holds.
+#pragma unroll 1
+            for (int pl = 0; pl < kEnterPlanes; ++pl)
 #pragma unroll
-            for (int i = 0; i < PIECES; ++i) {
-                const int idx = tid + NT * i, pr = idx / CPR, ch = idx % CPR;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(lt + pr * N * sizeof(T) + ((ch ^ (pr % CPR)) * 16));
-                *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(dst + static_cast<int64_t>(pr) * N) +
-                                          ch * 16) = v;
-            }
+                for (int i = 0; i < PIECES; ++i) {
+                    const int idx = tid + NT * i, pr = idx / CPR, ch = idx % CPR;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(lt + pl * PLANE + pr * N * 2 +
+                                                                    ((ch ^ (pr % CPR)) * 16));
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(dst) + pl * PLANE + 16 * idx) = v;
+                }
         };
+        // The run's initial state is the first chunk's entering state too (LDS
+        // is free: the previous item ended with a barrier, and the first block
+        // stages behind one).
+        if (init) store_enter(static_cast<IT*>(p.s16) + enter_tile(c0, h));
+
         // The returned states, written from the accumulators directly (each
         // chunk's with return_intermediate_states, else only the requests'
         // last chunks').
         auto put = [&](int64_t row) {
-            ST* const dst = static_cast<ST*>(p.states) + row * tile;
+            const Rsrc sr = make_rsrc(static_cast<ST*>(p.states) + row * tile + hs, P * N * sizeof(ST));
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
-                    st4 v;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = static_cast<ST>(acc[nt][qt][i]);
-                    *reinterpret_cast<st4*>(dst + elem(nt, qt)) = v;
-                }
+                for (int qt = 0; qt < 2; ++qt) bstore_state4<ST>(sr, sizeof(ST) * local(nt, qt), acc[nt][qt]);
         };
 
         // Per-chunk scalars are requested a chunk ahead of their use.
@@ -716,6 +755,7 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
             const int rqn = lists ? ld_uniform(p.list_head + (more ? c + 1 : c)) : -1;
             const float decay = expf(cl);
             const int first_req = rq;
+
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
                 const int s0 = KB * sb;
@@ -785,11 +825,11 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
                         }
                 }
             }
-            // The state after chunk c: the next chunk's entering state (io type)
-            // if the run goes on, and the returned states (state type).
+            // The state after chunk c: the next chunk's entering state if the run
+            // goes on, and the returned states (state type).
             if (more) {
                 lds_barrier();  // every wave is done with this block's operands
-                store_tile(static_cast<IT*>(p.s16) + static_cast<int64_t>(c + 1) * tile + hs);
+                store_enter(static_cast<IT*>(p.s16) + enter_tile(c + 1, h));
             }
             if (p.return_all) {
                 put(c);
@@ -817,13 +857,21 @@ constexpr int scan_pitch(int Q) { return Q + 8; }       // (v x)^T row pitch, el
 constexpr int state_pitch(int N) { return N + 8; }      // entering-state row pitch
 
 // LDS bytes of the scan kernel: the decay exponents with the steps folded in
-// and the log2-scaled running sums (fp32), the skip coefficients, the entering state [P][N + 8] and x^T
-// [P][Q + 8], both in the io type.
+// and the log2-scaled running sums (fp32), the skip coefficients, the entering
+// state's two planes [2][P][N + 8] and x^T [P][Q + 8], all three in the io type.
 // The epilogue's fp32 scratch (16 rows per wave) then takes the x^T area and
 // what follows it.
 __host__ __device__ constexpr int scan_epilogue_pitch(int P) { return P + 4; }
+// Waves per SIMD the scan is compiled for (its register budget): four for
+// chunks of 256 (two 8-wave workgroups per CU, as many as its LDS allows at
+// dstate 128), three for chunks of 128 (three 4-wave workgroups at dstate 128;
+// its two tiles of C B^T in flight need more than 128 registers).
+__host__ __device__ constexpr int scan_waves_per_simd(int Q) { return Q >= 256 ? 4 : 3; }
+// Blocks of 32 C B^T columns each tile has in flight: one for chunks of 256
+// (within 128 registers), two for chunks of 128.
+__host__ __device__ constexpr int scan_cb_depth(int Q) { return Q >= 256 ? 1 : 2; }
 __host__ __device__ constexpr unsigned scan_lds_bytes(int P, int N, int Q) {
-    return 4u * Q + 4u * Q + 4u * P + 2u * P * state_pitch(N) +
+    return 4u * Q + 4u * Q + 4u * P + 2u * kEnterPlanes * P * state_pitch(N) +
            (2u * P * scan_pitch(Q) > 4u * 16 * scan_epilogue_pitch(P) * (scan_threads(Q) / 64)
                 ? 2u * P * scan_pitch(Q)
                 : 4u * 16 * scan_epilogue_pitch(P) * (scan_threads(Q) / 64));
@@ -836,7 +884,7 @@ __host__ __device__ constexpr unsigned scan_lds_bytes(int P, int N, int Q) {
 // tile, the entering state, the first C operands, D -- is issued at the start,
 // each product's next operands before its current matrix-core work.
 template <typename IT, typename ST, int P, int N, int Q>
-__global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdParams p) {
+__global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_scan_kernel(const SsdParams p) {
     typedef typename Mfma<IT>::v8 v8;
     constexpr int NT = scan_threads(Q), NW = NT / 64;
     constexpr int PT = P / 16, TT = 2, KN = N / 32;
@@ -863,8 +911,8 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
     float* cum2 = sl + Q;                          // [Q] cum_s log2(e)
     static_assert(NT == 2 * Q, "one value per thread");
     float* sd = cum2 + Q;  // [P] skip coefficients
-    unsigned short* sS = reinterpret_cast<unsigned short*>(sd + P);
-    unsigned short* xv = sS + P * SP;
+    unsigned short* sS = reinterpret_cast<unsigned short*>(sd + P);  // [2][P][SP]
+    unsigned short* xv = sS + kEnterPlanes * P * SP;
 
     const IT* Cp = static_cast<const IT*>(p.C);
     const uint32_t xrow = static_cast<uint32_t>(H * P * 2);
@@ -883,13 +931,16 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
         rx[r][0] = bload_nt(xr, off);
         rx[r][1] = bload_nt(xr, off + xrow);
     }
-    // The entering state (zeros for a chunk that opens a request without one).
+    // The entering state's two planes (zeros for a chunk that opens a request
+    // without one).
     const bool has_state = d.enter != kEnterZero;
-    const Rsrc sr = make_rsrc(static_cast<const IT*>(p.s16) + (c * H + h) * P * N,
-                              has_state ? P * N * 2 : 0);
-    u16x8 rs[SPASS];
+    const Rsrc sr = make_rsrc(static_cast<const IT*>(p.s16) + (c * H + h) * kEnterPlanes * P * N,
+                              has_state ? kEnterPlanes * P * N * 2 : 0);
+    u16x8 rs[kEnterPlanes][SPASS];
 #pragma unroll
-    for (int r = 0; r < SPASS; ++r) rs[r] = bload(sr, 16 * (tid + NT * r));
+    for (int pl = 0; pl < kEnterPlanes; ++pl)
+#pragma unroll
+        for (int r = 0; r < SPASS; ++r) rs[pl][r] = bload(sr, pl * P * N * 2 + 16 * (tid + NT * r));
     // C operands of the entering-state product, first k step.
     int trow[TT];
 #pragma unroll
@@ -913,7 +964,7 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
     // after the products inside the chunk.
     const int er = lane / 8, ec = (lane % 8) * (P / 8);
     static_assert(P / 8 == 8, "eight lanes per row, 16 bytes each");
-    constexpr int ZL = NW * TT * 2048 <= 2 * P * SP ? TT : 0;
+    constexpr int ZL = NW * TT * 2048 <= 2 * kEnterPlanes * P * SP ? TT : 0;
     const Rsrc zr = make_rsrc(p.z ? static_cast<const IT*>(p.z) + xoff : nullptr, p.z ? len * xrow : 0u);
     u16x8 ez[TT][2];
     auto z_load = [&](int k) {
@@ -939,10 +990,12 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
         }
     }
 #pragma unroll
-    for (int r = 0; r < SPASS; ++r) {
-        const int ci = tid + NT * r, pr = ci / (N / 8), n8 = 8 * (ci % (N / 8));
-        *reinterpret_cast<u16x8*>(sS + pr * SP + swz(pr, n8)) = rs[r];
-    }
+    for (int pl = 0; pl < kEnterPlanes; ++pl)
+#pragma unroll
+        for (int r = 0; r < SPASS; ++r) {
+            const int ci = tid + NT * r, pr = ci / (N / 8), n8 = 8 * (ci % (N / 8));
+            *reinterpret_cast<u16x8*>(sS + pl * P * SP + pr * SP + swz(pr, n8)) = rs[pl][r];
+        }
     lds_barrier();
 
     f32x4 acc[TT][PT];
@@ -954,7 +1007,7 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
 #pragma unroll
     for (int k = 0; k < TT; ++k) live[k] = 16 * (wave + NW * k) < len;
 
-    // ---- the entering state: C_t . S_in, then scaled by exp(cum_t)
+    // ---- the entering state: C_t . (S_hi + S_lo), then scaled by exp(cum_t)
     if (has_state) {
 #pragma unroll
         for (int ks = 0; ks < KN; ++ks) {
@@ -963,17 +1016,20 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
 #pragma unroll
                 for (int k = 0; k < TT; ++k) cn[k] = c_frag(k, 32 * (ks + 1));
             }
-            v8 sf[PT];
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const int pr = 16 * pt + lane % 16;
-                sf[pt] = *reinterpret_cast<const v8*>(sS + pr * SP + swz(pr, 32 * ks + kcol));
+            for (int pl = 0; pl < kEnterPlanes; ++pl) {
+                v8 sf[PT];
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const int pr = 16 * pt + lane % 16;
+                    sf[pt] = *reinterpret_cast<const v8*>(sS + pl * P * SP + pr * SP + swz(pr, 32 * ks + kcol));
+                }
+#pragma unroll
+                for (int k = 0; k < TT; ++k)
+                    if (live[k])
+#pragma unroll
+                        for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(cf[k], sf[pt], acc[k][pt]);
             }
-#pragma unroll
-            for (int k = 0; k < TT; ++k)
-                if (live[k])
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(cf[k], sf[pt], acc[k][pt]);
             if (ks + 1 < KN) {
 #pragma unroll
                 for (int k = 0; k < TT; ++k) cf[k] = cn[k];
@@ -1003,12 +1059,12 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
     // times x. Tile k needs the s blocks kk <= its last row; its C B^T entries
     // are requested two blocks ahead of their products (clamped to the chunk's
     // tile, so a block the tile turns out not to need is a harmless read).
-    typedef typename CbStore<IT>::type CBT;
-    const CBT* cbp = reinterpret_cast<const CBT*>(p.cb) + (c * p.ngroups + g) * Q * Q;
-    // Eight C B^T entries of one row: one 16-byte load for bf16, two for fp32.
-    constexpr int CW = sizeof(CBT) == 2 ? 1 : 2;
+    typedef float CBT;
+    const CBT* cbp = p.cb + (c * p.ngroups + g) * Q * Q;
+    // Eight fp32 C B^T entries of one row: two 16-byte loads.
+    constexpr int CW = 2;
     typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-    constexpr int DEPTH = 2;  // s blocks of C B^T in flight per tile
+    constexpr int DEPTH = scan_cb_depth(Q);  // s blocks of C B^T in flight per tile
     u32x4v cb[TT][DEPTH][CW];
     const Rsrc cbr = make_rsrc(cbp, Q * Q * sizeof(CBT));
     auto cb_load = [&](int k, int kk, int dd) {
@@ -1018,14 +1074,7 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
         for (int w = 0; w < CW; ++w)
             cb[k][dd][w] = __builtin_amdgcn_raw_buffer_load_b128(cbr, off + 16 * w, 0, 0);
     };
-    auto cb_value = [&](int k, int dd, int j) -> float {
-        if constexpr (CW == 1) {
-            const unsigned word = cb[k][dd][0][j / 2];
-            return __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
-        } else {
-            return __uint_as_float(cb[k][dd][j / 4][j % 4]);
-        }
-    };
+    auto cb_value = [&](int k, int dd, int j) -> float { return __uint_as_float(cb[k][dd][j / 4][j % 4]); };
     // Every step issues one load per (tile, slot) in the same order, whether or
     // not the tile needs the block, so the wait before each use stays a count of
     // the loads issued after it.
@@ -1056,7 +1105,7 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
                 if (live[k] && t0 + 15 >= kk) {
                     const int t = t0 + lane % 16;
                     const float ct = cum2[t];
-                    v8 a;
+                    v8 ah, al;  // the decayed entries' high and low parts
                     // Only the block that reaches the tile's rows needs the causal
                     // mask (s <= t); masked entries take exp2(-inf) = 0, a select.
                     // Rows past the chunk are computed from finite values and
@@ -1065,15 +1114,25 @@ __global__ __launch_bounds__(scan_threads(Q), 4) void ssd_scan_kernel(const SsdP
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
                             const float ex = col + j <= t ? ct - ls[j] : -__builtin_huge_valf();
-                            a[j] = static_cast<IT>(cb_value(k, dd, j) * __builtin_amdgcn_exp2f(ex));
+                            IT hi, lo;
+                            split16(cb_value(k, dd, j) * __builtin_amdgcn_exp2f(ex), hi, lo);
+                            ah[j] = hi;
+                            al[j] = lo;
                         }
                     } else {
 #pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            a[j] = static_cast<IT>(cb_value(k, dd, j) * __builtin_amdgcn_exp2f(ct - ls[j]));
+                        for (int j = 0; j < 8; ++j) {
+                            IT hi, lo;
+                            split16(cb_value(k, dd, j) * __builtin_amdgcn_exp2f(ct - ls[j]), hi, lo);
+                            ah[j] = hi;
+                            al[j] = lo;
+                        }
                     }
 #pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(a, xf[pt], acc[k][pt]);
+                    for (int pt = 0; pt < PT; ++pt) {
+                        acc[k][pt] = Mfma<IT>::mma16(ah, xf[pt], acc[k][pt]);
+                        acc[k][pt] = Mfma<IT>::mma16(al, xf[pt], acc[k][pt]);
+                    }
                 }
                 cb_load(k, kk + 32 * DEPTH, dd);  // in flight during the next blocks
             }

@@ -1,22 +1,22 @@
 """SSD prefill: the GPU call, the oracle on the same inputs, and the comparison.
 
-Tolerance, derived from the GPU's arithmetic (each product on the matrix cores
-takes 16-bit operands and accumulates in fp32):
-  out:    the scan rounds each operand of a product once to the io type (the
-          masked C B^T entry, v x, and the entering state), so each term is off
-          by at most ~2u of itself (u = 2^-8 for bf16, 2^-11 for fp16), plus the
-          final rounding of y (u |y|):
-              |gpu - ref| <= 3 u mag + u |ref| + 1e-5,
-          with mag = sum of |terms| -- the same recurrence run on |x|, |B|, |C|,
-          |D|, |initial state| (every decay and step is positive), times
-          |z sigmoid(z)|.
-  states: the state kernel feeds v x exp(.) as a high and a low 16-bit part
-          (error <= 2^-16 of the term for bf16, 2^-22 for fp16, whose subnormals
-          add at most 2^-25 |B| per term: under 4e-5 for a chunk of 256 tokens
-          with |B| < 5), accumulates in fp32 over the chunk and across chunks,
-          then rounds once to the state type (u_s |ref|):
-              |gpu - ref| <= 4 * 2^-16 mag_s + 1.01 u_s |ref| + atol,
-          atol = 4e-5 for fp16 io, 1e-6 for bf16 io.
+Tolerances (the bar the decode step is held to, applied unchanged):
+  16-bit results (out, and fp16/bf16 states): |gpu - ref| <= 1e-2 + 2e-2 |ref|
+      element by element;
+  fp32 states: max |gpu - ref| <= 1e-5 max(1, max |ref|) over the compared tensor.
+
+Beside the bar each check reports a diagnostic: the error against the size of
+the terms that make up each result, err / (2^-14 mag + u |ref|), where mag is
+the same recurrence run on |x|, |B|, |C|, |D|, |initial state| (every decay and
+step is positive) times |z sigmoid(z)|, and u the result type's spacing at 1
+(the final rounding). The matrix-core products take 16-bit operands and
+accumulate in fp32; x, B and C enter exactly and every derived operand (decayed
+C B^T entry, weighted x, entering state) as a high and a low 16-bit part, so a
+bf16 product is off by about 2^-16 of its terms and the diagnostic stays near or
+below one for bf16 io (an operand that lost its low part shows as a value of
+tens). With fp16 io the low parts of small values fall into fp16's subnormals,
+an absolute error of up to 2^-25 per term that the relative diagnostic does not
+model, so its values there are larger while the bar still holds.
 """
 from __future__ import annotations
 
@@ -69,29 +69,47 @@ def _report(err, tol, what):
                              f"(worst err/tol {ratio:.2f}); first at {idx.tolist()}")
 
 
+def bar_tolerance(ref, dtype):
+    """The tolerance array of the bar for results stored in `dtype`."""
+    if dtype == torch.float32:
+        return np.full(ref.shape, 1e-5 * max(1.0, float(np.max(np.abs(ref), initial=0.0))))
+    return 1e-2 + 2e-2 * np.abs(ref)
+
+
+def diagnostic(err, ref, mag, dtype):
+    """err / (2^-14 mag + u |ref| + 1e-30): the error against the terms' size."""
+    return float(np.max(err / (2.0 ** -14 * mag + UNIT[dtype] * np.abs(ref) + 1e-30),
+                        initial=0.0))
+
+
 def check_out(gpu_out, ref_out, mag_out, io_dtype, rows=None, what="out"):
+    """Every element of out within the bar; returns (worst err / bar, diagnostic)."""
     g = np64(gpu_out)
     if rows is not None:
         g, ref_out, mag_out = g[rows], ref_out[rows], mag_out[rows]
     assert np.all(np.isfinite(g)), f"{what}: non-finite values"
-    u = UNIT[io_dtype]
-    tol = 3 * u * mag_out + u * np.abs(ref_out) + 1e-5
-    _report(np.abs(g - ref_out), tol, what)
-    return float(np.max(np.abs(g - ref_out) / tol))
+    err = np.abs(g - ref_out)
+    tol = bar_tolerance(ref_out, io_dtype)
+    _report(err, tol, what)
+    return float(np.max(err / tol, initial=0.0)), diagnostic(err, ref_out, mag_out, io_dtype)
 
 
-def check_states(gpu_states, ref_states, mag_states, state_dtype, io_dtype, what="states"):
+def check_states(gpu_states, ref_states, mag_states, state_dtype, io_dtype=None, what="states"):
+    """Returned states within the bar of their type; returns (worst err / bar,
+    diagnostic)."""
     g = np64(gpu_states)
     assert g.shape == ref_states.shape, (what, g.shape, ref_states.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite values"
-    atol = 4e-5 if io_dtype == torch.float16 else 1e-6
-    tol = 4 * 2.0 ** -16 * mag_states + 1.01 * UNIT[state_dtype] * np.abs(ref_states) + atol
-    _report(np.abs(g - ref_states), tol, what)
-    return float(np.max(np.abs(g - ref_states) / tol))
+    err = np.abs(g - ref_states)
+    tol = bar_tolerance(ref_states, state_dtype)
+    _report(err, tol, what)
+    return (float(np.max(err / tol, initial=0.0)),
+            diagnostic(err, ref_states, mag_states, state_dtype))
 
 
 def check_all(w, gpu_out, gpu_states, ref, mag):
-    """Every row of out and every returned state."""
+    """Every row of out and every returned state; returns the (worst err / bar,
+    diagnostic) pairs of both."""
     r_out = check_out(gpu_out, ref.out, mag.out, w.x.dtype)
     if w.return_intermediate_states:
         r_st = check_states(gpu_states, ref.chunk_states, mag.chunk_states, w.state_dtype,

@@ -1,5 +1,8 @@
-"""SSD chunked prefill on the GPU against the fp64 oracle, element by element,
-within the tolerance derived in ssd_harness.py."""
+"""SSD chunked prefill on the GPU against the fp64 oracle, element by element:
+16-bit results within 1e-2 + 2e-2 |ref|, fp32 states within 1e-5 of their scale
+(ssd_harness.py)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -63,8 +66,9 @@ def test_small_cases(name):
     _, states = sh.run_gpu(w, out)
     torch.cuda.synchronize()
     ref, mag = sh.oracle_ref(w)
-    r_out, r_st = sh.check_all(w, out, states, ref, mag)
-    print(f"[ssd] {name}: worst err/tol out {r_out:.3f}, states {r_st:.3f}", flush=True)
+    (r_out, d_out), (r_st, d_st) = sh.check_all(w, out, states, ref, mag)
+    print(f"[ssd] {name}: worst err/bar out {r_out:.3f}, states {r_st:.3f} "
+          f"(diagnostic err/terms: out {d_out:.3f}, states {d_st:.3f})", flush=True)
 
 
 def test_last_chunk_indices_disagreeing_with_seq_idx():
@@ -105,29 +109,32 @@ def test_repeatable_bit_for_bit():
 
 
 @pytest.mark.parametrize("name", ["ssd_mamba2_2p7b", "ssd_nemotron_h"])
-def test_named_workload_sampled_requests(name):
-    """The full-size prefill, as the benchmark runs it; the oracle checks
-    requests cut out of it -- the shortest, the longest and one more -- on every
-    row and on four heads spread over the groups (rows and final states)."""
+def test_named_workload_every_request(name):
+    """The full-size prefill, as the benchmark runs it; every request is cut out
+    (all heads) and checked against the oracle on every row of out and on its
+    final state. The oracle runs the requests on parallel host threads."""
+    from concurrent.futures import ThreadPoolExecutor
     w = wl.SSD_NAMED[name](DEV)
     print(f"[ssd] {name}: tokens {w.x.shape[0]}, chunks {w.seq_idx.numel()}", flush=True)
     out = torch.full_like(w.x, float("nan"))
     _, states = sh.run_gpu(w, out)
     torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all() and torch.isfinite(states.float()).all()
-    lengths = w.meta["lengths"]
-    picks = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), len(lengths) // 2})
-    H = w.x.shape[1]
-    heads = [0, H // 3, (2 * H) // 3 + 1, H - 1]
-    for b in picks:
-        cut, (lo, hi), hs = sh.cut_request(w, b, heads)
-        ref, mag = sh.oracle_ref(cut)
-        r_out = sh.check_out(out[lo:hi][:, hs], ref.out, mag.out, w.x.dtype,
-                             what=f"out of request {b}")
-        r_st = sh.check_states(states[b:b + 1][:, hs], ref.final_states, mag.final_states,
-                               w.state_dtype, w.x.dtype, f"state of request {b}")
-        print(f"[ssd] {name} request {b} ({hi - lo} tokens): worst err/tol out {r_out:.3f}, "
-              f"state {r_st:.3f}", flush=True)
+    nreq = len(w.meta["lengths"])
+    cuts = [sh.cut_request(w, b) for b in range(nreq)]
+    orc = oracle.default()
+    with ThreadPoolExecutor(max_workers=min(16, nreq, os.cpu_count() or 1)) as ex:
+        refs = list(ex.map(lambda cut: sh.oracle_ref(cut[0], orc), cuts))
+    worst = [0.0, 0.0]
+    for b, ((cut, (lo, hi), hs), (ref, mag)) in enumerate(zip(cuts, refs)):
+        (r_out, d_out) = sh.check_out(out[lo:hi], ref.out, mag.out, w.x.dtype,
+                                      what=f"out of request {b}")
+        (r_st, d_st) = sh.check_states(states[b:b + 1], ref.final_states, mag.final_states,
+                                       w.state_dtype, w.x.dtype, f"state of request {b}")
+        worst = [max(worst[0], r_out), max(worst[1], r_st)]
+        print(f"[ssd] {name} request {b} ({hi - lo} tokens): worst err/bar out {r_out:.3f}, "
+              f"state {r_st:.3f} (diagnostic {d_out:.3f}, {d_st:.3f})", flush=True)
+    print(f"[ssd] {name}: {nreq} of {nreq} requests compared, all heads; worst err/bar "
+          f"out {worst[0]:.3f}, states {worst[1]:.3f}", flush=True)
 
 
 def test_empty_request_list_and_chunks():
