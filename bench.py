@@ -2,20 +2,26 @@
 """SSU decode throughput on one MI355X: tokens/s and achieved HBM GB/s.
 
 A step is one call of the update over one synthetic decode batch with every
-input already resident in HBM. The headline workload is the Mamba2-2.7B-shaped
-one-token batch (256 sequences, 80 heads x 64 x 128, fp32 state in 512 slots,
-bf16 x/B/C/z). The other named workloads are timed too and reported under
-"workloads". The roofline figure divides the algorithmic bytes of one launch by
-the launch's average duration from HIP events on the launch stream.
+input already resident in HBM. The headline workload is the largest decode
+configuration, the Nemotron-H-shaped one-token batch (512 sequences, 128 heads x
+64 x 128, 8 groups, fp32 state in 1024 slots, bf16 x/B/C/z). The other named
+workloads are timed too and reported under "workloads", each with its own
+roofline block. The roofline figure divides the algorithmic bytes of one launch
+by the launch's average duration from HIP events on the launch stream.
+
+No timed point can be served from the 256 MB Infinity Cache: a workload whose
+call touches less than 1 GiB of state cycles through enough copies of its state
+cache that at least 1 GiB of state lies between two uses of one copy.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode full|kernel|copy]
 
 --mode kernel times only the chosen workload (for profiler runs; an ssd_* name
-times the SSD chunked prefill); --mode copy times only the reference copy kernel
-used to calibrate traffic counters; --mode sweep times the one-token step over
-decode batch sizes (back to back and replayed from a HIP graph) and over dstate
-and state widths, one JSON line per point. The SSD prefill workloads are reported under
-"workloads" with their own oracle baseline.
+times the SSD chunked prefill; --record PATH writes its JSON record there);
+--mode copy times only the reference copy kernel used to calibrate traffic
+counters; --mode sweep times the one-token step over decode batch sizes (back to
+back and replayed from a HIP graph) and over dstate and state widths, one JSON
+line per point. The SSD prefill workloads are reported under "workloads" with
+their own oracle baseline.
 """
 from __future__ import annotations
 
@@ -32,7 +38,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSU tokens/sec and achieved HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-HEADLINE = "mamba2_2p7b"
+HEADLINE = "nemotron_h"
+# Bytes of state that must lie between two uses of one state copy (4x the
+# 256 MB Infinity Cache).
+MIN_TOUCH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -51,6 +60,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=6.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--record", help="kernel mode: also write the JSON record to this file")
     return ap.parse_args()
 
 
@@ -135,11 +145,11 @@ def accounting(w):
 
 # ---------------------------------------------------------------------- timing
 
-def make_call(w, hpb, lpl=0, order=0):
+def make_call(w, hpb, lpl=0, order=0, state=None):
     import torch
     import selective_state_update_ssu_amd as ssu
 
-    state = w.state
+    state = w.state if state is None else state
     out = torch.empty_like(w.x)
     common = dict(D=w.D, z=w.z, dt_bias=w.dt_bias, dt_softplus=w.dt_softplus,
                   pad_slot_id=w.pad_slot_id, disable_state_update=w.disable_state_update,
@@ -165,23 +175,39 @@ def make_call(w, hpb, lpl=0, order=0):
 
 
 def time_calls(call, steps, warmup):
-    """Warm up, then time exactly `steps` calls. Returns (wall ms per step,
-    event ms per launch on the launch stream)."""
+    """Warm up, then time exactly `steps` calls. `call` is one callable or a list
+    cycled through (call i runs calls[i % len]). Returns (wall ms per step, event
+    ms per launch on the launch stream)."""
     import torch
 
-    for _ in range(warmup):
-        call()
+    calls = call if isinstance(call, (list, tuple)) else [call]
+    for i in range(warmup):
+        calls[i % len(calls)]()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
-    for _ in range(steps):
-        call()
+    for i in range(steps):
+        calls[i % len(calls)]()
     end.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / steps, start.elapsed_time(end) / steps
+
+
+def state_copies(acc):
+    """Copies of the state cache to cycle through so that at least
+    MIN_TOUCH_BYTES of state lie between two uses of one copy."""
+    touched = acc["state_read_bytes"] + acc["state_write_bytes"]
+    return max(1, -(-MIN_TOUCH_BYTES // max(touched, 1)))
+
+
+def rotated_calls(w, hpb, lpl=0, copies=1):
+    """`copies` calls of the workload, each on its own copy of the state cache
+    (the first on w.state itself)."""
+    states = [w.state] + [w.state.clone() for _ in range(copies - 1)]
+    return [make_call(w, hpb, lpl, state=st) for st in states]
 
 
 def stream_library():
@@ -292,69 +318,119 @@ def ring_tracker_times(steps=200):
 
 # ------------------------------------------------------------------ CPU leg
 
-def cpu_baseline(seconds):
-    """The fp64 oracle on the headline workload's sequences, on the host cores:
-    first one thread on the first 16 sequences (their rows and slots), then one
-    thread per core (at most 16) on disjoint 16-sequence slices, each repeating
-    its calls for about `seconds`. The oracle releases the interpreter lock
-    inside its C calls, so the threads run in parallel; nothing in the oracle
-    changes. `value` is the all-cores rate; the single-thread rate is reported
-    beside it."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_threads():
+    """Host threads for the CPU leg: every CPU this process may run on, capped by
+    OMP_NUM_THREADS when the environment sets it (a GPU machine grants each GPU's
+    jobs a share of its host, and says so there)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(cap))) if cap.isdigit() and int(cap) > 0 else max(1, n)
+
+
+def cpu_baseline(seconds, name=HEADLINE, nseq=32, block=32):
+    """The fp64 oracle on a bounded sample of the headline workload -- its first
+    `nseq` sequences, from the same draw the GPU timed, copied to the host -- split
+    into independent (block of `block` sequences, head) tasks, each an oracle call
+    on that head's state rows, x, dt, z and its group's B and C. First one thread
+    runs the tasks in turn for about `seconds`, then one thread per available core
+    does (each thread its own tasks, round robin); the oracle releases the
+    interpreter lock inside its C calls, so they run in parallel and nothing in
+    the oracle changes. Rates are tokens/s: (sequence, head) units done / heads /
+    wall time."""
     import threading
     import numpy as np
+    import torch
     import oracle
     from selective_state_update_ssu_amd import workloads as wl
 
-    w = wl.mamba2_2p7b("cpu")
-    nseq = 16
-
-    def sample(first):
-        src = w.src[first:first + nseq].long().numpy()
-        used = sorted(set(src.tolist()))
-        remap = {s: i for i, s in enumerate(used)}
-        r = slice(first, first + nseq)
-        sub = dict(
-            state=w.state[torch_index(used)].double().numpy(),
-            x=w.x[r].double().numpy(), dt=w.dt[r].double().numpy(),
-            A=w.A.double().numpy(), B=w.B[r].double().numpy(), C=w.C[r].double().numpy(),
-            D=w.D.double().numpy(), z=w.z[r].double().numpy(),
-            dt_bias=w.dt_bias.double().numpy())
-        return sub, np.array([remap[v] for v in src])
-
+    w = wl.NAMED[name]("cuda")
+    nslots, H, P, N, G = w.dims
+    hpg = H // G
+    src_all = w.src.long().cpu().numpy()
+    src = src_all[:nseq]
+    used = sorted(set(int(v) for v in src))
+    remap = {v: i for i, v in enumerate(used)}
+    f64 = lambda t: t.detach().double().cpu().numpy()
+    state = f64(w.state[torch.as_tensor(used, device=w.state.device)])  # [slots, H, P, N]
+    x, dt, z = f64(w.x[:nseq]), f64(w.dt[:nseq]), f64(w.z[:nseq]) if w.z is not None else None
+    B, C = f64(w.B[:nseq]), f64(w.C[:nseq])
+    A, D, bias = f64(w.A), f64(w.D), f64(w.dt_bias)
+    del w
+    torch.cuda.empty_cache()
+    tasks = []
+    for b0 in range(0, nseq, block):
+        r = slice(b0, b0 + block)
+        s_loc = np.array([remap[int(v)] for v in src[r]])
+        rows = sorted(set(s_loc.tolist()))
+        rmap = {v: i for i, v in enumerate(rows)}
+        sl = np.array([rmap[v] for v in s_loc])
+        for h in range(H):
+            g = h // hpg
+            tasks.append(dict(
+                state=np.ascontiguousarray(state[rows][:, h:h + 1]),
+                x=np.ascontiguousarray(x[r, h:h + 1]), dt=np.ascontiguousarray(dt[r, h:h + 1]),
+                A=A[h:h + 1], B=np.ascontiguousarray(B[r, g:g + 1]),
+                C=np.ascontiguousarray(C[r, g:g + 1]), D=D[h:h + 1],
+                z=None if z is None else np.ascontiguousarray(z[r, h:h + 1]),
+                dt_bias=bias[h:h + 1], src=sl, units=len(sl)))
     orc = oracle.default()
 
-    def run(sub, s, out, i):
-        calls = 0
+    def run(mine, out, i):
+        units = 0
         t0 = time.perf_counter()
+        k = 0
         while True:
-            orc.one_token(sub["state"], sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"],
-                          D=sub["D"], z=sub["z"], dt_bias=sub["dt_bias"], dt_softplus=True,
-                          src=s, dst=s)
-            calls += 1
+            t = mine[k % len(mine)]
+            orc.one_token(t["state"], t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"],
+                          z=t["z"], dt_bias=t["dt_bias"], dt_softplus=True, src=t["src"],
+                          dst=t["src"])
+            units += t["units"]
+            k += 1
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
-        out[i] = (calls, el)
+        out[i] = (units, el)
 
     one = [None]
-    run(*sample(0), one, 0)
-    single = nseq * one[0][0] / one[0][1]
-    threads = max(1, min(16, os.cpu_count() or 1, w.x.shape[0] // nseq))
+    run(tasks, one, 0)
+    single = one[0][0] / H / one[0][1]
+    threads = min(cpu_threads(), len(tasks))
     res = [None] * threads
-    samples = [sample(i * nseq) for i in range(threads)]
-    ts = [threading.Thread(target=run, args=(*samples[i], res, i)) for i in range(threads)]
+    ts = [threading.Thread(target=run, args=(tasks[i::threads], res, i)) for i in range(threads)]
     t0 = time.perf_counter()
     for t in ts:
         t.start()
     for t in ts:
         t.join()
     wall = time.perf_counter() - t0
-    total = sum(nseq * c for c, _ in res)
-    return {"value": total / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "single_thread_value": single,
-            "sample": f"{threads} threads, each on its own 16 of the 256 sequences of "
-                      f"{HEADLINE} (all 80 heads, their slots), fp64, {total} tokens in "
-                      f"{wall:.1f} s; one thread on the first 16: {single:.0f} tokens/s"}
+    units = sum(u for u, _ in res)
+    try:
+        available = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        available = os.cpu_count()
+    return {"value": units / H / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": single, "host_cpus": os.cpu_count(),
+            "available_cpus": available, "cpu_model": cpu_model(),
+            "sample": f"the first {nseq} of the {name} batch's {len(src_all)} sequences (same draw as the "
+                      f"GPU run; {H} heads, their slots), as {len(tasks)} ({block}-sequence block, "
+                      f"head) oracle calls in fp64; {threads} threads for {wall:.1f} s did "
+                      f"{units} (sequence, head) units = {units / H:.0f} tokens; one thread: "
+                      f"{single:.0f} tokens/s"}
 
 
 def torch_index(idx):
@@ -668,17 +744,33 @@ def describe(w):
     return d
 
 
+def roofline_block(name, acc, kernel_us):
+    gbps = acc["bytes"] / (kernel_us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic_for(name, kernel_us * 1e-3),
+            "algorithmic_bytes": acc["bytes"], "kernel_us": kernel_us}
+
+
 def run_workload(name, steps, warmup, hpb, lpl=0):
     import torch
     from selective_state_update_ssu_amd import workloads as wl
 
     w = wl.NAMED[name]("cuda")
     acc = accounting(w)
-    wall, ev = time_calls(make_call(w, hpb, lpl), steps, warmup)
+    copies = state_copies(acc)
+    cache_resident = copies > 64
+    if cache_resident:
+        # A launch-bound call whose state is a few hundred KB: it stays in the
+        # caches whatever we do; its figure is not an HBM one.
+        copies = 1
+    wall, ev = time_calls(rotated_calls(w, hpb, lpl, copies), steps, warmup)
     rec = dict(config=describe(w), ms_per_step=wall, kernel_us=ev * 1e3,
                tokens_per_s=acc["live_rows"] / (wall * 1e-3),
-               hbm_gbps=acc["bytes"] / (ev * 1e-3) / 1e9, **acc)
+               hbm_gbps=acc["bytes"] / (ev * 1e-3) / 1e9, state_copies=copies, **acc)
     rec["frac_of_peak"] = rec["hbm_gbps"] / HBM_PEAK_GBPS
+    rec["roofline"] = roofline_block(name, acc, rec["kernel_us"])
+    if cache_resident:
+        rec["cache_resident"] = True
     pattern_us = pattern_ceiling(w, steps, warmup)
     if pattern_us is not None:
         # The same state reads and writes with no arithmetic: how close the
@@ -707,18 +799,24 @@ def sweep(steps, warmup):
     for batch in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
         w = wl.one_token("sweep", 1, batch=batch, H=80, P=64, N=128, G=1, nslots=2 * batch,
                          device="cuda", state_dtype="f32", io="bf16", with_z=True)
-        call = make_call(w, 0)
-        eager = med(call)
+        acc = accounting(w)
+        # Small batches cycle through copies of the state cache (at least 1 GiB of
+        # state between two uses of one copy), and a graph holds one call per copy,
+        # so neither figure is served from the Infinity Cache.
+        copies = state_copies(acc)
+        calls = rotated_calls(w, 0, copies=copies)
+        eager = med(calls)
+        length = max(steps, copies)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            call()  # warm the binding on the capture stream
+            calls[0]()  # warm the binding on the capture stream
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for _ in range(steps):
-                call()
+            for i in range(length):
+                calls[i % copies]()
         torch.cuda.synchronize()
         ts = []
         for _ in range(3):
@@ -727,13 +825,13 @@ def sweep(steps, warmup):
             graph.replay()
             e1.record()
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3 / steps)
-        nbytes = accounting(w)["bytes"]
+            ts.append(e0.elapsed_time(e1) * 1e3 / length)
+        nbytes = acc["bytes"]
         replayed = statistics.median(ts)
-        print(json.dumps({"sweep": "batch", "batch": batch, "eager_us": eager,
-                          "graph_us": replayed, "graph_gbps": nbytes / replayed / 1e3}),
-              flush=True)
-        del graph, w, call
+        print(json.dumps({"sweep": "batch", "batch": batch, "state_copies": copies,
+                          "eager_us": eager, "graph_us": replayed,
+                          "graph_gbps": nbytes / replayed / 1e3}), flush=True)
+        del graph, w, calls
         torch.cuda.empty_cache()
     for sd, esz in (("f32", 4), ("bf16", 2)):
         for N in (16, 32, 64, 128, 256):
@@ -741,9 +839,10 @@ def sweep(steps, warmup):
             w = wl.one_token("sweep_ds", 7, batch=batch, H=80, P=64, N=N, G=1,
                              nslots=2 * batch, device="cuda", state_dtype=sd, io="bf16",
                              with_z=True)
-            t = med(make_call(w, 0))
+            acc = accounting(w)
+            t = med(rotated_calls(w, 0, copies=state_copies(acc)))
             print(json.dumps({"sweep": "dstate", "state": sd, "dstate": N, "batch": batch,
-                              "us": t, "gbps": accounting(w)["bytes"] / t / 1e3}), flush=True)
+                              "us": t, "gbps": acc["bytes"] / t / 1e3}), flush=True)
             del w
             torch.cuda.empty_cache()
 
@@ -778,10 +877,16 @@ def main():
         sweep(min(args.steps, 100), args.warmup)
         return
 
+    def record(rec):
+        if args.record:
+            with open(args.record, "w") as f:
+                json.dump(rec, f)
+
     if args.mode == "kernel" and args.workload.startswith("ssd_"):
         rec = run_ssd_workload(args.workload, args.steps, args.warmup)
         print(f"[bench] {args.workload}: {rec['us_per_prefill']:.1f} us/prefill",
               file=sys.stderr, flush=True)
+        record(rec)
         print(json.dumps(rec))
         return
     head = run_workload(args.workload, args.steps, args.warmup, args.heads_per_block,
@@ -790,19 +895,21 @@ def main():
           f"{head['hbm_gbps']:.0f} GB/s, {head['tokens_per_s'] / 1e6:.3f} M tokens/s",
           file=sys.stderr, flush=True)
     if args.mode == "kernel":
+        record(head)
         print(json.dumps(head))
         return
 
     extra = {}
     if not args.no_extra:
-        for name in ("tiny", "bf16_state", "bf16_state_sr", "nemotron_h", "nemotron_h_readonly",
-                     "packed_mtp", "dense_mtp"):
+        for name in ("mamba2_2p7b", "tiny", "bf16_state", "bf16_state_sr", "nemotron_h",
+                     "nemotron_h_readonly", "packed_mtp", "dense_mtp"):
             if name == args.workload:
                 continue
             rec = run_workload(name, max(20, args.steps // 2), max(5, args.warmup // 2),
                                args.heads_per_block, args.loads_per_lane)
             extra[name] = {k: rec[k] for k in ("tokens_per_s", "hbm_gbps", "frac_of_peak",
                                                "kernel_us", "ms_per_step", "bytes", "live_rows",
+                                               "state_copies", "cache_resident", "roofline",
                                                "state_traffic_only_us",
                                                "frac_of_state_traffic_only") if k in rec}
             print(f"[bench] {name}: {rec['kernel_us']:.1f} us/launch, {rec['hbm_gbps']:.0f} GB/s",
@@ -821,9 +928,8 @@ def main():
     copy_gbps = ceil["copy"]
     rings = ring_tracker_times()
     print(f"[bench] ring trackers: {json.dumps(rings)}", file=sys.stderr, flush=True)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, args.workload)
 
-    kernel_ms = head["kernel_us"] * 1e-3
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -843,16 +949,8 @@ def main():
         "copy_gbps": copy_gbps,
         "frac_of_copy": head["hbm_gbps"] / copy_gbps,
         "stream_ceilings_gbps": ceil,
-        "roofline": {
-            "bound": "hbm",
-            "achieved": head["hbm_gbps"],
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": head["frac_of_peak"],
-            "traffic": traffic_for(args.workload, kernel_ms),
-            "algorithmic_bytes": head["bytes"],
-            "kernel_us": head["kernel_us"],
-        },
+        "state_copies": head["state_copies"],
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "workloads": extra,
         "ring_trackers": rings,

@@ -55,11 +55,16 @@
  * element is rounded stochastically instead of to nearest: with q the spacing of
  * the state format at |v|, m = floor(|v| / q) and frac = |v| / q - m, the stored
  * magnitude is (m + 1) q when U >= 1 - frac and m q otherwise (infinite past the
- * largest finite value), U being a uniform number of 16 (bf16) or 24 (fp16) bits
- * taken from the top of a random word. Element e = (h * headdim + p) * dstate + n
- * of the state written by packed row r (row b for ssu_one_token) uses word e % 4
- * of Philox4x32 (Salmon et al., SC'11) with philox_rounds rounds, counter
- * (e / 4, r mod 2^32, r / 2^32, 0) and key (seed mod 2^32, seed / 2^32). The vLLM
+ * largest finite value), U being a uniform number of 16 (bf16) or 24 (fp16)
+ * random bits divided by 2^16 or 2^24. The bits come from Philox4x32 (Salmon et
+ * al., SC'11) with philox_rounds rounds, key (seed mod 2^32, seed / 2^32) and a
+ * counter per group of elements. Element e = (h * headdim + p) * dstate + n of
+ * the state written by packed row r (row b for ssu_one_token) takes:
+ *   fp16: counter (e / 4, r mod 2^32, r / 2^32, 0); word w = e % 4 of the
+ *         output; the top 24 bits of that word;
+ *   bf16: counter (e / 8, r mod 2^32, r / 2^32, 0); word w = (e % 8) / 2 of the
+ *         output; its low 16 bits for even e, its high 16 bits for odd e.
+ * (Words are numbered 0..3 in the order Philox returns them.) The vLLM
  * dispatch page forwards exactly these two knobs (a device seed and a round count,
  * 10 by default) when stochastic rounding is enabled; the rule and the counter
  * layout are this library's. `out` is always rounded to nearest.

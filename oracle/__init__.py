@@ -38,7 +38,7 @@ def build(source: str = SOURCE, output: str = LIBRARY) -> str:
 
 class _Rounding(ctypes.Structure):
     _fields_ = [("sr_format", ctypes.c_int), ("rand_seed", ctypes.c_uint64),
-                ("philox_rounds", ctypes.c_int)]
+                ("philox_rounds", ctypes.c_int), ("row_base", ctypes.c_int64)]
 
 
 SR_FORMATS = {None: 0, "f16": 1, "bf16": 2}
@@ -126,11 +126,11 @@ class Oracle:
                 _f64(z), _f64(dt_bias), out, rows)
 
     @staticmethod
-    def _rounding(sr_format, rand_seed, philox_rounds):
+    def _rounding(sr_format, rand_seed, philox_rounds, row_base=0):
         if sr_format is None:
             return None
         return ctypes.byref(_Rounding(SR_FORMATS[sr_format], int(rand_seed) & (2**64 - 1),
-                                      int(philox_rounds)))
+                                      int(philox_rounds), int(row_base)))
 
     def philox4x32(self, counter, key, rounds=10):
         """The four output words of Philox4x32 for one counter and key."""
@@ -153,8 +153,10 @@ class Oracle:
     def one_token(self, state, x, dt, A, B, C, *, D=None, z=None, dt_bias=None,
                   dt_softplus=False, src=None, dst=None, pad_slot_id=-1,
                   disable_state_update=False, out_init=None, sr_format=None, rand_seed=0,
-                  philox_rounds=10) -> Result:
-        """One token per sequence: row b of x/dt/B/C/z/out is sequence b."""
+                  philox_rounds=10, sr_row_base=0) -> Result:
+        """One token per sequence: row b of x/dt/B/C/z/out is sequence b.
+        sr_row_base: the call-wide row number of row 0, for the stochastic
+        rounding's counters when this problem is cut out of a larger call."""
         (state, x, dt, dt_per_dim, A, B, C, D, z, dt_bias, out,
          batch) = self._common(state, x, dt, A, B, C, D, z, dt_bias, out_init)
         nslots, H, P, N = state.shape
@@ -166,7 +168,7 @@ class Oracle:
             _p(x, _dp), _p(dt, _dp), dt_per_dim, _p(A, _dp), _p(B, _dp), _p(C, _dp),
             _p(D, _dp), _p(z, _dp), _p(dt_bias, _dp), int(bool(dt_softplus)),
             _p(src, _ip), _p(dst, _ip), int(pad_slot_id), int(bool(disable_state_update)),
-            self._rounding(sr_format, rand_seed, philox_rounds), _p(out, _dp))
+            self._rounding(sr_format, rand_seed, philox_rounds, sr_row_base), _p(out, _dp))
         if rc != 0:
             raise ValueError("oracle_ssu_one_token rejected its arguments")
         return Result(out, state_out)
@@ -175,7 +177,7 @@ class Oracle:
                       src_table=None, src_strides=None, dst_table=None, dst_strides=None,
                       steps=None, D=None, z=None, dt_bias=None, dt_softplus=False,
                       pad_slot_id=-1, disable_state_update=False, out_init=None,
-                      sr_format=None, rand_seed=0, philox_rounds=10) -> Result:
+                      sr_format=None, rand_seed=0, philox_rounds=10, sr_row_base=0) -> Result:
         """Packed varlen form. A 2-D table [nseq, steps] takes strides (steps, 1)
         unless strides are given; a flat table needs explicit strides and steps."""
         (state, x, dt, dt_per_dim, A, B, C, D, z, dt_bias, out,
@@ -208,7 +210,7 @@ class Oracle:
             int(steps), _p(x, _dp), _p(dt, _dp), dt_per_dim, _p(A, _dp), _p(B, _dp),
             _p(C, _dp), _p(D, _dp), _p(z, _dp), _p(dt_bias, _dp), int(bool(dt_softplus)),
             int(pad_slot_id), int(bool(disable_state_update)),
-            self._rounding(sr_format, rand_seed, philox_rounds), _p(out, _dp))
+            self._rounding(sr_format, rand_seed, philox_rounds, sr_row_base), _p(out, _dp))
         if rc != 0:
             raise ValueError("oracle_ssu_packed_varlen rejected its arguments")
         return Result(out, state_out)

@@ -162,6 +162,7 @@ static void store_state(double *dst, const double *s, int64_t elems, int64_t row
     }
     const uint32_t key[2] = {(uint32_t)rd->rand_seed, (uint32_t)(rd->rand_seed >> 32)};
     const int bf16 = rd->sr_format == 2;
+    row += rd->row_base;                         /* the call-wide row number */
     const int64_t group = bf16 ? 8 : 4;          /* elements per Philox call */
     for (int64_t e = 0; e < elems; ++e) {
         const uint32_t ctr[4] = {(uint32_t)(e / group), (uint32_t)row,

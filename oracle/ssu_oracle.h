@@ -46,11 +46,16 @@ extern "C" {
  *   bf16 (G = 8): 16 bits of word (e % 8) / 2, its low half for even e and its
  *                 high half for odd e.
  * With sr_format 0 stored states are the unrounded fp64 values.
+ * row_base: the number, in the call the random bits are counted over, of this
+ * problem's row 0 -- 0 for a whole call; for a problem cut out of a larger call
+ * (a run of consecutive sequences), the packed row where the cut begins, so the
+ * counters keep their call-wide row numbers.
  */
 typedef struct {
     int sr_format;          /* 0 none, 1 fp16, 2 bf16 */
     uint64_t rand_seed;
     int philox_rounds;
+    int64_t row_base;
 } oracle_rounding;
 
 /* One token per sequence (row b is sequence b). src/dst may be NULL. */

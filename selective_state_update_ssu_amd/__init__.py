@@ -25,6 +25,7 @@ in fp32; B, C [rows, groups, dstate] in x's dtype; A, D, dt_bias fp32 [heads].
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import threading
 
@@ -34,7 +35,8 @@ from . import _abi
 
 __all__ = ["ssu_one_token", "ssu_packed_varlen", "update_replayssm_ring_trackers",
            "reset_replayssm_ring_trackers", "commit_replayssm_ring_trackers",
-           "ssd_combined_fwd_varlen", "library_path", "library"]
+           "ssd_combined_fwd_varlen", "ssd_workspace_bytes", "reset_ssd_workspaces",
+           "library_path", "library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBRARY = os.path.join(_HERE, "_lib", "libssu_amd.so")
@@ -78,22 +80,32 @@ def _contig(name, t):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _per_head(name, t, heads):
+def _per_head(name, t, heads, dim=None, dstate=None):
     """One fp32 value per head. Besides a [heads] vector this accepts the tied
-    views callers pass for a per-head parameter: [heads, dim, dstate] with both
-    inner strides 0, and [heads, 1] (MATE page, `_per_head`)."""
+    views callers pass for a per-head parameter (MATE page, `_per_head`): a
+    [heads, dim] or [heads, dim, dstate] tensor whose every dimension after the
+    first has size 1 or stride 0 -- e.g. D[:, None].expand(heads, dim) or
+    A[:, None, None].expand(heads, dim, dstate). Its first column is the
+    per-head vector. A parameter that varies along dim or dstate is per channel,
+    which this library does not implement."""
     if t is None:
         return None
     if t.dtype != torch.float32:
         raise NotImplementedError(f"{name} must be fp32, got {t.dtype}")
-    if t.dim() == 3 and t.shape[0] == heads and t.stride(1) == 0 and t.stride(2) == 0:
-        t = t[:, 0, 0]
-    elif t.dim() == 2 and t.shape == (heads, 1):
-        t = t[:, 0]
-    if t.dim() != 1 or t.shape[0] != heads:
-        raise NotImplementedError(
-            f"{name} must hold one value per head ([{heads}] or a tied view), got "
-            f"{tuple(t.shape)} with strides {tuple(t.stride())}")
+    if t.dim() not in (1, 2, 3) or t.shape[0] != heads:
+        raise ValueError(f"{name} must be [{heads}], [{heads}, dim] or [{heads}, dim, dstate]; "
+                         f"got {tuple(t.shape)}")
+    for i, size in enumerate(t.shape[1:], start=1):
+        want = dim if i == 1 else dstate
+        if size != 1 and want is not None and size != want:
+            raise ValueError(f"{name} dimension {i} has size {size}, expected 1 or {want}")
+        if size != 1 and t.stride(i) != 0:
+            raise NotImplementedError(
+                f"{name} varies along dimension {i} (shape {tuple(t.shape)}, strides "
+                f"{tuple(t.stride())}); only per-head values (size 1 or stride 0 there) are "
+                f"implemented")
+    while t.dim() > 1:
+        t = t[..., 0]
     return t.contiguous()
 
 
@@ -123,6 +135,8 @@ def _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus, pad_slot_i
         raise NotImplementedError(f"x dtype {x.dtype} is not supported")
     if dt.dtype != torch.float32:
         raise NotImplementedError(f"dt must be fp32, got {dt.dtype}")
+    if dt.shape == (rows, heads, dim) and dim > 1 and dt.stride(2) == 0:
+        dt = dt[:, :, 0]  # one value per (row, head) broadcast along dim
     if dt.shape == (rows, heads) or dt.shape == (rows, heads, 1):
         dt_per_dim = 0
     elif dt.shape == (rows, heads, dim):
@@ -144,9 +158,9 @@ def _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus, pad_slot_i
         out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype:
         raise ValueError(f"out must be {x.dtype} {tuple(x.shape)}, got {out.dtype} {tuple(out.shape)}")
-    A = _per_head("A", A, heads)
-    D = _per_head("D", D, heads)
-    dt_bias = _per_head("dt_bias", dt_bias, heads)
+    A = _per_head("A", A, heads, dim, dstate)
+    D = _per_head("D", D, heads, dim, dstate)
+    dt_bias = _per_head("dt_bias", dt_bias, heads, dim, dstate)
     _check_device(state.device, x=x, dt=dt, A=A, B=B, C=C, out=out, D=D, z=z, dt_bias=dt_bias)
     for name, t in (("state", state), ("x", x), ("dt", dt), ("B", B), ("C", C), ("z", z),
                     ("out", out)):
@@ -161,7 +175,8 @@ def _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus, pad_slot_i
         rand_seed=_ptr(_seed(rand_seed, state.device)), philox_rounds=int(philox_rounds),
         heads_per_block=int(heads_per_block), loads_per_lane=int(loads_per_lane),
         tile_order=int(tile_order))
-    return op, out, rows
+    # The temporaries whose pointers op holds stay referenced until the launch.
+    return op, out, rows, (A, D, dt_bias, dt)
 
 
 def _index(name, t, device):
@@ -180,6 +195,23 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a public call with `stream` (a torch.cuda.Stream, when given) as the
+    current stream: the temporaries the binding makes (contiguous copies of
+    per-head parameters, a missing out, workspace) are then allocated and
+    written on the stream the kernels run on, so the caching allocator cannot
+    hand their memory to other work while the kernels still read it. Inputs the
+    caller produced on another stream must be ordered by the caller, as for any
+    torch op."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, stream=None, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kwargs)
+    return wrapper
+
+
 def _raise(lib, rc, entry):
     msg = lib.ssu_last_error().decode(errors="replace")
     if rc == _abi.SSU_ERR_INVALID_ARGUMENT:
@@ -189,6 +221,7 @@ def _raise(lib, rc, entry):
     raise RuntimeError(f"{entry}: {msg} (status {rc})")
 
 
+@_on_stream
 def ssu_one_token(state, x, dt, A, B, C, out=None, *, D=None, z=None, dt_bias=None,
                   dt_softplus=False, state_batch_indices=None, dst_state_batch_indices=None,
                   pad_slot_id=-1, disable_state_update=False, rand_seed=None,
@@ -201,9 +234,9 @@ def ssu_one_token(state, x, dt, A, B, C, out=None, *, D=None, z=None, dt_bias=No
     heads_per_block / loads_per_lane / tile_order pick the launch shape (0: the
     library default)."""
     lib = library()
-    op, out, batch = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
-                               pad_slot_id, disable_state_update, heads_per_block,
-                               loads_per_lane, tile_order, rand_seed, philox_rounds)
+    op, out, batch, _keep = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
+                                      pad_slot_id, disable_state_update, heads_per_block,
+                                      loads_per_lane, tile_order, rand_seed, philox_rounds)
     src, src_dt = _index("state_batch_indices", state_batch_indices, state.device)
     dst, dst_dt = _index("dst_state_batch_indices", dst_state_batch_indices, state.device)
     for name, t in (("state_batch_indices", src), ("dst_state_batch_indices", dst)):
@@ -243,6 +276,7 @@ def _flatten_dense(name, t, lead, min_dim=4):
     return t.reshape(lead[0] * lead[1], *t.shape[2:])
 
 
+@_on_stream
 def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens=None, out=None, *,
                       num_accepted_tokens=None, state_batch_indices=None,
                       dst_state_batch_indices=None, D=None, z=None, dt_bias=None,
@@ -276,9 +310,9 @@ def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens=None, out=None, *,
         x = x.reshape(rows, *x.shape[2:])
         if cu_seqlens is None:
             seq_len = max(dsteps, 1)
-    op, out, rows = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
-                              pad_slot_id, disable_state_update, heads_per_block,
-                              loads_per_lane, tile_order, rand_seed, philox_rounds)
+    op, out, rows, _keep = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
+                                     pad_slot_id, disable_state_update, heads_per_block,
+                                     loads_per_lane, tile_order, rand_seed, philox_rounds)
     cu, meta = _index("cu_seqlens", cu_seqlens, state.device)
     na, na_dt = _index("num_accepted_tokens", num_accepted_tokens, state.device)
     if cu is not None:
@@ -362,6 +396,7 @@ def _ring_args(ring_start, prev_num_accepted, prev_query_len, state_batch_indice
         slot_stride=stride, n=slots.shape[0], pad_slot_id=int(pad_slot_id))
 
 
+@_on_stream
 def update_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len,
                                    state_batch_indices, logical_window=None,
                                    ring_buffer_len=None, pad_slot_id=-1, stream=None):
@@ -382,6 +417,7 @@ def update_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len
         _raise(lib, rc, "ssu_ring_update")
 
 
+@_on_stream
 def reset_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len,
                                   state_batch_indices, pad_slot_id=-1, stream=None):
     """Zero the three ring trackers of every named slot."""
@@ -389,6 +425,7 @@ def reset_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len,
                                    state_batch_indices, pad_slot_id=pad_slot_id, stream=stream)
 
 
+@_on_stream
 def commit_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len,
                                    state_batch_indices, num_accepted_tokens, query_start_loc,
                                    logical_window, ring_buffer_len, pad_slot_id=-1,
@@ -413,12 +450,46 @@ def commit_replayssm_ring_trackers(ring_start, prev_num_accepted, prev_query_len
 
 # ------------------------------------------------------------------- prefill
 
+# Prefill scratch, one buffer per (device, stream): grown to the largest call
+# seen, reused by every later call on that stream (MATE page: the module keeps
+# its SSD workspaces across calls, because per-call scratch allocation is what
+# makes a wrapper expensive).
+_ssd_workspaces = {}
+
+
+def ssd_workspace_bytes(nchunks, batch, nheads, headdim, dstate, ngroups, chunk_size):
+    """Bytes a caller-provided `workspace` of ssd_combined_fwd_varlen must hold:
+    the library's figure plus 255 bytes, since the binding aligns the start to 256."""
+    return int(library().ssu_ssd_workspace_bytes(nchunks, batch, nheads, headdim, dstate,
+                                                 ngroups, chunk_size)) + 255
+
+
+def _cached_workspace(device, nbytes):
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           torch.cuda.current_stream(device).cuda_stream)
+    with _lock:
+        ws = _ssd_workspaces.get(key)
+        if ws is None or ws.numel() < nbytes + 255:
+            ws = torch.empty(nbytes + 255, dtype=torch.uint8, device=device)
+            _ssd_workspaces[key] = ws
+        return ws
+
+
+def reset_ssd_workspaces():
+    """Drop every cached prefill workspace (the memory returns to torch's caching
+    allocator once no queued kernel uses it)."""
+    with _lock:
+        _ssd_workspaces.clear()
+
+
+@_on_stream
 def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seqlens,
                             last_chunk_indices, seq_idx, out=None, D=None, z=None,
                             dt_bias=None, dt_softplus=False, dt_limit=(0.0, float("inf")),
                             initial_states=None, return_intermediate_states=False,
                             state_dtype=None, checkpoint_token_indices=None,
-                            checkpoint_state_slots=None, checkpoint_states=None, stream=None):
+                            checkpoint_state_slots=None, checkpoint_states=None, workspace=None,
+                            stream=None):
     """SSD chunked prefill over packed variable-length requests (include/ssd.h).
 
     The call and its checks follow `ssd_combined_fwd_varlen` on the MATE page
@@ -430,6 +501,15 @@ def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seq
     [nchunks, heads, dim, dstate] with return_intermediate_states, else each
     request's final state [batch, heads, dim, dstate], in state_dtype (default:
     initial_states' dtype, else C's). The checkpoint_* arguments are refused.
+
+    Scratch: the kernels need a workspace (`ssd_workspace_bytes`). Without
+    `workspace` the binding keeps one per (device, stream), grown to the largest
+    call seen and reused, so repeated calls allocate only the returned states
+    (and `out` when it is not given); calls on one stream are ordered, so they
+    can share it. `reset_ssd_workspaces()` frees them. A caller that runs
+    prefills concurrently on one stream's behalf, or wants the memory under its
+    own control, passes a uint8 tensor of at least `ssd_workspace_bytes(...)`
+    bytes as `workspace`.
     """
     if any(v is not None for v in (checkpoint_token_indices, checkpoint_state_slots,
                                    checkpoint_states)):
@@ -516,7 +596,12 @@ def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seq
     states = torch.empty((rows, heads, dim, dstate), dtype=state_dtype, device=device)
     ws_bytes = lib.ssu_ssd_workspace_bytes(nchunks, batch, heads, dim, dstate, groups,
                                            int(chunk_size))
-    workspace = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=device)
+    if workspace is None:
+        workspace = _cached_workspace(device, ws_bytes)
+    elif (workspace.device != device or workspace.dtype != torch.uint8 or
+          not workspace.is_contiguous() or workspace.numel() < ws_bytes + 255):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device} of at least "
+                         f"ssd_workspace_bytes(...) = {ws_bytes + 255} bytes")
     ws_ptr = (workspace.data_ptr() + 255) // 256 * 256
     args = _abi.SsdArgs()
     args.struct_size = ctypes.sizeof(_abi.SsdArgs)

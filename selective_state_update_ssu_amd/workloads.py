@@ -5,7 +5,9 @@ It holds none of the update's arithmetic, so the GPU path and the CPU reference
 can both consume what it produces without sharing any of the method.
 
 Every tensor is drawn from its own torch generator, seeded from (workload seed,
-tensor name), on the device it is asked for. Low-precision operands are drawn in
+tensor name), on the device it is asked for; the slot structure (permutations,
+pads, lengths, acceptance counts) is drawn on the CPU, so it is the same on every
+device. Low-precision operands are drawn in
 fp32 and rounded to nearest-even by the dtype cast, so both sides of a comparison
 see identical bits. Values differ between devices (CPU and GPU generators are
 different streams); a comparison always hands the same tensors to both sides.
@@ -77,7 +79,10 @@ def uniform(shape, lo, hi, seed, name, device):
 
 
 def permutation(n, seed, name, device):
-    return torch.randperm(n, generator=_generator(seed, name, device), device=device)
+    """A seeded permutation of range(n), drawn on the CPU whatever the device, so
+    that the slot structure (which slots, which pads) of a workload is the same
+    on every device and its byte accounting can be done on either."""
+    return torch.randperm(n, generator=_generator(seed, name, "cpu")).to(device)
 
 
 @dataclass

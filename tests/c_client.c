@@ -7,6 +7,13 @@
  *     (fp32 state and io);
  *   - placement exact: slots the oracle leaves alone keep their bytes, and rows
  *     of inert sequences keep a NaN sentinel bit for bit.
+ * A third call writes a bf16 state with stochastic rounding. Its expected bits
+ * follow the layout include/ssu.h states for bf16 (Philox counter (e / 8, row,
+ * 0), word (e % 8) / 2, its low half for even e and high half for odd e), built
+ * here from the oracle's Philox and rounding rule on the oracle's unrounded
+ * state; every stored value must equal that result except where the GPU's fp32
+ * state sits next to a rounding threshold (at most 0.5 % of the elements, each
+ * one bf16 step away).
  * Prints "c client ok" and exits 0 on success, 1 on a mismatch, 2 on a HIP or
  * library error.
  */
@@ -54,7 +61,20 @@ static void* to_device(const void* host, size_t bytes) {
     return d;
 }
 
-/* Per-head parameters shared by both calls. */
+/* bf16 <-> float by bit patterns: round to nearest even (finite inputs). */
+static uint16_t bf16_bits(float v) {
+    uint32_t u;
+    memcpy(&u, &v, sizeof u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+static float bf16_value(uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float v;
+    memcpy(&v, &u, sizeof v);
+    return v;
+}
+
+/* Per-head parameters shared by the calls. */
 static float A[H], D[H], dt_bias[H];
 
 /* Compare a GPU result with the oracle's. Returns the number of failures. */
@@ -292,6 +312,99 @@ int main(void) {
             return 2;
         }
         failures += compare("packed", ROWS, state0, state_gpu, state_ref, t.out, out_ref, live);
+    }
+
+    /* ---- bf16 state, stochastic rounding: four sequences, each writing a slot
+       no sequence reads. */
+    {
+        enum { BATCH = 4 };
+        const int32_t src[BATCH] = {2, 6, 11, 0};
+        const int32_t dst[BATCH] = {3, 7, 10, 1};
+        const int64_t seed = 0x1234ABCD5678EF01ll;
+        const int rounds = 10;
+        const size_t elems = (size_t)NSLOTS * SLOT;
+        uint16_t* s16 = malloc(elems * sizeof(uint16_t));
+        double* s16_64 = malloc(elems * sizeof(double));
+        for (size_t i = 0; i < elems; ++i) {
+            s16[i] = bf16_bits(state0[i]);
+            s16_64[i] = bf16_value(s16[i]);
+        }
+        Tokens t = make_tokens(BATCH);
+        void* dstate = to_device(s16, elems * sizeof(uint16_t));
+        void* dsrc = to_device(src, sizeof src);
+        void* ddst = to_device(dst, sizeof dst);
+        void* dseed = to_device(&seed, sizeof seed);
+        ssu_one_token_args a;
+        memset(&a, 0, sizeof a);
+        a.struct_size = sizeof a;
+        a.op = operands(dstate, &t, dA, dD, dbias);
+        a.op.state_dtype = SSU_BF16;
+        a.op.rand_seed = dseed;
+        a.op.philox_rounds = rounds;
+        a.batch = BATCH;
+        a.src_slots = dsrc;
+        a.src_dtype = SSU_I32;
+        a.dst_slots = ddst;
+        a.dst_dtype = SSU_I32;
+        if (ssu_one_token(&a, stream) != SSU_OK) {
+            fprintf(stderr, "ssu_one_token (bf16, stochastic rounding): %s\n", ssu_last_error());
+            return 2;
+        }
+        CHECK_HIP(hipStreamSynchronize(stream));
+        uint16_t* g16 = malloc(elems * sizeof(uint16_t));
+        CHECK_HIP(hipMemcpy(g16, dstate, elems * sizeof(uint16_t), hipMemcpyDeviceToHost));
+
+        int64_t src64[BATCH], dst64[BATCH];
+        for (int b = 0; b < BATCH; ++b) src64[b] = src[b], dst64[b] = dst[b];
+        double* ref = malloc(elems * sizeof(double));
+        double* out_ref = malloc((size_t)BATCH * H * P * sizeof(double));
+        double *x64 = widen(t.x, (size_t)BATCH * H * P), *z64 = widen(t.z, (size_t)BATCH * H * P);
+        double *dt64 = widen(t.dt, (size_t)BATCH * H), *B64 = widen(t.B, (size_t)BATCH * G * N);
+        double* C64 = widen(t.C, (size_t)BATCH * G * N);
+        /* The unrounded fp64 states: no rounding argument. */
+        if (oracle_ssu_one_token(s16_64, ref, NSLOTS, H, P, N, G, BATCH, x64, dt64, 0, A64, B64,
+                                 C64, D64, z64, bias64, 1, src64, dst64, -1, 0, NULL, out_ref) != 0) {
+            fprintf(stderr, "oracle_ssu_one_token refused its arguments\n");
+            return 2;
+        }
+        const uint32_t key[2] = {(uint32_t)seed, (uint32_t)((uint64_t)seed >> 32)};
+        long flips = 0, bad = 0, written = 0;
+        for (int b = 0; b < BATCH; ++b) {
+            const size_t o = (size_t)dst[b] * SLOT;
+            for (uint32_t e = 0; e < SLOT; ++e) {
+                /* The header's bf16 layout: row b's counter (e / 8, b, 0, 0). */
+                const uint32_t ctr[4] = {e / 8, (uint32_t)b, 0u, 0u};
+                uint32_t words[4];
+                oracle_philox4x32(ctr, key, rounds, words);
+                const uint32_t word = words[(e % 8) / 2];
+                const uint32_t bits = (e % 2) ? (word >> 16) : (word & 0xFFFFu);
+                const uint32_t w = bits << 16; /* the rounding reads the word's top bits */
+                double want;
+                oracle_round_stochastic(&ref[o + e], &w, 1, 2, &want);
+                const double got = bf16_value(g16[o + e]);
+                ++written;
+                if (got == want) continue;
+                /* The other neighbour, decided by the fp32 state near a threshold. */
+                const double step = fabs(want) * 0x1p-7;
+                if (fabs(got - want) <= step * 1.0000001 && fabs(got - ref[o + e]) <= step) ++flips;
+                else ++bad;
+            }
+        }
+        /* Slots no call writes keep their bytes. */
+        for (int s = 0; s < NSLOTS; ++s) {
+            int written_slot = 0;
+            for (int b = 0; b < BATCH; ++b) written_slot |= dst[b] == s;
+            if (!written_slot && memcmp(g16 + (size_t)s * SLOT, s16 + (size_t)s * SLOT,
+                                        SLOT * sizeof(uint16_t)) != 0) {
+                fprintf(stderr, "bf16 SR: slot %d changed but no sequence writes it\n", s);
+                ++bad;
+            }
+        }
+        const int ok = bad == 0 && flips * 200 <= written;
+        printf("bf16 stochastic rounding: %ld of %ld elements match the header's layout, "
+               "%ld threshold flips, %ld mismatches: %s\n", written - flips - bad, written,
+               flips, bad, ok ? "matches" : "MISMATCH");
+        failures += !ok;
     }
 
     CHECK_HIP(hipStreamDestroy(stream));

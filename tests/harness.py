@@ -2,9 +2,10 @@
 
 Test infrastructure: the GPU side goes through the Python binding (and so the
 C ABI); the oracle side widens the very same tensors to fp64 on the CPU. For
-full-size workloads the oracle runs on a sample of sequences: the sample's rows
-and the slots it touches are cut out, slot ids renumbered, and the oracle's
-results compared with the matching rows and slots of the full GPU run.
+full-size workloads the oracle runs on runs of consecutive sequences that
+together cover the whole call: each run's rows and the slots it touches are cut
+out, slot ids renumbered, and the oracle's results compared with the matching
+rows and slots of the full GPU run.
 
 Tolerances (per compared tensor):
   fp32 results   max |gpu - ref| <= 1e-5 * max(1, max |ref|)
@@ -109,12 +110,17 @@ def oracle_sample(w: Workload, seqs, state_before, rounding=True):
     """The oracle on sequences `seqs` of a workload with 2-D (or no) tables.
     Returns (rows, out_ref [len(rows), H, P], slots, state_ref [len(slots), ...]):
     `rows` index the full out tensor, `slots` the full state cache. Stochastic
-    rounding numbers rows within the sample, so with a seed `seqs` must be a
-    prefix 0..k-1 (whose rows keep their numbers)."""
+    rounding numbers its random bits by the call-wide packed row, so with a seed
+    `seqs` must be a run of consecutive sequences, and the oracle is told the
+    packed row where the run begins (sr_row_base)."""
     orc = oracle.default()
     sr = sr_args(w, rounding)
     if sr:
-        assert list(seqs) == list(range(len(seqs))), "stochastic rounding needs a prefix sample"
+        seqs = list(seqs)
+        assert seqs == list(range(seqs[0], seqs[0] + len(seqs))), \
+            "stochastic rounding needs consecutive sequences"
+        sr = dict(sr, sr_row_base=(seqs[0] if w.mode == "one_token"
+                                   else int(i64(w.cu_seqlens)[seqs[0]])))
     nslots = w.state.shape[0]
     pad = w.pad_slot_id
     seqs = list(seqs)

@@ -633,6 +633,42 @@ def pin_stochastic_rounding_in_the_update(orc):
             assert np.array_equal(sr.state[s], pb["state"][s])
 
 
+def pin_stochastic_rounding_row_base(orc):
+    """A run of consecutive sequences cut out of a call and run with the cut's
+    first packed row as the row base stores exactly the bits the whole call
+    stores for them (the counters number rows call-wide); without the base the
+    bits differ. One-token and packed."""
+    rng = np.random.default_rng(59)
+    H, P, N, G = 2, 3, 8, 1
+    seed, fmt = 0x0F1E_2D3C_4B5A_6978, "bf16"
+    # one token per sequence: sequences 3..5 of 7, each writing its own slot
+    pb = _rand_problem(rng, rows=7, H=H, P=P, N=N, G=G, nslots=14)
+    src, dst = np.arange(7), np.arange(7, 14)
+    whole = orc.one_token(src=src, dst=dst, dt_softplus=True, sr_format=fmt, rand_seed=seed,
+                          **pb)
+    cut = {k: (v[3:6] if k in ("x", "dt", "B", "C", "z") else v) for k, v in pb.items()}
+    part = orc.one_token(src=src[3:6], dst=dst[3:6], dt_softplus=True, sr_format=fmt,
+                         rand_seed=seed, sr_row_base=3, **cut)
+    unbased = orc.one_token(src=src[3:6], dst=dst[3:6], dt_softplus=True, sr_format=fmt,
+                            rand_seed=seed, **cut)
+    for s_ in dst[3:6]:
+        assert np.array_equal(part.state[s_], whole.state[s_]), s_
+    assert not all(np.array_equal(unbased.state[s_], whole.state[s_]) for s_ in dst[3:6])
+    # packed: sequences 1..2 of lengths [2, 3, 2] own rows 2..6
+    pb = _rand_problem(rng, rows=7, H=H, P=P, N=N, G=G, nslots=12)
+    table = np.array([[0, 1, 2], [3, 4, 5], [6, 7, 8]])
+    whole = orc.packed_varlen(cu_seqlens=[0, 2, 5, 7], src_table=table, dst_table=table,
+                              num_accepted=[1, 2, 1], dt_softplus=True, sr_format="f16",
+                              rand_seed=seed, **pb)
+    cut = {k: (v[2:7] if k in ("x", "dt", "B", "C", "z") else v) for k, v in pb.items()}
+    part = orc.packed_varlen(cu_seqlens=[0, 3, 5], src_table=table[1:], dst_table=table[1:],
+                             num_accepted=[2, 1], dt_softplus=True, sr_format="f16",
+                             rand_seed=seed, sr_row_base=2, **cut)
+    for s_ in table[1:].reshape(-1):
+        assert np.array_equal(part.state[s_], whole.state[s_]), s_
+    assert np.array_equal(part.out, whole.out[2:7])
+
+
 # ------------------------------------------------------------ SSD prefill
 
 def _ssd_problem(rng, *, lengths, H, P, N, G, chunk, init=True, runs_ids=None):

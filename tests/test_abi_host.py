@@ -345,3 +345,35 @@ def test_error_text_is_per_thread(lib):
     assert seen["b", "rc"] == UNS and "dstate 48" in seen["b", "after both"]
     assert seen["a", "empty rc"] == _abi.SSU_OK and seen["a", "after empty"] == ""
     assert "dstate 48" in seen["b", "after a cleared"]
+
+
+def test_per_head_views_host():
+    """The binding's per-head parameter forms (pure host logic, CPU tensors):
+    tied views with size 1 or stride 0 after the head dimension give the
+    per-head vector; a parameter that varies along dim or dstate is refused."""
+    import torch
+    from selective_state_update_ssu_amd import _per_head
+
+    H, P, N = 4, 8, 16
+    v = torch.arange(H, dtype=torch.float32) - 1.5
+    for form in (v, v[:, None], v[:, None].expand(H, P), v[:, None, None].expand(H, P, N),
+                 v[:, None, None].expand(H, 1, N), v[:, None, None].contiguous()):
+        got = _per_head("D", form, H, P, N)
+        assert got.shape == (H,) and torch.equal(got, v), tuple(form.shape)
+    with pytest.raises(NotImplementedError):
+        _per_head("D", torch.randn(H, P), H, P, N)            # per channel
+    with pytest.raises(NotImplementedError):
+        _per_head("A", torch.randn(H, P, 1).expand(H, P, N), H, P, N)  # varies along dim
+    with pytest.raises(ValueError):
+        _per_head("D", v[:, None].expand(H, P + 1), H, P, N)  # wrong dim size
+    with pytest.raises(NotImplementedError):
+        _per_head("D", v.double(), H, P, N)
+
+
+def test_ssd_workspace_api_host(lib):
+    """The prefill's workspace figure for callers that bring their own buffer,
+    and the cache reset (nothing cached on a machine that ran no prefill)."""
+    n = lib.ssu_ssd_workspace_bytes(6, 3, 8, 64, 128, 2, 256)
+    assert ssu.ssd_workspace_bytes(6, 3, 8, 64, 128, 2, 256) == n + 255
+    ssu.reset_ssd_workspaces()
+    assert ssu._ssd_workspaces == {}

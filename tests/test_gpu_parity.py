@@ -3,7 +3,7 @@
 Small shapes (spanning several workgroups and a ragged row block) are compared
 in full; the named decode workloads run at their real sizes, in the launch
 configuration the benchmark times, with exact placement checked over the whole
-call and a sample of sequences compared against the oracle."""
+call and every sequence compared against the oracle."""
 import itertools
 import sys
 
@@ -39,41 +39,39 @@ def compare_full(name, w, out, after, before, ref):
 
 # ----------------------------------------------------------- named workloads
 
-def _sample(w, untouched, k=6):
-    n = w.rows if w.mode == "one_token" else w.cu_seqlens.shape[0] - 1
-    picks = [0, n - 1, n // 2, n // 3]
-    if w.mode == "one_token":
-        inert = [b for b in range(n) if untouched[b]]
-    else:
-        cu = hz.i64(w.cu_seqlens)
-        inert = [b for b in range(n) if cu[b + 1] > cu[b] and untouched[cu[b]]]
-    picks += inert[:2]
-    rng = np.random.default_rng(0)
-    picks += rng.choice(n, size=min(k, n), replace=False).tolist()
-    return sorted(set(int(p) for p in picks))
+def _runs(n, size):
+    return [list(range(b, min(b + size, n))) for b in range(0, n, size)]
 
 
 @pytest.mark.parametrize("name", list(wl.NAMED))
 def test_named_workload(name):
+    """The full-size workload in the benchmark's launch configuration: exact
+    placement over the whole call, and every sequence compared against the
+    oracle (runs of 32 consecutive sequences, each cut out with its slots)."""
     _say(f"[parity] named workload {name}")
     w = wl.NAMED[name](DEV)
     out, after, before = hz.gpu_run(w)
     written, untouched = hz.check_placement(name, w, out, after, before)
-    if hz.sr_args(w):
-        # Stochastic rounding numbers rows, so the sample is a prefix of sequences.
-        seqs = list(range(12))
-        rows, out_ref, slots, state_sr = hz.oracle_sample(w, seqs, before)
-        _, _, _, state_plain = hz.oracle_sample(w, seqs, before, rounding=False)
-        e_out = hz.check_out_rows(name + " out", out, rows, out_ref)
-        e_st = hz.check_slots_sr(name + " state", after, before, slots, state_sr, state_plain)
-        _say(f"[parity] {name}: rounding flips {e_st:.2e}")
-        return
-    seqs = _sample(w, untouched)
-    rows, out_ref, slots, state_ref = hz.oracle_sample(w, seqs, before)
-    e_out = hz.check_out_rows(name + " out", out, rows, out_ref)
-    e_st = hz.check_slots(name + " state", after, before, slots, state_ref)
-    _say(f"[parity] {name}: {len(written)} slots written, {int(untouched.sum())} rows inert, "
-         f"sampled {len(seqs)} sequences, worst out {e_out:.3g}, worst state {e_st:.3g}")
+    n = w.rows if w.mode == "one_token" else w.cu_seqlens.shape[0] - 1
+    worst_out = worst_st = 0.0
+    compared = 0
+    for seqs in _runs(n, 32):
+        rows, out_ref, slots, state_ref = hz.oracle_sample(w, seqs, before)
+        e_out = hz.check_out_rows(f"{name} out (sequences {seqs[0]}..{seqs[-1]})", out, rows,
+                                  out_ref)
+        if hz.sr_args(w):
+            _, _, _, state_plain = hz.oracle_sample(w, seqs, before, rounding=False)
+            e_st = hz.check_slots_sr(f"{name} state", after, before, slots, state_ref,
+                                     state_plain)
+        else:
+            e_st = hz.check_slots(f"{name} state", after, before, slots, state_ref)
+        worst_out, worst_st = max(worst_out, e_out), max(worst_st, e_st)
+        compared += len(seqs)
+    assert compared == n
+    _say(f"[parity] {name}: {compared} of {n} sequences compared ({n - int(untouched.sum())} "
+         f"rows written, {len(written)} slots written, {int(untouched.sum())} rows inert); "
+         f"worst out {worst_out:.3g}, worst state {worst_st:.3g}"
+         + (" (stochastic rounding: share of threshold flips)" if hz.sr_args(w) else ""))
 
 
 @pytest.mark.parametrize("name", ["nemotron_h", "packed_mtp", "bf16_state"])
@@ -362,15 +360,30 @@ def test_packed_one_row_per_sequence_without_starts():
     compare_full("onerow", w, out, state, w.state, ref)
 
 
-def test_tied_parameter_views_bit_identical():
-    """Per-head A/D/dt_bias given as tied stride-0 [heads, dim, dstate] views or
-    [heads, 1] columns give the same bits as [heads] vectors."""
+@pytest.mark.parametrize("form", ["hpn_all_zero", "hp_zero", "hpn_last_zero_p1", "column"])
+def test_tied_parameter_views_bit_identical(form):
+    """Per-head A/D/dt_bias given as tied views give the same bits as [heads]
+    vectors: [heads, dim, dstate] with both inner strides 0, [heads, dim] with
+    stride 0 along dim, [heads, 1, dstate] with stride 0 along dstate, and
+    [heads, 1] columns; dt as a [rows, heads, dim] view with stride 0 along dim
+    gives the bits of the [rows, heads] dt."""
     w = wl.one_token("tied", 909, batch=5, H=4, P=64, N=128, G=1, nslots=12, device=DEV)
     o1, s1, _ = hz.gpu_run(w)
     H, P, N = 4, 64, 128
-    w.A = w.A[:, None, None].expand(H, P, N)
-    w.dt_bias = w.dt_bias[:, None, None].expand(H, P, N)
-    w.D = w.D[:, None].contiguous()
+    if form == "hpn_all_zero":
+        w.A = w.A[:, None, None].expand(H, P, N)
+        w.dt_bias = w.dt_bias[:, None, None].expand(H, P, N)
+        w.D = w.D[:, None].contiguous()
+    elif form == "hp_zero":
+        w.A = w.A[:, None].expand(H, P)
+        w.D = w.D[:, None].expand(H, P)
+        w.dt_bias = w.dt_bias[:, None].expand(H, P)
+        w.dt = w.dt[:, :, None].expand(w.rows, H, P)
+    elif form == "hpn_last_zero_p1":
+        w.D = w.D[:, None, None].expand(H, 1, N)
+        w.dt_bias = w.dt_bias[:, None, None].expand(H, 1, N)
+    else:
+        w.A, w.D, w.dt_bias = (t[:, None].contiguous() for t in (w.A, w.D, w.dt_bias))
     o2, s2, _ = hz.gpu_run(w)
     assert torch.equal(hz.bits(o1), hz.bits(o2)) and torch.equal(hz.bits(s1), hz.bits(s2))
 

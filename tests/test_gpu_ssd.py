@@ -165,3 +165,53 @@ def test_empty_request_list_and_chunks():
     w.initial_states = None
     _, mag = sh.oracle_ref(w)
     sh.check_states(states, ref.chunk_states, mag.chunk_states, torch.float32, w.x.dtype)
+
+
+def test_repeated_calls_allocate_only_the_returned_states():
+    """After the first call of a shape, each further call on the same stream
+    makes exactly one allocation (the returned states): the workspace is cached.
+    A caller-provided workspace gives the same bits; reset drops the cache."""
+    import selective_state_update_ssu_amd as ssu
+    w = _make("bf16_f32_ragged")
+    out = torch.empty_like(w.x)
+    first = ssu.ssd_combined_fwd_varlen(*w.args(), out=out, **w.kwargs())
+    torch.cuda.synchronize()
+    counts = []
+    for _ in range(3):
+        before = torch.cuda.memory_stats()["allocation.all.allocated"]
+        states = ssu.ssd_combined_fwd_varlen(*w.args(), out=out, **w.kwargs())
+        counts.append(torch.cuda.memory_stats()["allocation.all.allocated"] - before)
+        assert torch.equal(states, first)
+        del states
+    print(f"[ssd] allocations per repeated call: {counts}", flush=True)
+    assert counts == [1, 1, 1], counts
+    nchunks, batch = w.seq_idx.numel(), w.last_chunk_indices.numel()
+    H, P, N, G = w.x.shape[1], w.x.shape[2], w.B.shape[2], w.B.shape[1]
+    ws = torch.empty(ssu.ssd_workspace_bytes(nchunks, batch, H, P, N, G, w.chunk_size),
+                     dtype=torch.uint8, device=DEV)
+    out2 = torch.empty_like(w.x)
+    mine = ssu.ssd_combined_fwd_varlen(*w.args(), out=out2, workspace=ws, **w.kwargs())
+    torch.cuda.synchronize()
+    assert torch.equal(mine, first) and torch.equal(out2, out)
+    with pytest.raises(ValueError):
+        ssu.ssd_combined_fwd_varlen(*w.args(), out=out2, workspace=ws[:100], **w.kwargs())
+    ssu.reset_ssd_workspaces()
+    assert ssu._ssd_workspaces == {}
+
+
+def test_explicit_stream():
+    """A prefill on a side stream given as `stream`: the same bits as on the
+    current stream, and its workspace is that stream's own."""
+    import selective_state_update_ssu_amd as ssu
+    w = _make("f16_bf16_d64")
+    out = torch.empty_like(w.x)
+    ref_states = ssu.ssd_combined_fwd_varlen(*w.args(), out=out, **w.kwargs())
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    out2 = torch.empty_like(w.x)
+    side.wait_stream(torch.cuda.current_stream())
+    states = ssu.ssd_combined_fwd_varlen(*w.args(), out=out2, stream=side, **w.kwargs())
+    side.synchronize()
+    assert torch.equal(states, ref_states) and torch.equal(out2, out)
+    keys = {k[1] for k in ssu._ssd_workspaces}
+    assert side.cuda_stream in keys

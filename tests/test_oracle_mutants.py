@@ -47,6 +47,7 @@ MUTANTS = [
     ("packed_state_not_chained",
      "step_token(&pb, s, begin + t, out);",
      "memcpy(s, state_in + r * slot_elems, (size_t)slot_elems * sizeof(double));\n            step_token(&pb, s, begin + t, out);"),
+    ("sr_row_base_ignored", "    row += rd->row_base;", "    (void)0;"),
     ("valid_upper_bound", "slot >= 0 && slot < nslots", "slot >= 0 && slot <= nslots - 2"),
     ("pad_id_ignored", "return slot != pad_slot_id && slot >= 0", "return slot >= 0"),
     ("ring_window_off_by_one", "if (counted + 1 > logical_window) {", "if (counted + 1 >= logical_window) {"),
