@@ -125,6 +125,31 @@ size_t ssu_ssd_workspace_bytes(int64_t nchunks, int64_t batch, int64_t nheads,
  */
 int ssu_ssd_prefill(const ssu_ssd_args *args, void *stream);
 
+/* Bytes of the static scratch ssu_ssd_prefill_noalloc uses on each GPU. */
+#define SSU_SSD_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * ssu_ssd_prefill without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The caller still owns
+ * every input and output; args->workspace must be NULL and workspace_bytes 0.
+ * The scratch is a static array of SSU_SSD_STATIC_SCRATCH_BYTES (128 MiB) in the
+ * library's device code: each GPU the library runs on holds one until the
+ * process ends, and its address is looked up on the entry point's first call on
+ * a device (make the stream's device current, as for every HIP call). Calls
+ * that overlap in time on one GPU share that array and race: order them on one
+ * stream (or use ssu_ssd_prefill with a workspace each). The array keeps the
+ * last call's contents; no call needs it cleared.
+ *
+ * Returns what ssu_ssd_prefill returns, and SSU_ERR_UNSUPPORTED when the call's
+ * workspace (ssu_ssd_workspace_bytes) exceeds SSU_SSD_STATIC_SCRATCH_BYTES
+ * (it holds up to 27 chunks of 128 tokens at 128 heads x 64 x 128 with 8 groups,
+ * 42 chunks of 256 at 80 heads x 64 x 128 with 1 group), SSU_ERR_LAUNCH when
+ * no device is current or the scratch cannot be found on it. Results are those
+ * of ssu_ssd_prefill, bit for bit (the same kernels).
+ */
+int ssu_ssd_prefill_noalloc(const ssu_ssd_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -489,7 +489,7 @@ def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seq
                             initial_states=None, return_intermediate_states=False,
                             state_dtype=None, checkpoint_token_indices=None,
                             checkpoint_state_slots=None, checkpoint_states=None, workspace=None,
-                            stream=None):
+                            static_scratch=False, stream=None):
     """SSD chunked prefill over packed variable-length requests (include/ssd.h).
 
     The call and its checks follow `ssd_combined_fwd_varlen` on the MATE page
@@ -509,7 +509,10 @@ def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seq
     can share it. `reset_ssd_workspaces()` frees them. A caller that runs
     prefills concurrently on one stream's behalf, or wants the memory under its
     own control, passes a uint8 tensor of at least `ssd_workspace_bytes(...)`
-    bytes as `workspace`.
+    bytes as `workspace`. With static_scratch=True the call goes to
+    `ssu_ssd_prefill_noalloc`, whose scratch is the library's static per-GPU
+    array (SSU_SSD_STATIC_SCRATCH_BYTES; larger calls raise NotImplementedError):
+    the binding then allocates only the returned states (and `out` if absent).
     """
     if any(v is not None for v in (checkpoint_token_indices, checkpoint_state_slots,
                                    checkpoint_states)):
@@ -596,13 +599,18 @@ def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seq
     states = torch.empty((rows, heads, dim, dstate), dtype=state_dtype, device=device)
     ws_bytes = lib.ssu_ssd_workspace_bytes(nchunks, batch, heads, dim, dstate, groups,
                                            int(chunk_size))
-    if workspace is None:
-        workspace = _cached_workspace(device, ws_bytes)
-    elif (workspace.device != device or workspace.dtype != torch.uint8 or
-          not workspace.is_contiguous() or workspace.numel() < ws_bytes + 255):
-        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device} of at least "
-                         f"ssd_workspace_bytes(...) = {ws_bytes + 255} bytes")
-    ws_ptr = (workspace.data_ptr() + 255) // 256 * 256
+    if static_scratch:
+        if workspace is not None:
+            raise ValueError("static_scratch and workspace exclude each other")
+        ws_ptr, ws_bytes = None, 0
+    else:
+        if workspace is None:
+            workspace = _cached_workspace(device, ws_bytes)
+        elif (workspace.device != device or workspace.dtype != torch.uint8 or
+              not workspace.is_contiguous() or workspace.numel() < ws_bytes + 255):
+            raise ValueError(f"workspace must be a contiguous uint8 tensor on {device} of at "
+                             f"least ssd_workspace_bytes(...) = {ws_bytes + 255} bytes")
+        ws_ptr = (workspace.data_ptr() + 255) // 256 * 256
     args = _abi.SsdArgs()
     args.struct_size = ctypes.sizeof(_abi.SsdArgs)
     args.tokens, args.nheads, args.headdim, args.dstate, args.ngroups = (tokens, heads, dim,
@@ -620,7 +628,8 @@ def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seq
     args.initial_states, args.out, args.states = _ptr(initial_states), _ptr(out), _ptr(states)
     args.return_intermediate_states = int(bool(return_intermediate_states))
     args.workspace, args.workspace_bytes = ws_ptr, ws_bytes
-    rc = lib.ssu_ssd_prefill(ctypes.byref(args), _stream(device, stream))
+    entry = lib.ssu_ssd_prefill_noalloc if static_scratch else lib.ssu_ssd_prefill
+    rc = entry(ctypes.byref(args), _stream(device, stream))
     if rc != _abi.SSU_OK:
-        _raise(lib, rc, "ssu_ssd_prefill")
+        _raise(lib, rc, entry.__name__)
     return states

@@ -11,7 +11,8 @@ SSU_OK, SSU_ERR_INVALID_ARGUMENT, SSU_ERR_UNSUPPORTED, SSU_ERR_LAUNCH = 0, 1, 2,
 ABI_VERSION = 1
 
 EXPORTS = ("ssu_one_token", "ssu_packed_varlen", "ssu_ring_update", "ssu_ring_commit",
-           "ssu_last_error", "ssu_version", "ssu_ssd_workspace_bytes", "ssu_ssd_prefill")
+           "ssu_last_error", "ssu_version", "ssu_ssd_workspace_bytes", "ssu_ssd_prefill",
+           "ssu_ssd_prefill_noalloc")
 
 
 class Operands(ctypes.Structure):
@@ -94,8 +95,9 @@ def load(path: str) -> ctypes.CDLL:
         f.argtypes = [ctypes.POINTER(RingArgs), c_void_p]
     lib.ssu_ssd_workspace_bytes.restype = c_size_t
     lib.ssu_ssd_workspace_bytes.argtypes = [c_int64] * 7
-    lib.ssu_ssd_prefill.restype = c_int32
-    lib.ssu_ssd_prefill.argtypes = [ctypes.POINTER(SsdArgs), c_void_p]
+    for f in (lib.ssu_ssd_prefill, lib.ssu_ssd_prefill_noalloc):
+        f.restype = c_int32
+        f.argtypes = [ctypes.POINTER(SsdArgs), c_void_p]
     lib.ssu_last_error.restype = c_char_p
     lib.ssu_last_error.argtypes = []
     lib.ssu_version.restype = c_int32

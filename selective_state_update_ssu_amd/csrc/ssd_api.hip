@@ -1,9 +1,11 @@
 // ssd_api.hip -- the SSD prefill entry points declared in include/ssd.h:
 // host-side validation of the argument struct (never of device data), the
-// workspace layout, and the kernel launches.
+// workspace layout, the kernel launches, and the static scratch of the entry
+// point that allocates nothing.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "ssd.h"
 #include "ssd_kernel.hpp"
@@ -163,14 +165,10 @@ extern "C" size_t ssu_ssd_workspace_bytes(int64_t nchunks, int64_t batch, int64_
     return layout(nchunks, batch, nheads, headdim, dstate, ngroups, chunk_size).total;
 }
 
-extern "C" int ssu_ssd_prefill(const ssu_ssd_args* args, void* stream) {
-    if (!args) return ssu::report(SSU_ERR_INVALID_ARGUMENT, "args is NULL");
-    if (args->struct_size != sizeof(ssu_ssd_args))
-        return ssu::report(SSU_ERR_INVALID_ARGUMENT, "struct_size %u, expected %zu",
-                           args->struct_size, sizeof(ssu_ssd_args));
-    const ssu_ssd_args& a = *args;
-    if (const int rc = check(a)) return rc;
+namespace {
 
+// The launches of one validated prefill, with a.workspace as its scratch.
+int launch(const ssu_ssd_args& a, void* stream) {
     const Layout l = layout(a.nchunks, a.batch, a.nheads, a.headdim, a.dstate, a.ngroups,
                             a.chunk_size);
     char* ws = static_cast<char*>(a.workspace);
@@ -224,4 +222,81 @@ extern "C" int ssu_ssd_prefill(const ssu_ssd_args* args, void* stream) {
     if (err != hipSuccess)
         return ssu::report(SSU_ERR_LAUNCH, "SSD prefill launch failed: %s", hipGetErrorString(err));
     return ssu::report_ok();
+}
+
+}  // namespace
+
+// Scratch of ssu_ssd_prefill_noalloc: one array per GPU, placed by the loader
+// with the library's device code and held until the process ends. In host code
+// `scratch` is only a handle for the symbol, never a device address: its device
+// address is looked up once per device (with that device current) and kept in
+// scratch_ptr, which is what kernels and copies receive.
+constexpr size_t kStaticScratch = SSU_SSD_STATIC_SCRATCH_BYTES;
+static_assert(kStaticScratch % 256 == 0, "whole 256-byte blocks");
+static __device__ __align__(256) unsigned char scratch[kStaticScratch];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, looked up on its first use there.
+int current_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return ssu::report(SSU_ERR_LAUNCH, "no usable current HIP device (%d)", dev);
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return ssu::report(SSU_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s",
+                               dev, hipGetErrorString(e));
+        scratch_ptr[dev] = ptr;
+    }
+    *out = scratch_ptr[dev];
+    return SSU_OK;
+}
+
+}  // namespace
+
+extern "C" int ssu_ssd_prefill(const ssu_ssd_args* args, void* stream) {
+    if (!args) return ssu::report(SSU_ERR_INVALID_ARGUMENT, "args is NULL");
+    if (args->struct_size != sizeof(ssu_ssd_args))
+        return ssu::report(SSU_ERR_INVALID_ARGUMENT, "struct_size %u, expected %zu",
+                           args->struct_size, sizeof(ssu_ssd_args));
+    const ssu_ssd_args& a = *args;
+    if (const int rc = check(a)) return rc;
+    return launch(a, stream);
+}
+
+extern "C" int ssu_ssd_prefill_noalloc(const ssu_ssd_args* args, void* stream) {
+    if (!args) return ssu::report(SSU_ERR_INVALID_ARGUMENT, "args is NULL");
+    if (args->struct_size != sizeof(ssu_ssd_args))
+        return ssu::report(SSU_ERR_INVALID_ARGUMENT, "struct_size %u, expected %zu",
+                           args->struct_size, sizeof(ssu_ssd_args));
+    if (args->workspace || args->workspace_bytes)
+        return ssu::report(SSU_ERR_INVALID_ARGUMENT,
+                           "workspace must be NULL and workspace_bytes 0: this entry point uses "
+                           "the library's static scratch");
+    // Sizes first (host arithmetic only), then the device's scratch.
+    if (args->nchunks >= 0 && args->batch >= 0 && args->nheads >= 0 && args->headdim >= 0 &&
+        args->dstate >= 0 && args->ngroups >= 0 && args->chunk_size >= 0) {
+        const size_t need = layout(args->nchunks, args->batch, args->nheads, args->headdim,
+                                   args->dstate, args->ngroups, args->chunk_size).total;
+        if (need > kStaticScratch)
+            return ssu::report(SSU_ERR_UNSUPPORTED,
+                               "this prefill needs %zu bytes of scratch; the static scratch holds "
+                               "%zu (SSU_SSD_STATIC_SCRATCH_BYTES): pass a workspace to "
+                               "ssu_ssd_prefill instead",
+                               need, kStaticScratch);
+    }
+    ssu_ssd_args a = *args;
+    if (a.nheads >= 1 && a.headdim >= 1 && a.dstate >= 1 && a.ngroups >= 1 && a.nchunks >= 1) {
+        if (const int rc = current_scratch(&a.workspace)) return rc;
+        a.workspace_bytes = kStaticScratch;
+    }
+    if (const int rc = check(a)) return rc;
+    return launch(a, stream);
 }

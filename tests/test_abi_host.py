@@ -377,3 +377,39 @@ def test_ssd_workspace_api_host(lib):
     assert ssu.ssd_workspace_bytes(6, 3, 8, 64, 128, 2, 256) == n + 255
     ssu.reset_ssd_workspaces()
     assert ssu._ssd_workspaces == {}
+
+
+def _ssd_args(**kw):
+    a = _abi.SsdArgs()
+    a.struct_size = ctypes.sizeof(_abi.SsdArgs)
+    a.tokens, a.nheads, a.headdim, a.dstate, a.ngroups = 300, 4, 64, 128, 2
+    a.chunk_size, a.nchunks, a.batch = 256, 2, 1
+    a.x, a.dt, a.A, a.B, a.C, a.out, a.states = (addr(i) for i in range(20, 27))
+    a.io_dtype, a.dt_dtype, a.state_dtype = _abi.SSU_BF16, _abi.SSU_F32, _abi.SSU_F32
+    a.dt_min, a.dt_max = 0.0, float("inf")
+    a.cu_chunk_seqlens, a.seq_idx, a.last_chunk_indices = addr(30), addr(31), addr(32)
+    a.meta_dtype = _abi.SSU_I32
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_ssd_noalloc_host_checks(lib):
+    """The static-scratch prefill refuses a caller workspace and calls whose
+    scratch exceeds SSU_SSD_STATIC_SCRATCH_BYTES before touching any device; the
+    header's constant is what the library enforces."""
+    text = open(os.path.join(ROOT, "include", "ssd.h")).read()
+    m = re.search(r"#define SSU_SSD_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    cap = int(m.group(1)) << int(m.group(2))
+    a = _ssd_args(workspace=addr(40), workspace_bytes=1 << 20)
+    assert lib.ssu_ssd_prefill_noalloc(ctypes.byref(a), None) == INV
+    assert "static scratch" in lib.ssu_last_error().decode()
+    # The largest chunk count that fits, and one more.
+    n = 1
+    while lib.ssu_ssd_workspace_bytes(n + 1, 1, 128, 64, 128, 8, 128) <= cap:
+        n += 1
+    a = _ssd_args(nheads=128, ngroups=8, chunk_size=128, nchunks=n + 1, tokens=128 * (n + 1))
+    assert lib.ssu_ssd_prefill_noalloc(ctypes.byref(a), None) == UNS
+    msg = lib.ssu_last_error().decode()
+    assert "static scratch holds" in msg and str(cap) in msg, msg
+    assert n == 27, n
