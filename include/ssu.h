@@ -145,7 +145,10 @@ typedef struct ssu_operands {
     int32_t loads_per_lane;   /* launch shape: 16-byte state loads each lane keeps in
                                  flight, 0 = library default, else 2 or 4 */
     int32_t tile_order;       /* launch shape: 0 = library default, 1 = each XCD takes
-                                 a contiguous range of tiles, 2 = hardware order */
+                                 a contiguous range of tiles, 2 = hardware order, 3 = each
+                                 XCD takes an equal contiguous share (a block of heads) of
+                                 every sequence's tiles (as 1 when a sequence's tiles do
+                                 not split evenly over the 8 XCDs) */
 } ssu_operands;
 
 /*

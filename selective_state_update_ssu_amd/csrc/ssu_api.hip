@@ -97,8 +97,9 @@ int check_operands(const ssu_operands& op, int64_t rows, bool work, bool packed)
     if (op.philox_rounds < 0 || op.philox_rounds > 64)
         return fail(SSU_ERR_INVALID_ARGUMENT, "philox_rounds must be in [0, 64], got %d",
                     op.philox_rounds);
-    if (op.tile_order < 0 || op.tile_order > 2)
-        return fail(SSU_ERR_INVALID_ARGUMENT, "tile_order must be 0, 1 or 2, got %d", op.tile_order);
+    if (op.tile_order < 0 || op.tile_order > 3)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "tile_order must be 0, 1, 2 or 3, got %d",
+                    op.tile_order);
     if (op.loads_per_lane != 0 && op.loads_per_lane != 2 && op.loads_per_lane != 4)
         return fail(SSU_ERR_INVALID_ARGUMENT, "loads_per_lane must be 0, 2 or 4, got %d",
                     op.loads_per_lane);
@@ -158,13 +159,16 @@ int check_operands(const ssu_operands& op, int64_t rows, bool work, bool packed)
 // 128, headdim 64): a read+write one-token call streams best in small tiles
 // (2 loads per lane, 2 heads per workgroup with an fp32 state, 1 with a 16-bit
 // one); a read-only call and the packed call, which writes several states per
-// state read, in larger ones (4 loads per lane, 2 heads per workgroup). Calls
-// whose sequences all have the same number of tokens (one-token calls, packed
-// calls without cu_seqlens) gain from each XCD walking a contiguous range of
-// tiles; varlen packed calls do not, since a contiguous range of sequences can
-// hold more tokens than another, so their tiles go round robin.
+// state read, in larger ones (4 loads per lane, 2 heads per workgroup). Tile
+// order: each XCD takes an equal contiguous share of every sequence's tiles (a
+// block of its heads), which keeps each XCD streaming contiguous memory and
+// gives every XCD the same share of each sequence however their token counts
+// differ (1-2 % faster than contiguous ranges of sequences on the one-token
+// shapes, 3 % on varlen packed calls, whose contiguous ranges of sequences carry
+// unequal token counts); packed calls without cu_seqlens (every sequence the
+// same length) stream best with each XCD walking a contiguous range of tiles.
 struct Shape {
-    int heads_per_block, loads_per_lane, xcd_order;
+    int heads_per_block, loads_per_lane, xcd_order;  // xcd_order as in ssu::KernelParams
 };
 
 Shape default_shape(const ssu_operands& op, bool packed, bool equal_lengths) {
@@ -172,13 +176,13 @@ Shape default_shape(const ssu_operands& op, bool packed, bool equal_lengths) {
     Shape s;
     const bool sr = op.rand_seed && op.state_dtype != SSU_F32 && !read_only;
     if (packed)
-        s = {2, 4, equal_lengths ? 1 : 0};
+        s = {2, 4, equal_lengths ? 1 : 2};
     else if (read_only)
-        s = {2, 4, 1};
+        s = {2, 4, 2};
     else if (sr)  // the Philox work of stochastic rounding wants bigger tiles
-        s = {1, 4, 1};
+        s = {1, 4, 2};
     else
-        s = {op.state_dtype == SSU_F32 ? 2 : 1, 2, 1};
+        s = {op.state_dtype == SSU_F32 ? 2 : 1, 2, 2};
     const int64_t hpg = op.nheads / op.ngroups;
     const int hmax = ssu::max_heads_per_block(static_cast<int>(op.dstate), packed);
     while (s.heads_per_block > 1 && (hpg % s.heads_per_block != 0 || s.heads_per_block > hmax))
@@ -210,7 +214,9 @@ void fill_common(ssu::KernelParams& k, const ssu_operands& op, bool packed,
     const Shape dflt = default_shape(op, packed, equal_lengths);
     k.heads_per_block = op.heads_per_block ? op.heads_per_block : dflt.heads_per_block;
     k.loads_per_lane = op.loads_per_lane ? op.loads_per_lane : dflt.loads_per_lane;
-    k.xcd_order = op.tile_order ? op.tile_order == 1 : dflt.xcd_order;
+    // tile_order 1: contiguous ranges, 2: hardware order, 3: per-sequence shares.
+    k.xcd_order = op.tile_order == 0 ? dflt.xcd_order
+                                     : (op.tile_order == 1 ? 1 : (op.tile_order == 3 ? 2 : 0));
     k.head_blocks = k.nheads / k.heads_per_block;
     k.dt_per_dim = op.dt_per_dim;
     k.dt_softplus = op.dt_softplus ? 1 : 0;

@@ -265,6 +265,20 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t n) {
     return xcd < tall ? xcd * per + k : tall * per + (xcd - tall) * (per - 1) + k;
 }
 
+// Tile of workgroup `id` out of `n` = sequences x `per_seq` tiles when every XCD
+// should take an equal contiguous share of each sequence's tiles (a block of its
+// heads): XCD x walks, sequence after sequence, tiles [x per_seq / kXcds,
+// (x + 1) per_seq / kXcds) of each. Every XCD then carries the same share of
+// every sequence, however the sequences' token counts differ, and still streams
+// contiguous memory. A bijection of [0, n) when per_seq is a multiple of kXcds
+// (else the contiguous-range order).
+__device__ __forceinline__ int64_t xcd_split(int64_t id, int64_t n, int64_t per_seq) {
+    if (per_seq % kXcds) return xcd_tile(id, n);
+    const int64_t share = per_seq / kXcds;
+    const int64_t xcd = id % kXcds, k = id / kXcds;
+    return (k / share) * per_seq + xcd * share + k % share;
+}
+
 // ------------------------------------------------------------------ kernel
 
 template <typename ST, typename IT, int N, int LOADS, bool PACKED, bool SR>
@@ -289,7 +303,10 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
     const bool row_leader = (lane % LPR) == 0;
 
     int64_t wg = blockIdx.x;
-    if (p.xcd_order) wg = xcd_tile(wg, gridDim.x);
+    if (p.xcd_order == 1)
+        wg = xcd_tile(wg, gridDim.x);
+    else if (p.xcd_order == 2)
+        wg = xcd_split(wg, gridDim.x, static_cast<int64_t>(p.head_blocks) * p.row_blocks);
     const int rb = static_cast<int>(wg % p.row_blocks);
     wg /= p.row_blocks;
     const int hblk = static_cast<int>(wg % p.head_blocks);

@@ -52,7 +52,9 @@ struct KernelParams {
     int32_t nheads, headdim, ngroups, heads_per_group;
     int32_t heads_per_block;  // heads per workgroup (same group)
     int32_t loads_per_lane;   // one of kLoadDepths
-    int32_t xcd_order;        // nonzero: each XCD walks a contiguous range of tiles
+    int32_t xcd_order;        // 0: hardware order; 1: each XCD walks a contiguous range
+                              // of tiles; 2: each XCD takes an equal contiguous share of
+                              // every sequence's tiles
     int32_t head_blocks;      // nheads / heads_per_block
     int32_t row_blocks;       // ceil(headdim / rows per block), set by the launcher
 

@@ -133,7 +133,7 @@ INV, UNS = _abi.SSU_ERR_INVALID_ARGUMENT, _abi.SSU_ERR_UNSUPPORTED
     (dict(heads_per_block=8), INV, "heads_per_block"),
     (dict(loads_per_lane=3), INV, "loads_per_lane"),
     (dict(loads_per_lane=8), INV, "loads_per_lane"),
-    (dict(tile_order=3), INV, "tile_order"),
+    (dict(tile_order=4), INV, "tile_order"),
     (dict(nheads=12, ngroups=4, heads_per_block=2), INV, "divide"),
     (dict(dstate=256, heads_per_block=4), UNS, "exceeds"),
     (dict(state=0), INV, "state must not be NULL"),

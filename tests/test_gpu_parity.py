@@ -76,12 +76,12 @@ def test_named_workload(name):
 
 @pytest.mark.parametrize("name", ["nemotron_h", "packed_mtp", "bf16_state"])
 def test_launch_shapes_bit_identical(name):
-    """The launch shape (heads per workgroup, loads per lane) changes nothing in
-    the arithmetic of an element: every shape gives the same bits."""
+    """The launch shape (heads per workgroup, loads per lane, tile order) changes
+    nothing in the arithmetic of an element: every shape gives the same bits."""
     w = wl.NAMED[name](DEV)
     o1, s1, _ = hz.gpu_run(w, heads_per_block=1, loads_per_lane=2, tile_order=2)
     shapes = ((2, 2), (4, 1), (4, 2)) if w.mode == "packed" else ((2, 2), (2, 4), (4, 1), (4, 2), (4, 4))
-    for order in (1, 2):
+    for order in (1, 2, 3):
         for lpl, hpb in shapes:
             o2, s2, _ = hz.gpu_run(w, heads_per_block=hpb, loads_per_lane=lpl, tile_order=order)
             assert torch.equal(hz.bits(o1), hz.bits(o2)), (lpl, hpb, order)
