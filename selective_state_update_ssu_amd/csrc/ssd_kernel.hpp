@@ -942,9 +942,16 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
 #pragma unroll
         for (int r = 0; r < SPASS; ++r) rs[pl][r] = bload(sr, pl * P * N * 2 + 16 * (tid + NT * r));
     // C operands of the entering-state product, first k step.
+    // Token tiles of this wave: w and 2 NW - 1 - w, so that every wave's pair
+    // covers about the same share of the causal triangle (tile i needs i / 2 + 1
+    // blocks of C B^T).
+    static_assert(TT == 2, "tile pairs");
+    int t0_of[TT];
+    t0_of[0] = 16 * wave;
+    t0_of[1] = 16 * (2 * NW - 1 - wave);
     int trow[TT];
 #pragma unroll
-    for (int k = 0; k < TT; ++k) trow[k] = min(16 * (wave + NW * k) + lane % 16, len - 1);
+    for (int k = 0; k < TT; ++k) trow[k] = min(t0_of[k] + lane % 16, len - 1);
     const int kcol = 8 * (lane / 16);
     auto c_frag = [&](int k, int kk) {
         return *reinterpret_cast<const v8*>(Cp + ((d.lo + trow[k]) * p.ngroups + g) * N + kk + kcol);
@@ -968,7 +975,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
     const Rsrc zr = make_rsrc(p.z ? static_cast<const IT*>(p.z) + xoff : nullptr, p.z ? len * xrow : 0u);
     u16x8 ez[TT][2];
     auto z_load = [&](int k) {
-        const uint32_t off = (16 * (wave + NW * k) + er) * xrow + 2 * ec;
+        const uint32_t off = (t0_of[k] + er) * xrow + 2 * ec;
         ez[k][0] = bload_nt(zr, off);
         ez[k][1] = bload_nt(zr, off + 8 * xrow);
     };
@@ -1005,7 +1012,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
         for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool live[TT];
 #pragma unroll
-    for (int k = 0; k < TT; ++k) live[k] = 16 * (wave + NW * k) < len;
+    for (int k = 0; k < TT; ++k) live[k] = t0_of[k] < len;
 
     // ---- the entering state: C_t . (S_hi + S_lo), then scaled by exp(cum_t)
     if (has_state) {
@@ -1039,7 +1046,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
         for (int k = 0; k < TT; ++k)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = min(16 * (wave + NW * k) + 4 * (lane / 16) + i, Q - 1);
+                const int t = min(t0_of[k] + 4 * (lane / 16) + i, Q - 1);
                 const float f = __builtin_amdgcn_exp2f(cum2[t]);
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) acc[k][pt][i] *= f;
@@ -1068,7 +1075,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
     u32x4v cb[TT][DEPTH][CW];
     const Rsrc cbr = make_rsrc(cbp, Q * Q * sizeof(CBT));
     auto cb_load = [&](int k, int kk, int dd) {
-        const int t0 = 16 * (wave + NW * k);
+        const int t0 = t0_of[k];
         const uint32_t off = ((t0 + lane % 16) * Q + min(kk, Q - 32) + kcol) * sizeof(CBT);
 #pragma unroll
         for (int w = 0; w < CW; ++w)
@@ -1082,12 +1089,14 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
     for (int dd = 0; dd < DEPTH; ++dd)
 #pragma unroll
         for (int k = 0; k < TT; ++k) cb_load(k, 32 * dd, dd);
-    // The loop runs DEPTH s blocks per iteration so that slot indices stay static.
-    for (int kb = 0; kb < len; kb += 32 * DEPTH) {
+    // The loop runs DEPTH s blocks per iteration so that slot indices stay static,
+    // up to the last block this wave's later live tile needs.
+    const int kend = min(len, (live[1] ? t0_of[1] : t0_of[0]) + 16);
+    for (int kb = 0; kb < kend; kb += 32 * DEPTH) {
 #pragma unroll
         for (int dd = 0; dd < DEPTH; ++dd) {
             const int kk = kb + 32 * dd;
-            if (kk >= len) break;
+            if (kk >= kend) break;
             const int col = kk + kcol;
             v8 xf[PT];
 #pragma unroll
@@ -1101,7 +1110,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
             for (int j = 0; j < 8; ++j) ls[j] = sl[col + j];
 #pragma unroll
             for (int k = 0; k < TT; ++k) {
-                const int t0 = 16 * (wave + NW * k);
+                const int t0 = t0_of[k];
                 if (live[k] && t0 + 15 >= kk) {
                     const int t = t0 + lane % 16;
                     const float ct = cum2[t];
@@ -1151,7 +1160,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             const int pr = 16 * pt + lane % 16;
-            const int t = 16 * (wave + NW * k) + 4 * (lane / 16);
+            const int t = t0_of[k] + 4 * (lane / 16);
             typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
             const u16x4 xr4 = *reinterpret_cast<const u16x4*>(xv + pr * XP + swz(pr, t));
 #pragma unroll
@@ -1174,7 +1183,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
                              k < ZL ? zslot[2 * 64 * NW * k + 1] : ez[k][1]};
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const int row = er + 8 * half, t = 16 * (wave + NW * k) + row;
+            const int row = er + 8 * half, t = t0_of[k] + row;
             if (t < len) {
                 const f32x4* srow = reinterpret_cast<const f32x4*>(scratch + row * EP + ec);
                 u16x8 o;
