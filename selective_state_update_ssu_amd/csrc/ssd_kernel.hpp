@@ -1076,15 +1076,18 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
     const Rsrc cbr = make_rsrc(cbp, Q * Q * sizeof(CBT));
     auto cb_load = [&](int k, int kk, int dd) {
         const int t0 = t0_of[k];
-        const uint32_t off = ((t0 + lane % 16) * Q + min(kk, Q - 32) + kcol) * sizeof(CBT);
+        // A block past the tile's last row is never used: its load stays in the
+        // instruction stream (the waits count loads) but reads nothing.
+        const uint32_t off = kk > t0 + 15 ? kOutOfRange
+                                           : ((t0 + lane % 16) * Q + min(kk, Q - 32) + kcol) * sizeof(CBT);
 #pragma unroll
         for (int w = 0; w < CW; ++w)
             cb[k][dd][w] = __builtin_amdgcn_raw_buffer_load_b128(cbr, off + 16 * w, 0, 0);
     };
     auto cb_value = [&](int k, int dd, int j) -> float { return __uint_as_float(cb[k][dd][j / 4][j % 4]); };
     // Every step issues one load per (tile, slot) in the same order, whether or
-    // not the tile needs the block, so the wait before each use stays a count of
-    // the loads issued after it.
+    // not the tile needs the block (an unneeded block's load reads nothing), so
+    // the wait before each use stays a count of the loads issued after it.
 #pragma unroll
     for (int dd = 0; dd < DEPTH; ++dd)
 #pragma unroll
