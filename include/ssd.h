@@ -113,7 +113,8 @@ size_t ssu_ssd_workspace_bytes(int64_t nchunks, int64_t batch, int64_t nheads,
  * Returns SSU_OK, SSU_ERR_INVALID_ARGUMENT (inconsistent sizes or dtypes, a null
  * required pointer, out overlapping an input, a workspace too small or
  * misaligned), SSU_ERR_UNSUPPORTED (a headdim / dstate / chunk_size without
- * compiled kernels -- headdim 64, dstate 64 or 128, chunk_size 128 or 256 -- or
+ * compiled kernels -- headdim 64, 128, 192 or 256, dstate 64, 128 or 256,
+ * chunk_size 128 or 256 -- or
  * a misaligned operand) or SSU_ERR_LAUNCH.
  *
  * Device data is not validated by the host. Preconditions, as on the pages:

@@ -97,9 +97,9 @@ int check(const ssu_ssd_args& a) {
     if (!ssd::supported_shape(a.headdim, a.dstate, a.chunk_size))
         return report(SSU_ERR_UNSUPPORTED,
                       "no kernel for headdim %lld, dstate %lld, chunk_size %lld (built: headdim "
-                      "64, dstate 64 or 128, chunk_size 128 or 256)",
+                      "64, 128, 192 or 256, dstate 64, 128 or 256, chunk_size 128 or 256)",
                       (long long)a.headdim, (long long)a.dstate, (long long)a.chunk_size);
-    if (a.nchunks * a.nheads > INT32_MAX || a.nchunks * a.ngroups * 16 > INT32_MAX)
+    if (a.nchunks * a.nheads * (a.headdim / 64) > INT32_MAX || a.nchunks * a.ngroups * 16 > INT32_MAX)
         return report(SSU_ERR_UNSUPPORTED, "too many chunks for one launch");
     // The kernels address a chunk's rows with 32-bit byte offsets.
     if (a.chunk_size * a.nheads * a.headdim * 2 >= (int64_t(1) << 30) ||
@@ -207,6 +207,8 @@ int launch(const ssu_ssd_args& a, void* stream) {
     p.nheads = static_cast<int32_t>(a.nheads);
     p.ngroups = static_cast<int32_t>(a.ngroups);
     p.heads_per_group = static_cast<int32_t>(a.nheads / a.ngroups);
+    p.headdim = static_cast<int32_t>(a.headdim);
+    p.dstate = static_cast<int32_t>(a.dstate);
     p.dt_dtype = a.dt_dtype;
     p.meta_i64 = a.meta_dtype == SSU_I64;
     p.D_per_dim = a.D_per_dim != 0;

@@ -106,6 +106,7 @@ struct SsdParams {
     int64_t tokens, nchunks, batch;
     float dt_min, dt_max;
     int32_t nheads, ngroups, heads_per_group;
+    int32_t headdim, dstate;  // full sizes; the walk and the scan work on blocks of them
     int32_t dt_dtype;
     int32_t meta_i64;
     int32_t D_per_dim, dt_softplus;
@@ -153,6 +154,11 @@ __device__ __forceinline__ void split16(float v, IT& hi, IT& lo) {
 // Each chunk's entering state reaches the scan as these two planes, [2][P][N]
 // per (chunk, head).
 constexpr int kEnterPlanes = 2;
+// Headdim columns one walk item or one scan workgroup covers; headdim is a
+// multiple of it.
+constexpr int kHeadBlock = 64;
+// Largest dstate block of one walk item.
+constexpr int kWalkStateBlock = 128;
 
 // 16-bit io value <-> bits <-> fp32.
 template <typename T>
@@ -205,28 +211,29 @@ __device__ __forceinline__ float bload_f32(Rsrc r, uint32_t off) {
 // Four consecutive state-type elements at byte offset `off` of a buffer
 // descriptor, as fp32 (one 16-byte load for fp32, one 8-byte load otherwise),
 // and back.
+// `soff` is a wave-uniform part of the offset (it travels in a scalar register).
 template <typename ST>
-__device__ __forceinline__ f32x4 bload_state4(Rsrc r, uint32_t off) {
+__device__ __forceinline__ f32x4 bload_state4(Rsrc r, uint32_t off, uint32_t soff) {
     if constexpr (sizeof(ST) == 4) {
-        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
     } else {
         typedef ST st4 __attribute__((ext_vector_type(4)));
-        const st4 v = __builtin_bit_cast(st4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+        const st4 v = __builtin_bit_cast(st4, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
         return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
                      static_cast<float>(v[3])};
     }
 }
 template <typename ST>
-__device__ __forceinline__ void bstore_state4(Rsrc r, uint32_t off, f32x4 v) {
+__device__ __forceinline__ void bstore_state4(Rsrc r, uint32_t off, uint32_t soff, f32x4 v) {
     typedef ST st4 __attribute__((ext_vector_type(4)));
     st4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = static_cast<ST>(v[i]);
     if constexpr (sizeof(ST) == 4) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), r, off, soff, 0);
     } else {
         typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), r, off, soff, 0);
     }
 }
 
@@ -583,13 +590,18 @@ __host__ __device__ constexpr unsigned walk_lds_bytes(int P, int N) {
     return 2u * (N + 2 * P) * kWalkPitch;
 }
 
-template <typename IT, typename ST, int P, int N, int Q>
+template <typename IT, typename ST, int N, int Q>
 __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_walk_kernel(const SsdParams p) {
+    // N is the dstate block of one item (the whole dstate up to 128, else 128 of
+    // it) and P = kHeadBlock the headdim block: the state's (p, n) entries evolve
+    // independently, so a head's state splits into blocks walked as items of
+    // their own. PF and NF are the full headdim and dstate (row strides).
+    constexpr int P = kHeadBlock;
     typedef typename Mfma<IT>::v8 v8;
     constexpr int NT = walk_threads(N), NW = NT / 64;
     constexpr int KB = Q < kWalkKB ? Q : kWalkKB, XP = kWalkPitch;
     constexpr int NSB = Q / KB;                          // blocks per chunk
-    static_assert(P == 64 && NW == 2 * (N / 32), "waves: dstate row blocks x headdim halves");
+    static_assert(NW == 2 * (N / 32), "waves: dstate row blocks x headdim halves");
     constexpr int XQ = P / 8, BQ = N / 8;                // 16-byte pieces of a token's x / B row
     constexpr int XN = (KB / 2) * XQ, BN = (KB / 2) * BQ;  // two-token pieces per block
     constexpr int XPASS = XN / NT, BPASS = BN / NT;
@@ -605,20 +617,22 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
     unsigned short* xhi = bt + N * XP;                             // [P][XP]
     unsigned short* xlo = xhi + P * XP;
 
-    const int H = p.nheads;
-    const int64_t nitems = static_cast<int64_t>(ld_uniform(p.walk_info)) * H;
-    const uint32_t xrow = static_cast<uint32_t>(H * P * 2), brow = static_cast<uint32_t>(p.ngroups * N * 2);
-    const int64_t tile = static_cast<int64_t>(H) * P * N;
+    const int H = p.nheads, PF = p.headdim, NF = p.dstate;
+    const int PB = PF / P, NB = NF / N;                  // headdim and dstate blocks
+    const int SB = PB * NB;                              // items per (run, head)
+    const int64_t nitems = static_cast<int64_t>(ld_uniform(p.walk_info)) * H * SB;
+    const uint32_t xrow = static_cast<uint32_t>(H * PF * 2), brow = static_cast<uint32_t>(p.ngroups * NF * 2);
+    const int64_t tile = static_cast<int64_t>(H) * PF * NF;
     const bool lists = !p.return_all && p.batch > 0;
     // First element of chunk c's entering state for head h (both planes).
-    auto enter_tile = [&](int64_t c, int h) { return (c * H + h) * (kEnterPlanes * P * N); };
+    auto enter_tile = [&](int64_t c, int h) { return (c * H + h) * (kEnterPlanes * static_cast<int64_t>(PF) * NF); };
 
     // Workgroups are dealt to the XCDs round robin, so with a grid of a multiple
     // of the XCD count each XCD always sees the same residue of item % XCDs.
     // Heads are permuted so that residue x means the contiguous heads
     // [x H / XCDs, (x + 1) H / XCDs): every XCD works on every run, and the
     // heads sharing B rows (a group, or part of one) share one L2.
-    const bool by_xcd = H % ssu::kXcds == 0 && gridDim.x % ssu::kXcds == 0;
+    const bool by_xcd = (H * SB) % ssu::kXcds == 0 && gridDim.x % ssu::kXcds == 0;
     // Items are dealt in rounds of one per workgroup, every other round in
     // reverse ("snake" order): with the runs longest first, a workgroup that
     // got one of the longest walks gets one of the shortest next.
@@ -629,26 +643,32 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
             if (round * G >= nitems) break;
             continue;  // this round's tail is short; a reversed round may still hold an item
         }
-        const int r = static_cast<int>(item / H), u = static_cast<int>(item % H);
-        const int h = by_xcd ? (u % ssu::kXcds) * (H / ssu::kXcds) + u / ssu::kXcds : u;
+        // (run, head, block) with the H * SB (head, block) pairs as "virtual heads"
+        // permuted like the heads above: an XCD's share is whole heads.
+        const int HS = H * SB;
+        const int r = static_cast<int>(item / HS), u = static_cast<int>(item % HS);
+        const int vh = by_xcd ? (u % ssu::kXcds) * (HS / ssu::kXcds) + u / ssu::kXcds : u;
+        const int h = vh / SB, pb = (vh % SB) / NB, nb = vh % NB;
         const int c0 = ld_uniform(p.walk_first + r), nc = ld_uniform(p.walk_len + r);
         const int g = h / p.heads_per_group;
-        const IT* xh = static_cast<const IT*>(p.x) + h * P;
-        const IT* bg = static_cast<const IT*>(p.B) + g * N;
-        const int64_t hs = static_cast<int64_t>(h) * P * N;
+        const IT* xh = static_cast<const IT*>(p.x) + h * PF + pb * P;
+        const IT* bg = static_cast<const IT*>(p.B) + g * NF + nb * N;
+        // This item's block of the head's [PF][NF] state: rows pb P.., columns nb N..
+        const int64_t hs = static_cast<int64_t>(h) * PF * NF + static_cast<int64_t>(pb) * P * NF + nb * N;
+        // Bytes from the block's first element to past its last, rows NF apart.
+        auto block_bytes = [&](int esz) { return static_cast<uint32_t>(((P - 1) * NF + N) * esz); };
         // Offset of this lane's four consecutive state elements of tile (nt, qt)
-        // inside the head's [P][N] block.
-        auto local = [&](int nt, int qt) {
-            return static_cast<uint32_t>((q0 + 16 * qt + lane % 16) * N + n0 + 16 * nt + 4 * (lane / 16));
-        };
+        // inside the block: a per-lane part and a wave-uniform part per tile.
+        const uint32_t lane_el = static_cast<uint32_t>((q0 + lane % 16) * NF + n0 + 4 * (lane / 16));
+        auto tile_el = [&](int nt, int qt) { return static_cast<uint32_t>(16 * qt * NF + 16 * nt); };
 
         // The operands of one block: x and B rows of tokens [s0, s0 + KB) of chunk c
         // (zeros past its end) and the weights of the token pairs.
         u16x8 rx[XPASS][2], rb[BPASS][2];
         float2 rw[XPASS];
         auto fetch = [&](const ChunkDesc& d, int c, int s0) {
-            const Rsrc xr = make_rsrc(xh + d.lo * H * P, d.len * xrow);
-            const Rsrc br = make_rsrc(bg + d.lo * p.ngroups * N, d.len * brow);
+            const Rsrc xr = make_rsrc(xh + d.lo * H * PF, d.len * xrow);
+            const Rsrc br = make_rsrc(bg + d.lo * p.ngroups * NF, d.len * brow);
             const Rsrc wr = make_rsrc(p.w + (static_cast<int64_t>(c) * H + h) * Q, 4u * Q);
 #pragma unroll
             for (int i = 0; i < XPASS; ++i) {
@@ -673,11 +693,12 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
         const bool init = d.enter >= 0 && d.enter < p.batch;
         if (init) {
             const Rsrc ir = make_rsrc(static_cast<const ST*>(p.init) + d.enter * tile + hs,
-                                      P * N * sizeof(ST));
+                                      block_bytes(sizeof(ST)));
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) acc[nt][qt] = bload_state4<ST>(ir, sizeof(ST) * local(nt, qt));
+                for (int qt = 0; qt < 2; ++qt)
+                    acc[nt][qt] = bload_state4<ST>(ir, sizeof(ST) * lane_el, sizeof(ST) * tile_el(nt, qt));
         } else {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
@@ -686,13 +707,17 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
         }
 
         // The state as the next chunk's entering state: the high and the low
-        // planes [2][P][N] (io type) at dst, through the B^T area of LDS so that
+        // planes of this item's block (io type; dst = the block's first element of
+        // the high plane, rows NF apart, the low plane PF * NF further), through
+        // the B^T area of LDS so that
         // every store writes whole 16-byte pieces of whole rows: each wave drops
         // its part of S^T into LDS (16-byte chunks of row p permuted by p, which
         // spreads the writes of sixteen rows over the banks), then the workgroup
         // copies the rows out. The caller makes sure every wave is done with the
         // B^T area; the next use of LDS is behind a barrier.
         auto store_enter = [&](IT* dst) {
+            // Both planes' rows of the block, from dst on (the low plane PF * NF further).
+            const Rsrc er = make_rsrc(dst, static_cast<uint32_t>((PF * NF + (P - 1) * NF + N) * 2));
             typedef unsigned short t4 __attribute__((ext_vector_type(4)));
             constexpr int CPR = N * 2 / 16;  // 16-byte chunks per row
             constexpr unsigned PLANE = P * N * 2;
@@ -724,23 +749,25 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
                     const int idx = tid + NT * i, pr = idx / CPR, ch = idx % CPR;
                     const u32x4 v = *reinterpret_cast<const u32x4*>(lt + pl * PLANE + pr * N * 2 +
                                                                     ((ch ^ (pr % CPR)) * 16));
-                    *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(dst) + pl * PLANE + 16 * idx) = v;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, er, static_cast<uint32_t>(pr * NF * 2 + ch * 16),
+                                                           static_cast<uint32_t>(pl * PF * NF * 2), 0);
                 }
         };
         // The run's initial state is the first chunk's entering state too (LDS
         // is free: the previous item ended with a barrier, and the first block
         // stages behind one).
-        if (init) store_enter(static_cast<IT*>(p.s16) + enter_tile(c0, h));
+        if (init) store_enter(static_cast<IT*>(p.s16) + enter_tile(c0, h) + (hs - static_cast<int64_t>(h) * PF * NF));
 
         // The returned states, written from the accumulators directly (each
         // chunk's with return_intermediate_states, else only the requests'
         // last chunks').
         auto put = [&](int64_t row) {
-            const Rsrc sr = make_rsrc(static_cast<ST*>(p.states) + row * tile + hs, P * N * sizeof(ST));
+            const Rsrc sr = make_rsrc(static_cast<ST*>(p.states) + row * tile + hs, block_bytes(sizeof(ST)));
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) bstore_state4<ST>(sr, sizeof(ST) * local(nt, qt), acc[nt][qt]);
+                for (int qt = 0; qt < 2; ++qt)
+                    bstore_state4<ST>(sr, sizeof(ST) * lane_el, sizeof(ST) * tile_el(nt, qt), acc[nt][qt]);
         };
 
         // Per-chunk scalars are requested a chunk ahead of their use.
@@ -829,7 +856,7 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
             // goes on, and the returned states (state type).
             if (more) {
                 lds_barrier();  // every wave is done with this block's operands
-                store_enter(static_cast<IT*>(p.s16) + enter_tile(c + 1, h));
+                store_enter(static_cast<IT*>(p.s16) + enter_tile(c + 1, h) + (hs - static_cast<int64_t>(h) * PF * NF));
             }
             if (p.return_all) {
                 put(c);
@@ -865,8 +892,12 @@ __host__ __device__ constexpr int scan_epilogue_pitch(int P) { return P + 4; }
 // Waves per SIMD the scan is compiled for (its register budget): four for
 // chunks of 256 (two 8-wave workgroups per CU, as many as its LDS allows at
 // dstate 128), three for chunks of 128 (three 4-wave workgroups at dstate 128;
-// its two tiles of C B^T in flight need more than 128 registers).
-__host__ __device__ constexpr int scan_waves_per_simd(int Q) { return Q >= 256 ? 4 : 3; }
+// its two tiles of C B^T in flight need more than 128 registers). At dstate 256
+// the entering state's planes leave LDS room for one workgroup per CU: two
+// waves per SIMD for chunks of 256, one for chunks of 128.
+__host__ __device__ constexpr int scan_waves_per_simd(int N, int Q) {
+    return N >= 256 ? (Q >= 256 ? 2 : 1) : (Q >= 256 ? 4 : 3);
+}
 // Blocks of 32 C B^T columns each tile has in flight: one for chunks of 256
 // (within 128 registers), two for chunks of 128.
 __host__ __device__ constexpr int scan_cb_depth(int Q) { return Q >= 256 ? 1 : 2; }
@@ -879,12 +910,15 @@ __host__ __device__ constexpr unsigned scan_lds_bytes(int P, int N, int Q) {
 
 // x^T and the entering state are stored permuted by swz().
 
-// One workgroup per (chunk, head); wave w owns token tiles w and w + Q / 32.
+// One workgroup per (chunk, head, block of kHeadBlock headdim columns); wave w
+// owns token tiles w and 2 NW - 1 - w. The outputs of different headdim columns
+// share nothing but the decayed C B^T entries, which each block recomputes.
 // Every load the workgroup needs before its first product -- steps, the x
 // tile, the entering state, the first C operands, D -- is issued at the start,
 // each product's next operands before its current matrix-core work.
-template <typename IT, typename ST, int P, int N, int Q>
-__global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_scan_kernel(const SsdParams p) {
+template <typename IT, typename ST, int N, int Q>
+__global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(N, Q)) void ssd_scan_kernel(const SsdParams p) {
+    constexpr int P = kHeadBlock;
     typedef typename Mfma<IT>::v8 v8;
     constexpr int NT = scan_threads(Q), NW = NT / 64;
     constexpr int PT = P / 16, TT = 2, KN = N / 32;
@@ -894,9 +928,11 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
     static_assert(XPASS * NT == (Q / 2) * (P / 8) && SPASS * NT == P * (N / 8), "passes");
     static_assert((SP * 2) % 16 == 0 && (XP * 2) % 16 == 0, "16-byte rows");
 
+    const int PF = p.headdim, PBK = PF / P;
     const int64_t wg = xcd_order(blockIdx.x, gridDim.x);
-    const int64_t c = wg / p.nheads;
-    const int h = static_cast<int>(wg % p.nheads);
+    const int64_t c = wg / (static_cast<int64_t>(p.nheads) * PBK);
+    const int h = static_cast<int>((wg / PBK) % p.nheads);
+    const int pb = static_cast<int>(wg % PBK);
     const ChunkDesc d = load_desc(p, c);
     if (d.len == 0) return;
     const int len = d.len;
@@ -915,8 +951,9 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
     unsigned short* xv = sS + kEnterPlanes * P * SP;
 
     const IT* Cp = static_cast<const IT*>(p.C);
-    const uint32_t xrow = static_cast<uint32_t>(H * P * 2);
-    const int64_t xoff = (d.lo * H + h) * P;  // the chunk's first x / z / out row of head h
+    const uint32_t xrow = static_cast<uint32_t>(H * PF * 2);
+    // The chunk's first x / z / out row of head h, at this block's columns.
+    const int64_t xoff = (d.lo * H + h) * PF + pb * P;
 
     // ---- loads issued up front.
     // cum_s log2(e) - log2(v_s) (tid < Q), then cum_s log2(e).
@@ -934,13 +971,14 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
     // The entering state's two planes (zeros for a chunk that opens a request
     // without one).
     const bool has_state = d.enter != kEnterZero;
-    const Rsrc sr = make_rsrc(static_cast<const IT*>(p.s16) + (c * H + h) * kEnterPlanes * P * N,
-                              has_state ? kEnterPlanes * P * N * 2 : 0);
+    // This block's rows of each plane (planes PF * N apart, rows contiguous).
+    const Rsrc sr = make_rsrc(static_cast<const IT*>(p.s16) + (c * H + h) * kEnterPlanes * PF * N + pb * P * N,
+                              has_state ? (PF + P) * N * 2 : 0);
     u16x8 rs[kEnterPlanes][SPASS];
 #pragma unroll
     for (int pl = 0; pl < kEnterPlanes; ++pl)
 #pragma unroll
-        for (int r = 0; r < SPASS; ++r) rs[pl][r] = bload(sr, pl * P * N * 2 + 16 * (tid + NT * r));
+        for (int r = 0; r < SPASS; ++r) rs[pl][r] = bload(sr, pl * PF * N * 2 + 16 * (tid + NT * r));
     // C operands of the entering-state product, first k step.
     // Token tiles of this wave: w and 2 NW - 1 - w, so that every wave's pair
     // covers about the same share of the causal triangle (tile i needs i / 2 + 1
@@ -960,8 +998,8 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
 #pragma unroll
     for (int k = 0; k < TT; ++k) cf[k] = c_frag(k, 0);
     // The skip coefficient of headdim row tid (zero without D).
-    const Rsrc dr = make_rsrc(p.D, p.D ? static_cast<uint32_t>((p.D_per_dim ? H * P : H) * 4) : 0u);
-    const float dcoef = bload_f32(dr, 4u * (p.D_per_dim ? h * P + min(tid, P - 1) : h));
+    const Rsrc dr = make_rsrc(p.D, p.D ? static_cast<uint32_t>((p.D_per_dim ? H * PF : H) * 4) : 0u);
+    const float dcoef = bload_f32(dr, 4u * (p.D_per_dim ? h * PF + pb * P + min(tid, P - 1) : h));
 
     // z rows of the epilogue (zeros without z): lane l finishes 8 consecutive
     // columns of rows l / 8 and l / 8 + 8 of each of its tiles, so every store
@@ -1197,7 +1235,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(Q)) void ssd_s
                     o[e] = bits_of<IT>(y);
                 }
                 __builtin_nontemporal_store(
-                    o, reinterpret_cast<u16x8*>(op + xoff + static_cast<int64_t>(t) * H * P + ec));
+                    o, reinterpret_cast<u16x8*>(op + xoff + static_cast<int64_t>(t) * H * PF + ec));
             }
         }
         ssu::wave_lds_sync();  // the next tile reuses the scratch
@@ -1211,10 +1249,13 @@ namespace ssd {
 // The launches of one prefill, on `stream`: the front (request list, prep and
 // C B^T), the state walk, the scan. Dispatches on the state type and the
 // (headdim, dstate, chunk) instance.
-template <typename IT, typename ST, int P, int N, int Q>
+template <typename IT, typename ST, int N, int Q>
 hipError_t launch_instance(const SsdParams& p, hipStream_t stream) {
+    constexpr int NB = N < kWalkStateBlock ? N : kWalkStateBlock;  // dstate block of a walk item
+    const int64_t blocks = static_cast<int64_t>(p.headdim / kHeadBlock) * (N / NB);
     const int64_t front = front_blocks<Q>(p.nchunks, p.nheads, p.ngroups);
-    if (front > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (front > 0x7fffffff || p.nchunks * p.nheads * (p.headdim / kHeadBlock) > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((ssd_front_kernel<IT, N, Q>), dim3(static_cast<unsigned>(front)),
                        dim3(kThreads), 0, stream, p);
     // The walk runs as many workgroups as fit on the device at once (each loops
@@ -1226,29 +1267,31 @@ hipError_t launch_instance(const SsdParams& p, hipStream_t stream) {
     int fit = resident[dev].load(std::memory_order_relaxed);
     if (fit == 0) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ssd_state_walk_kernel<IT, ST, P, N, Q>,
-                                                         walk_threads(N), walk_lds_bytes(P, N)) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ssd_state_walk_kernel<IT, ST, NB, Q>,
+                                                         walk_threads(NB), walk_lds_bytes(kHeadBlock, NB)) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return hipErrorInvalidValue;
         fit = per_cu * cus > 0 ? per_cu * cus : 1;
         resident[dev].store(fit, std::memory_order_relaxed);
     }
-    const int64_t walkers = std::min<int64_t>(fit, p.nchunks * p.nheads);
-    hipLaunchKernelGGL((ssd_state_walk_kernel<IT, ST, P, N, Q>), dim3(static_cast<unsigned>(walkers)),
-                       dim3(walk_threads(N)), walk_lds_bytes(P, N), stream, p);
-    hipLaunchKernelGGL((ssd_scan_kernel<IT, ST, P, N, Q>),
-                       dim3(static_cast<unsigned>(p.nchunks * p.nheads)), dim3(scan_threads(Q)),
-                       scan_lds_bytes(P, N, Q), stream, p);
+    const int64_t walkers = std::min<int64_t>(fit, p.nchunks * p.nheads * blocks);
+    hipLaunchKernelGGL((ssd_state_walk_kernel<IT, ST, NB, Q>), dim3(static_cast<unsigned>(walkers)),
+                       dim3(walk_threads(NB)), walk_lds_bytes(kHeadBlock, NB), stream, p);
+    hipLaunchKernelGGL((ssd_scan_kernel<IT, ST, N, Q>),
+                       dim3(static_cast<unsigned>(p.nchunks * p.nheads * (p.headdim / kHeadBlock))),
+                       dim3(scan_threads(Q)), scan_lds_bytes(kHeadBlock, N, Q), stream, p);
     return hipGetLastError();
 }
 
 template <typename IT, typename ST>
 hipError_t launch_shape(const SsdParams& p, int P, int N, int Q, hipStream_t stream) {
-    if (P != 64) return hipErrorInvalidValue;
-    if (N == 128 && Q == 256) return launch_instance<IT, ST, 64, 128, 256>(p, stream);
-    if (N == 128 && Q == 128) return launch_instance<IT, ST, 64, 128, 128>(p, stream);
-    if (N == 64 && Q == 256) return launch_instance<IT, ST, 64, 64, 256>(p, stream);
-    if (N == 64 && Q == 128) return launch_instance<IT, ST, 64, 64, 128>(p, stream);
+    if (P % kHeadBlock) return hipErrorInvalidValue;
+    if (N == 128 && Q == 256) return launch_instance<IT, ST, 128, 256>(p, stream);
+    if (N == 128 && Q == 128) return launch_instance<IT, ST, 128, 128>(p, stream);
+    if (N == 64 && Q == 256) return launch_instance<IT, ST, 64, 256>(p, stream);
+    if (N == 64 && Q == 128) return launch_instance<IT, ST, 64, 128>(p, stream);
+    if (N == 256 && Q == 256) return launch_instance<IT, ST, 256, 256>(p, stream);
+    if (N == 256 && Q == 128) return launch_instance<IT, ST, 256, 128>(p, stream);
     return hipErrorInvalidValue;
 }
 

@@ -8,9 +8,12 @@ namespace ssd {
 
 struct SsdParams;
 
-// Headdim, dstate and chunk sizes with compiled kernels.
+// Headdim, dstate and chunk sizes with compiled kernels: headdim a multiple of
+// 64 up to 256 (the kernels work on 64-column blocks), dstate 64, 128 or 256,
+// chunks of 128 or 256 tokens.
 inline bool supported_shape(int64_t P, int64_t N, int64_t Q) {
-    return P == 64 && (N == 64 || N == 128) && (Q == 128 || Q == 256);
+    return P >= 64 && P <= 256 && P % 64 == 0 && (N == 64 || N == 128 || N == 256) &&
+           (Q == 128 || Q == 256);
 }
 
 // All launches of one prefill; hipErrorInvalidValue for an instance not built.

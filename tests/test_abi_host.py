@@ -285,7 +285,8 @@ def ssd(lib, **kw):
     (dict(last_chunk_indices=0), INV, "last_chunk_indices"),
     (dict(states=0), INV, "states is required"),
     (dict(headdim=80), UNS, "no kernel"),
-    (dict(dstate=256), UNS, "no kernel"),
+    (dict(dstate=512), UNS, "no kernel"),
+    (dict(headdim=320), UNS, "no kernel"),
     (dict(chunk_size=64), UNS, "no kernel"),
     (dict(x=addr(1) + 8), UNS, "16-byte aligned"),
     (dict(states=addr(14) + 4), UNS, "states must be 16-byte aligned"),

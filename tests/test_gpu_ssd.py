@@ -48,6 +48,24 @@ CASES = {
     "more_runs_than_ranked": dict(lengths=[1 + (7 * i) % 5 for i in range(2096)]
                                   + [300, 700, 129, 257], H=2, P=64, N=64, G=1, chunk=128,
                                   with_init=True),
+    # headdim 128 (two 64-column blocks in the walk and the scan); bf16 io, fp32
+    # states, chunk 256, ragged requests, initial states, gate.
+    "headdim128": dict(lengths=[1, 255, 300, 700], H=4, P=128, N=128, G=2, chunk=256,
+                       with_init=True),
+    # headdim 128 with fp16 io, bf16 states, dstate 64, chunk 128, every chunk's state.
+    "headdim128_f16_all_chunks": dict(lengths=[130, 5, 400], H=2, P=128, N=64, G=1, chunk=128,
+                                      io="f16", state_dtype="bf16",
+                                      return_intermediate_states=True),
+    # dstate 256 (two 128-row blocks in the walk, eight k steps in the scan).
+    "dstate256": dict(lengths=[37, 256, 600], H=4, P=64, N=256, G=2, chunk=256, with_init=True),
+    "dstate256_q128_f16_states": dict(lengths=[129, 700, 3], H=2, P=64, N=256, G=1, chunk=128,
+                                      state_dtype="f16", with_init=True, D_per_dim=True),
+    # both at once, and headdim 192 and 256
+    "headdim128_dstate256": dict(lengths=[300, 90], H=2, P=128, N=256, G=1, chunk=128,
+                                 with_init=True, return_intermediate_states=True),
+    "headdim192": dict(lengths=[200, 333], H=2, P=192, N=128, G=1, chunk=256, with_init=True),
+    "headdim256_f16": dict(lengths=[150, 260], H=2, P=256, N=64, G=2, chunk=128, io="f16",
+                           with_init=True, D_per_dim=True),
 }
 
 
