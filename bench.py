@@ -203,6 +203,20 @@ def state_copies(acc):
     return max(1, -(-MIN_TOUCH_BYTES // max(touched, 1)))
 
 
+def prepared_calls(w, copies=1):
+    """Prepared one-token calls (checks and marshalling done once) on `copies`
+    copies of the state cache."""
+    import torch
+    import selective_state_update_ssu_amd as ssu
+
+    out = torch.empty_like(w.x)
+    states = [w.state] + [w.state.clone() for _ in range(copies - 1)]
+    return [ssu.prepare_one_token(st, w.x, w.dt, w.A, w.B, w.C, out, D=w.D, z=w.z,
+                                  dt_bias=w.dt_bias, dt_softplus=w.dt_softplus,
+                                  state_batch_indices=w.src, dst_state_batch_indices=w.dst)
+            for st in states]
+
+
 def rotated_calls(w, hpb, lpl=0, copies=1):
     """`copies` calls of the workload, each on its own copy of the state cache
     (the first on w.state itself)."""
@@ -785,8 +799,9 @@ def run_workload(name, steps, warmup, hpb, lpl=0):
 def sweep(steps, warmup):
     """One-token calls of the Mamba2-2.7B head shape (80 heads x 64 rows, bf16 io
     with gate, default launch shape): (1) fp32 state, dstate 128, batch 1 ..
-    1024, timed back to back and as `steps` calls captured in one HIP graph
-    (the graph shows the device time where the host bounds the eager rate);
+    1024, timed back to back (regular and prepared calls) and as `steps` calls
+    captured in one HIP graph (the graph shows the device time where the host
+    bounds the eager rate);
     (2) dstate 16 .. 256 with fp32 and bf16 state, batch chosen for ~1.35 GB
     per call. Prints one JSON line per point."""
     import statistics
@@ -806,6 +821,7 @@ def sweep(steps, warmup):
         copies = state_copies(acc)
         calls = rotated_calls(w, 0, copies=copies)
         eager = med(calls)
+        prepared = med(prepared_calls(w, copies))
         length = max(steps, copies)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -829,7 +845,7 @@ def sweep(steps, warmup):
         nbytes = acc["bytes"]
         replayed = statistics.median(ts)
         print(json.dumps({"sweep": "batch", "batch": batch, "state_copies": copies,
-                          "eager_us": eager, "graph_us": replayed,
+                          "eager_us": eager, "prepared_us": prepared, "graph_us": replayed,
                           "graph_gbps": nbytes / replayed / 1e3}), flush=True)
         del graph, w, calls
         torch.cuda.empty_cache()

@@ -33,7 +33,8 @@ import torch
 
 from . import _abi
 
-__all__ = ["ssu_one_token", "ssu_packed_varlen", "update_replayssm_ring_trackers",
+__all__ = ["ssu_one_token", "ssu_packed_varlen", "prepare_one_token", "prepare_packed_varlen",
+           "PreparedCall", "update_replayssm_ring_trackers",
            "reset_replayssm_ring_trackers", "commit_replayssm_ring_trackers",
            "ssd_combined_fwd_varlen", "ssd_workspace_bytes", "reset_ssd_workspaces",
            "library_path", "library"]
@@ -233,10 +234,19 @@ def ssu_one_token(state, x, dt, A, B, C, out=None, *, D=None, z=None, dt_bias=No
     stored fp16/bf16 states with Philox4x32-`philox_rounds`.
     heads_per_block / loads_per_lane / tile_order pick the launch shape (0: the
     library default)."""
-    lib = library()
-    op, out, batch, _keep = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
-                                      pad_slot_id, disable_state_update, heads_per_block,
-                                      loads_per_lane, tile_order, rand_seed, philox_rounds)
+    return _one_token_call(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
+                           state_batch_indices, dst_state_batch_indices, pad_slot_id,
+                           disable_state_update, rand_seed, philox_rounds, heads_per_block,
+                           loads_per_lane, tile_order)(stream)
+
+
+def _one_token_call(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
+                    state_batch_indices, dst_state_batch_indices, pad_slot_id,
+                    disable_state_update, rand_seed, philox_rounds, heads_per_block,
+                    loads_per_lane, tile_order):
+    op, out, batch, keep = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
+                                     pad_slot_id, disable_state_update, heads_per_block,
+                                     loads_per_lane, tile_order, rand_seed, philox_rounds)
     src, src_dt = _index("state_batch_indices", state_batch_indices, state.device)
     dst, dst_dt = _index("dst_state_batch_indices", dst_state_batch_indices, state.device)
     for name, t in (("state_batch_indices", src), ("dst_state_batch_indices", dst)):
@@ -245,10 +255,48 @@ def ssu_one_token(state, x, dt, A, B, C, out=None, *, D=None, z=None, dt_bias=No
     args = _abi.OneTokenArgs(struct_size=ctypes.sizeof(_abi.OneTokenArgs), op=op, batch=batch,
                              src_slots=_ptr(src), src_dtype=src_dt,
                              dst_slots=_ptr(dst), dst_dtype=dst_dt)
-    rc = lib.ssu_one_token(ctypes.byref(args), _stream(state.device, stream))
-    if rc != _abi.SSU_OK:
-        _raise(lib, rc, "ssu_one_token")
-    return out
+    return PreparedCall("ssu_one_token", args, state.device, out,
+                        (state, x, dt, B, C, z, src, dst, rand_seed) + keep)
+
+
+class PreparedCall:
+    """A decode call whose arguments were checked and marshalled once: calling it
+    launches the update again on the same tensors (their current contents) and
+    returns `out`. It keeps every tensor it points at alive. For decode loops
+    that reuse their buffers from step to step, as graph-captured loops do: the
+    per-call host work is one C call (see `prepare_one_token`)."""
+
+    __slots__ = ("_entry", "_args", "_ref", "_device", "out", "_keep")
+
+    def __init__(self, entry, args, device, out, keep):
+        self._entry, self._args, self._device, self.out, self._keep = entry, args, device, out, keep
+        self._ref = ctypes.byref(args)
+
+    def __call__(self, stream=None):
+        """Launch on `stream` (a torch.cuda.Stream; default: the current stream)."""
+        lib = library()
+        s = torch.cuda.current_stream(self._device) if stream is None else stream
+        rc = getattr(lib, self._entry)(self._ref, ctypes.c_void_p(s.cuda_stream))
+        if rc != _abi.SSU_OK:
+            _raise(lib, rc, self._entry)
+        return self.out
+
+
+def prepare_one_token(state, x, dt, A, B, C, out=None, *, D=None, z=None, dt_bias=None,
+                      dt_softplus=False, state_batch_indices=None,
+                      dst_state_batch_indices=None, pad_slot_id=-1,
+                      disable_state_update=False, rand_seed=None, philox_rounds=10,
+                      heads_per_block=0, loads_per_lane=0, tile_order=0):
+    """`ssu_one_token`'s checks and marshalling, done once. Returns a
+    PreparedCall; `call(stream=None)` runs the update on the tensors given here
+    (their contents at the time of the call) and returns out. Temporaries are
+    made now, on the current stream: a missing out, and contiguous copies of
+    per-head parameters given as tied views (A, D and dt_bias are then read as
+    they were at preparation, as model constants are)."""
+    return _one_token_call(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
+                           state_batch_indices, dst_state_batch_indices, pad_slot_id,
+                           disable_state_update, rand_seed, philox_rounds, heads_per_block,
+                           loads_per_lane, tile_order)
 
 
 def _table(name, t, device, nseq):
@@ -290,7 +338,38 @@ def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens=None, out=None, *,
     form (every operand 4-D), which runs as `batch` regular sequences of `steps`
     rows with no starts tensor. Without cu_seqlens a packed x must have one row
     per sequence."""
-    lib = library()
+    call, result = _packed_call(state, x, dt, A, B, C, cu_seqlens, out, num_accepted_tokens,
+                                state_batch_indices, dst_state_batch_indices, D, z, dt_bias,
+                                dt_softplus, pad_slot_id, disable_state_update, rand_seed,
+                                philox_rounds, steps, heads_per_block, loads_per_lane, tile_order)
+    call(stream)
+    return result
+
+
+def prepare_packed_varlen(state, x, dt, A, B, C, cu_seqlens=None, out=None, *,
+                          num_accepted_tokens=None, state_batch_indices=None,
+                          dst_state_batch_indices=None, D=None, z=None, dt_bias=None,
+                          dt_softplus=False, pad_slot_id=-1, disable_state_update=False,
+                          rand_seed=None, philox_rounds=10, steps=None, heads_per_block=0,
+                          loads_per_lane=0, tile_order=0):
+    """`ssu_packed_varlen`'s checks and marshalling, done once; returns a
+    PreparedCall whose `out` is the packed (or, for a dense x, the dense) out."""
+    call, result = _packed_call(state, x, dt, A, B, C, cu_seqlens, out, num_accepted_tokens,
+                                state_batch_indices, dst_state_batch_indices, D, z, dt_bias,
+                                dt_softplus, pad_slot_id, disable_state_update, rand_seed,
+                                philox_rounds, steps, heads_per_block, loads_per_lane, tile_order,
+                                no_copies=True)
+    call.out = result
+    return call
+
+
+def _packed_call(state, x, dt, A, B, C, cu_seqlens, out, num_accepted_tokens,
+                 state_batch_indices, dst_state_batch_indices, D, z, dt_bias, dt_softplus,
+                 pad_slot_id, disable_state_update, rand_seed, philox_rounds, steps,
+                 heads_per_block, loads_per_lane, tile_order, no_copies=False):
+    """(PreparedCall, the out tensor the public call returns). no_copies: refuse
+    dense operands whose flattening would copy them (a prepared call must read
+    the caller's tensors, not copies made once)."""
     dense_out = None
     dense_shape = None
     seq_len = 0
@@ -304,10 +383,14 @@ def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens=None, out=None, *,
             dense_out = out
             out = out.view(rows, *out.shape[2:])
         lead = (batch, dsteps)
+        dense = (x, dt, B, C, z)
         dt = _flatten_dense("dt", dt, lead, min_dim=3)
         B, C = _flatten_dense("B", B, lead), _flatten_dense("C", C, lead)
         z = _flatten_dense("z", z, lead)
         x = x.reshape(rows, *x.shape[2:])
+        if no_copies and any(a is not None and a.data_ptr() != b.data_ptr()
+                             for a, b in zip(dense, (x, dt, B, C, z))):
+            raise ValueError("a prepared dense call needs operands that flatten without a copy")
         if cu_seqlens is None:
             seq_len = max(dsteps, 1)
     op, out, rows, _keep = _operands(state, x, dt, A, B, C, out, D, z, dt_bias, dt_softplus,
@@ -358,12 +441,12 @@ def ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens=None, out=None, *,
         src_table=_ptr(src), src_dtype=src_dt, src_seq_stride=sss, src_step_stride=sst,
         dst_table=_ptr(dst), dst_dtype=dst_dt, dst_seq_stride=dss, dst_step_stride=dst_st,
         steps=int(steps))
-    rc = lib.ssu_packed_varlen(ctypes.byref(args), _stream(state.device, stream))
-    if rc != _abi.SSU_OK:
-        _raise(lib, rc, "ssu_packed_varlen")
     if dense_out is not None:
-        return dense_out
-    return out.view(dense_shape) if dense_shape is not None else out
+        result = dense_out
+    else:
+        result = out.view(dense_shape) if dense_shape is not None else out
+    keep = (state, x, dt, B, C, z, out, cu, na, src, dst, rand_seed) + _keep
+    return PreparedCall("ssu_packed_varlen", args, state.device, out, keep), result
 
 
 # ------------------------------------------------------------ ring trackers

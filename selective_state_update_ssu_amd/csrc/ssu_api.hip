@@ -160,13 +160,13 @@ int check_operands(const ssu_operands& op, int64_t rows, bool work, bool packed)
 // (2 loads per lane, 2 heads per workgroup with an fp32 state, 1 with a 16-bit
 // one); a read-only call and the packed call, which writes several states per
 // state read, in larger ones (4 loads per lane, 2 heads per workgroup). Tile
-// order: each XCD takes an equal contiguous share of every sequence's tiles (a
-// block of its heads), which keeps each XCD streaming contiguous memory and
-// gives every XCD the same share of each sequence however their token counts
-// differ (1-2 % faster than contiguous ranges of sequences on the one-token
-// shapes, 3 % on varlen packed calls, whose contiguous ranges of sequences carry
-// unequal token counts); packed calls without cu_seqlens (every sequence the
-// same length) stream best with each XCD walking a contiguous range of tiles.
+// order: varlen packed calls let each XCD take an equal contiguous share of
+// every sequence's tiles (a block of its heads), which balances sequences of
+// unequal token counts over the XCDs (3 % faster than contiguous ranges of
+// sequences); one-token calls do so when that share is large (at least 256 KiB
+// of state per sequence and XCD: 1-2 % faster at 80-128 heads of 64 x 128 fp32)
+// and otherwise, like packed calls without cu_seqlens, let each XCD walk a
+// contiguous range of tiles (smaller states stream better in longer runs).
 struct Shape {
     int heads_per_block, loads_per_lane, xcd_order;  // xcd_order as in ssu::KernelParams
 };
@@ -175,14 +175,18 @@ Shape default_shape(const ssu_operands& op, bool packed, bool equal_lengths) {
     const bool read_only = op.disable_state_update != 0;
     Shape s;
     const bool sr = op.rand_seed && op.state_dtype != SSU_F32 && !read_only;
+    // Bytes of one sequence's state each XCD streams under per-sequence shares.
+    const int64_t share = op.nheads * op.headdim * op.dstate * (op.state_dtype == SSU_F32 ? 4 : 2) /
+                          ssu::kXcds;
+    const int one_token_order = share >= (256 << 10) ? 2 : 1;
     if (packed)
         s = {2, 4, equal_lengths ? 1 : 2};
     else if (read_only)
-        s = {2, 4, 2};
+        s = {2, 4, one_token_order};
     else if (sr)  // the Philox work of stochastic rounding wants bigger tiles
-        s = {1, 4, 2};
+        s = {1, 4, one_token_order};
     else
-        s = {op.state_dtype == SSU_F32 ? 2 : 1, 2, 2};
+        s = {op.state_dtype == SSU_F32 ? 2 : 1, 2, one_token_order};
     const int64_t hpg = op.nheads / op.ngroups;
     const int hmax = ssu::max_heads_per_block(static_cast<int>(op.dstate), packed);
     while (s.heads_per_block > 1 && (hpg % s.heads_per_block != 0 || s.heads_per_block > hmax))

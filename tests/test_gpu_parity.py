@@ -518,3 +518,48 @@ def test_threads_and_streams_match_a_single_thread():
     for (s_ref, o_ref), (s_got, o_got) in zip(ref, got):
         assert torch.equal(hz.bits(s_ref), hz.bits(s_got))
         assert torch.equal(hz.bits(o_ref), hz.bits(o_got))
+
+
+# ------------------------------------------------------------- prepared calls
+
+def test_prepared_calls_match_the_regular_calls():
+    """A prepared call (checks and marshalling done once) gives the regular
+    call's bits, and calling it again continues from the updated state, as two
+    regular steps do; one-token, packed and dense forms."""
+    import selective_state_update_ssu_amd as ssu
+    w = wl.one_token("prep1", 404, batch=9, H=8, P=64, N=128, G=2, nslots=20, device=DEV,
+                     pad_fraction=0.2)
+    kw = dict(D=w.D, z=w.z, dt_bias=w.dt_bias, dt_softplus=True, state_batch_indices=w.src,
+              dst_state_batch_indices=w.dst)
+    s_reg, s_prep = w.state.clone(), w.state.clone()
+    o_reg = torch.full_like(w.x, float("nan"))
+    o_prep = torch.full_like(w.x, float("nan"))
+    call = ssu.prepare_one_token(s_prep, w.x, w.dt, w.A, w.B, w.C, o_prep, **kw)
+    for _ in range(2):
+        ssu.ssu_one_token(s_reg, w.x, w.dt, w.A, w.B, w.C, o_reg, **kw)
+        assert call() is o_prep
+        torch.cuda.synchronize()
+        assert torch.equal(hz.bits(o_reg), hz.bits(o_prep))
+        assert torch.equal(hz.bits(s_reg), hz.bits(s_prep))
+
+    for dense in (False, True):
+        p = wl.packed("prep2", 405, nseq=6, max_len=3, H=4, P=64, N=64, G=1, nslots=40,
+                      device=DEV, lengths=None if not dense else [3] * 6, dense=dense)
+        pk = dict(num_accepted_tokens=p.num_accepted, state_batch_indices=p.src_table,
+                  dst_state_batch_indices=p.dst_table, D=p.D, dt_bias=p.dt_bias,
+                  dt_softplus=True)
+        s_reg, s_prep = p.state.clone(), p.state.clone()
+        if dense:
+            d4 = lambda t: None if t is None else t.view(6, 3, *t.shape[1:])
+            args = (d4(p.x), d4(p.dt), p.A, d4(p.B), d4(p.C), None)
+            pk["z"] = d4(p.z)
+        else:
+            args = (p.x, p.dt, p.A, p.B, p.C, p.cu_seqlens)
+            pk["z"] = p.z
+        o_reg = ssu.ssu_packed_varlen(s_reg, *args, **pk)
+        call = ssu.prepare_packed_varlen(s_prep, *args, **pk)
+        o_prep = call()
+        torch.cuda.synchronize()
+        assert o_prep.shape == o_reg.shape
+        assert torch.equal(hz.bits(o_reg), hz.bits(o_prep)), dense
+        assert torch.equal(hz.bits(s_reg), hz.bits(s_prep)), dense
