@@ -11,11 +11,14 @@ kernel. There is no fallback: without the built library every call raises.
     ssu_packed_varlen(state, x, dt, A, B, C, cu_seqlens, out=None, *,
                       num_accepted_tokens, state_batch_indices,
                       dst_state_batch_indices, ...)
+    prepare_one_token(...), prepare_packed_varlen(...)  -> PreparedCall
+        (the same arguments, checked and marshalled once; call() relaunches)
 
     ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens,
                             cu_chunk_seqlens, last_chunk_indices, seq_idx, out=None, *,
                             D, z, dt_bias, dt_softplus, dt_limit, initial_states,
-                            return_intermediate_states, state_dtype)
+                            return_intermediate_states, state_dtype, workspace,
+                            static_scratch)
 
 Operand shapes follow the MATE documentation page "Source code for mate.mamba"
 (`selective_state_update`): state [slots, heads, dim, dstate]; x, z, out
@@ -266,19 +269,19 @@ class PreparedCall:
     that reuse their buffers from step to step, as graph-captured loops do: the
     per-call host work is one C call (see `prepare_one_token`)."""
 
-    __slots__ = ("_entry", "_args", "_ref", "_device", "out", "_keep")
+    __slots__ = ("_entry", "_fn", "_args", "_ref", "_device", "out", "_keep")
 
     def __init__(self, entry, args, device, out, keep):
         self._entry, self._args, self._device, self.out, self._keep = entry, args, device, out, keep
+        self._fn = getattr(library(), entry)
         self._ref = ctypes.byref(args)
 
     def __call__(self, stream=None):
         """Launch on `stream` (a torch.cuda.Stream; default: the current stream)."""
-        lib = library()
         s = torch.cuda.current_stream(self._device) if stream is None else stream
-        rc = getattr(lib, self._entry)(self._ref, ctypes.c_void_p(s.cuda_stream))
+        rc = self._fn(self._ref, ctypes.c_void_p(s.cuda_stream))
         if rc != _abi.SSU_OK:
-            _raise(lib, rc, self._entry)
+            _raise(library(), rc, self._entry)
         return self.out
 
 

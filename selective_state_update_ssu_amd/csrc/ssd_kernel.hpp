@@ -170,22 +170,9 @@ __device__ __forceinline__ unsigned short bits_of(float v) {
     return __builtin_bit_cast(unsigned short, static_cast<T>(v));
 }
 
-// One state-type element <-> fp32.
-template <typename ST>
-__device__ __forceinline__ float load_state(const void* p, int64_t i) {
-    return static_cast<float>(static_cast<const ST*>(p)[i]);
-}
-template <typename ST>
-__device__ __forceinline__ void store_state(void* p, int64_t i, float v) {
-    static_cast<ST*>(p)[i] = static_cast<ST>(v);
-}
-
-// Streaming data (x, z, out, the chunk contributions) is read and written
-// non-temporally, so that it does not push the operands every head of a group
-// shares (B, C, C B^T of the chunk) out of L2.
-__device__ __forceinline__ u16x8 stream_load(const void* p) {
-    return __builtin_nontemporal_load(static_cast<const u16x8*>(p));
-}
+// Streaming data (x, z, out) is read and written non-temporally (bload_nt and
+// non-temporal stores), so that it does not push the operands every head of a
+// group shares (B, C, C B^T of the chunk) out of L2.
 
 // Raw buffer over `bytes` bytes from `base` (dword 3 of a gfx9 raw buffer:
 // 32-bit data format, no swizzle). A load at an offset at or past `bytes`
@@ -1104,20 +1091,19 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(N, Q)) void ss
     // times x. Tile k needs the s blocks kk <= its last row; its C B^T entries
     // are requested two blocks ahead of their products (clamped to the chunk's
     // tile, so a block the tile turns out not to need is a harmless read).
-    typedef float CBT;
-    const CBT* cbp = p.cb + (c * p.ngroups + g) * Q * Q;
+    const float* cbp = p.cb + (c * p.ngroups + g) * Q * Q;
     // Eight fp32 C B^T entries of one row: two 16-byte loads.
     constexpr int CW = 2;
     typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
     constexpr int DEPTH = scan_cb_depth(Q);  // s blocks of C B^T in flight per tile
     u32x4v cb[TT][DEPTH][CW];
-    const Rsrc cbr = make_rsrc(cbp, Q * Q * sizeof(CBT));
+    const Rsrc cbr = make_rsrc(cbp, Q * Q * sizeof(float));
     auto cb_load = [&](int k, int kk, int dd) {
         const int t0 = t0_of[k];
         // A block past the tile's last row is never used: its load stays in the
         // instruction stream (the waits count loads) but reads nothing.
         const uint32_t off = kk > t0 + 15 ? kOutOfRange
-                                           : ((t0 + lane % 16) * Q + min(kk, Q - 32) + kcol) * sizeof(CBT);
+                                           : ((t0 + lane % 16) * Q + min(kk, Q - 32) + kcol) * sizeof(float);
 #pragma unroll
         for (int w = 0; w < CW; ++w)
             cb[k][dd][w] = __builtin_amdgcn_raw_buffer_load_b128(cbr, off + 16 * w, 0, 0);

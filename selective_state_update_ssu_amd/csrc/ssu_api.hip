@@ -158,8 +158,9 @@ int check_operands(const ssu_operands& op, int64_t rows, bool work, bool packed)
 // Default launch shape. Measured on MI355X at the named decode shapes (dstate
 // 128, headdim 64): a read+write one-token call streams best in small tiles
 // (2 loads per lane, 2 heads per workgroup with an fp32 state, 1 with a 16-bit
-// one); a read-only call and the packed call, which writes several states per
-// state read, in larger ones (4 loads per lane, 2 heads per workgroup). Tile
+// one); a read-only call in larger ones (4 loads per lane, 1 head per
+// workgroup), and so the packed call, which writes several states per state
+// read (4 loads per lane, 2 heads per workgroup). Tile
 // order: varlen packed calls let each XCD take an equal contiguous share of
 // every sequence's tiles (a block of its heads), which balances sequences of
 // unequal token counts over the XCDs (3 % faster than contiguous ranges of
@@ -182,7 +183,7 @@ Shape default_shape(const ssu_operands& op, bool packed, bool equal_lengths) {
     if (packed)
         s = {2, 4, equal_lengths ? 1 : 2};
     else if (read_only)
-        s = {2, 4, one_token_order};
+        s = {1, 4, one_token_order};
     else if (sr)  // the Philox work of stochastic rounding wants bigger tiles
         s = {1, 4, one_token_order};
     else
