@@ -143,7 +143,9 @@ typedef struct ssu_operands {
                                  nheads / ngroups (at most 2 for dstate 256
                                  and for ssu_packed_varlen) */
     int32_t loads_per_lane;   /* launch shape: 16-byte state loads each lane keeps in
-                                 flight, 0 = library default, else 2 or 4 */
+                                 flight, 0 = library default, else 2 or 4 (a lane
+                                 keeps fewer where dstate rows are too short to
+                                 give it that many) */
     int32_t tile_order;       /* launch shape: 0 = library default, 1 = each XCD takes
                                  a contiguous range of tiles, 2 = hardware order, 3 = each
                                  XCD takes an equal contiguous share (a block of heads) of

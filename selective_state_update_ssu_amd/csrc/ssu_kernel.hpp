@@ -1,11 +1,12 @@
 // ssu_kernel.hpp -- the selective state update kernel for gfx950 (CDNA4, wave64).
 //
 // One workgroup owns a (sequence, block of heads of one group, block of rows)
-// tile. Each head of the block gets a 256-thread head group (four wave64s). The
-// head's rows are spread so that one vector-memory instruction of a wave covers
-// RPI whole consecutive dstate rows -- 64 lanes x (16 or 8) bytes, one contiguous
-// run of the slot -- and each lane owns the same VEC consecutive dstate elements
-// of RL different rows for the whole call. The state therefore crosses HBM
+// tile. Each head of the block gets a head group of HW wave64s (four, or one or
+// two for dstate rows of 64 bytes or less). The head's rows are spread so that
+// one vector-memory instruction of a wave covers RPI whole consecutive dstate
+// rows -- 64 lanes x 16 bytes, one contiguous run of the slot -- and each lane
+// owns the same VEC consecutive dstate elements of RL different rows for the
+// whole call. The state therefore crosses HBM
 // exactly once in each direction: read once per sequence, kept in fp32 registers
 // across all tokens of a packed sequence, written once per token.
 //
@@ -242,16 +243,28 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// Lane geometry of one (state dtype, dstate, load depth) instance.
+// Lane geometry of one (state dtype, dstate, load depth) instance. Every lane
+// load moves 16 bytes. A head group of HW waves covers RB consecutive rows of
+// one head. Rows of more than 64 bytes take four waves per head group, each lane
+// up to LOADS rows (at most a quarter of a row's lanes, so RB stays within 64
+// rows). Rows of 64 bytes or less (dstate 16, or 32 with a 16-bit state) give a
+// lane LOADS rows, or all a row's lanes' worth if fewer, and the head group only
+// as many waves as it takes to cover 64 rows: one or two, so that each lane keeps
+// 32-64 bytes in flight instead of one short load.
 template <typename ST, int N, int LOADS>
 struct Geometry {
     static constexpr int kMaxVec = 16 / static_cast<int>(sizeof(ST));
-    static constexpr int VEC = kMaxVec < N / 4 ? kMaxVec : N / 4;  // elements per lane-load
-    static constexpr int LPR = N / VEC;                            // lanes per dstate row
-    static constexpr int RPI = 64 / LPR;                           // rows per wave instruction
-    static constexpr int RL = LOADS < LPR / 4 ? LOADS : LPR / 4;  // loads per lane
-    static constexpr int RB = 4 * RPI * RL;                        // rows per head group
-    static_assert(RL >= 1 && RB <= kHeadThreads, "geometry");
+    static constexpr int VEC = kMaxVec;                // elements per lane-load
+    static constexpr int LPR = N / VEC;                // lanes per dstate row
+    static constexpr int RPI = 64 / LPR;               // rows per wave instruction
+    static constexpr bool kShortRows = N * static_cast<int>(sizeof(ST)) <= 64;
+    static constexpr int RL = kShortRows ? (LOADS < LPR ? LOADS : LPR)
+                                         : (LOADS < LPR / 4 ? LOADS : LPR / 4);  // loads per lane
+    static constexpr int HW = kShortRows ? 64 / (RPI * RL) : 4;  // waves per head group
+    static constexpr int HT = 64 * HW;                          // threads per head group
+    static constexpr int RB = HW * RPI * RL;                    // rows per head group
+    static_assert(N % VEC == 0 && LPR >= 2, "a row spans at least two lanes");
+    static_assert(RL >= 1 && HW >= 1 && HW <= 4 && RPI * RL <= 64 && RB <= 64, "geometry");
 };
 
 // Tile of workgroup `id` out of `n` when each XCD should walk a contiguous range
@@ -282,11 +295,12 @@ __device__ __forceinline__ int64_t xcd_split(int64_t id, int64_t n, int64_t per_
 // ------------------------------------------------------------------ kernel
 
 template <typename ST, typename IT, int N, int LOADS, bool PACKED, bool SR>
-__global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void ssu_update_kernel(
+__global__ __launch_bounds__((Geometry<ST, N, LOADS>::HT * max_heads_per_block(N, PACKED))) void ssu_update_kernel(
     const KernelParams p) {
     // Lane geometry.
     typedef Geometry<ST, N, LOADS> Geo;
     constexpr int VEC = Geo::VEC, LPR = Geo::LPR, RPI = Geo::RPI, RL = Geo::RL, RB = Geo::RB;
+    constexpr int HT = Geo::HT, HW = Geo::HW;
     constexpr int W = VEC / Pack<ST>::kPerWord;               // 32-bit words per lane-load
     constexpr int T = PACKED ? kStageTokens : 1;              // tokens staged at a time
     typedef typename Words<W>::type words_t;
@@ -294,8 +308,8 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
     const int tid = threadIdx.x;
     // Head within the workgroup and wave within the head group are wave-uniform;
     // saying so keeps the slot base addresses in scalar registers.
-    const int lh = __builtin_amdgcn_readfirstlane(tid / kHeadThreads);
-    const int ht = tid % kHeadThreads;       // thread within the head group
+    const int lh = __builtin_amdgcn_readfirstlane(tid / HT);
+    const int ht = tid % HT;                 // thread within the head group
     const int wave = __builtin_amdgcn_readfirstlane(ht / 64);
     const int lane = ht % 64;
     const int rg = lane / LPR;               // row within one wave instruction
@@ -323,7 +337,7 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
     int64_t* const sW = reinterpret_cast<int64_t*>(lds + T * tok);
     // This wave's row sums, indexed by row within the wave's RPI * RL rows.
     constexpr int WROWS = RPI * RL;
-    float* const sY = reinterpret_cast<float*>(sW + T) + (lh * 4 + wave) * WROWS;
+    float* const sY = reinterpret_cast<float*>(sW + T) + (lh * HW + wave) * WROWS;
     enum { kXV = 0, kDA = 1, kDX = 2, kGZ = 3 };  // v*x, exp(A*v), D*x, z*sigmoid(z)
     auto factor = [&](int tt, int which, int pl) -> float& {
         return lds[tt * tok + 2 * N + (which * hpb + lh) * RB + pl];
@@ -374,9 +388,9 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
     // over (token, row) pairs of each head group, B/C over (token, n) pairs of the
     // whole workgroup, destination ids over the first nt threads. Elements past
     // the chunk or past headdim load a valid dummy address instead of branching.
-    constexpr int ROW_PASSES = (T * RB + kHeadThreads - 1) / kHeadThreads;
-    constexpr int BC_PASSES = (T * N + kHeadThreads - 1) / kHeadThreads;
-    const int nthreads = kHeadThreads * hpb;
+    constexpr int ROW_PASSES = (T * RB + HT - 1) / HT;
+    constexpr int BC_PASSES = (T * N + HT - 1) / HT;
+    const int nthreads = HT * hpb;
     typedef typename Bits<IT>::type bits_t;
     const bits_t* const xp = static_cast<const bits_t*>(p.x);
     const bits_t* const zp = static_cast<const bits_t*>(gated ? p.z : p.x);  // ungated: unused
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
     auto load_chunk = [&](int64_t t0, int64_t nt) {
 #pragma unroll
         for (int q = 0; q < ROW_PASSES; ++q) {
-            const int idx = ht + q * kHeadThreads, k = idx / RB, pl = idx % RB;
+            const int idx = ht + q * HT, k = idx / RB, pl = idx % RB;
             const bool live = k < nt && rb * RB + pl < P;
             const int64_t row = begin + t0 + k;
             const int64_t xi = live ? (row * H + h) * P + rb * RB + pl : 0;
@@ -424,7 +438,7 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
     auto store_chunk = [&](int64_t nt) {
 #pragma unroll
         for (int q = 0; q < ROW_PASSES; ++q) {
-            const int idx = ht + q * kHeadThreads, k = idx / RB, pl = idx % RB;
+            const int idx = ht + q * HT, k = idx / RB, pl = idx % RB;
             if (k < nt) {
                 float xv = 0.f, dA = 0.f, dx = 0.f, gz = 1.f;
                 if (rb * RB + pl < P) {
@@ -558,21 +572,15 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
                         static_cast<uint32_t>((static_cast<int64_t>(h) * P + prow_of[i]) * N + n0);
                     unsigned half[VEC];
                     if constexpr (__is_same(ST, __bf16)) {
-                        constexpr int PER = VEC < 8 ? VEC : 8;  // elements per call here
+                        // A lane's eight elements start at a multiple of 8: one call.
+                        static_assert(VEC == 8, "eight bf16 elements per lane-load");
+                        uint32_t c[4] = {e0 / 8, rlo, rhi, 0u};
+                        philox4x32(c, key0, key1, p.philox_rounds);
 #pragma unroll
-                        for (int j = 0; j < VEC / PER; ++j) {
-                            uint32_t c[4] = {e0 / 8 + j, rlo, rhi, 0u};
-                            philox4x32(c, key0, key1, p.philox_rounds);
-                            // VEC = 4 (dstate 16): e0 % 8 is 0 or 4, i.e. words 0-1 or 2-3.
-                            const bool upper = PER < 8 && (e0 & 4u);
-                            const uint32_t wsel[4] = {upper ? c[2] : c[0], upper ? c[3] : c[1],
-                                                      c[2], c[3]};
-#pragma unroll
-                            for (int k = 0; k < PER; ++k) {
-                                const uint32_t word = wsel[k / 2];
-                                const uint32_t bits = (k & 1) ? (word >> 16) : (word & 0xFFFFu);
-                                half[PER * j + k] = sr_bits_bf16(s[i][PER * j + k], bits << 16);
-                            }
+                        for (int k = 0; k < 8; ++k) {
+                            const uint32_t word = c[k / 2];
+                            const uint32_t bits = (k & 1) ? (word >> 16) : (word & 0xFFFFu);
+                            half[k] = sr_bits_bf16(s[i][k], bits << 16);
                         }
                     } else {
 #pragma unroll
@@ -602,12 +610,13 @@ __global__ __launch_bounds__(kHeadThreads* max_heads_per_block(N, PACKED)) void 
 
 template <typename ST, typename IT, int N, int LOADS>
 hipError_t launch_instance(KernelParams p, int64_t nseq, hipStream_t stream, LaunchShape* shape) {
-    constexpr int RB = Geometry<ST, N, LOADS>::RB;
+    typedef Geometry<ST, N, LOADS> Geo;
+    constexpr int RB = Geo::RB;
     p.row_blocks = (p.headdim + RB - 1) / RB;
     const uint64_t blocks = static_cast<uint64_t>(nseq) * p.head_blocks * p.row_blocks;
     if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks));
-    const dim3 block(static_cast<unsigned>(kHeadThreads * p.heads_per_block));
+    const dim3 block(static_cast<unsigned>(Geo::HT * p.heads_per_block));
     const unsigned lds = lds_bytes(N, p.heads_per_block, RB, p.packed ? kStageTokens : 1);
     if (shape) *shape = LaunchShape{grid.x, block.x, lds, static_cast<unsigned>(RB)};
     if constexpr (sizeof(ST) == 2) {

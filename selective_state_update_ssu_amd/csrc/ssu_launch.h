@@ -7,8 +7,6 @@
 
 namespace ssu {
 
-// Threads per head group (four wave64s): one head of one row block.
-constexpr int kHeadThreads = 256;
 // Depths of 16-byte state loads a lane may keep in flight; each is compiled. A
 // lane gets fewer when a head's dstate rows are too short to give it that many.
 constexpr int kLoadDepths[] = {2, 4};
@@ -16,8 +14,9 @@ constexpr int kLoadDepths[] = {2, 4};
 constexpr int kMaxHeadsPerBlock = 4;
 
 // Heads per workgroup an instance allows. Large states per lane (dstate 256) and
-// the packed kernel (state plus a chunk of staged tokens) stop at 512 threads, to
-// leave the compiler 256 VGPRs instead of spilling.
+// the packed kernel (state plus a chunk of staged tokens) stop at two heads (512
+// threads with four-wave head groups), to leave the compiler 256 VGPRs instead of
+// spilling.
 __host__ __device__ constexpr int max_heads_per_block(int dstate, bool packed) {
     return (dstate >= 256 || packed) ? 2 : kMaxHeadsPerBlock;
 }

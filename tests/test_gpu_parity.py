@@ -89,6 +89,31 @@ def test_launch_shapes_bit_identical(name):
             del o2, s2
 
 
+
+@pytest.mark.parametrize("state_dtype,N", [("bf16", 16), ("f16", 16), ("f32", 16), ("bf16", 32)])
+@pytest.mark.parametrize("mode", ["one_token", "packed"])
+def test_short_row_launch_shapes(state_dtype, N, mode):
+    """dstate rows of 64 bytes or less take one- or two-wave head groups whose
+    lanes hold two to four rows: every (loads_per_lane, heads_per_block, tile
+    order) gives the same bits, and those bits match the oracle. headdim 72
+    leaves a ragged second row block."""
+    if mode == "one_token":
+        w = wl.one_token("short", 111, batch=9, H=8, P=72, N=N, G=2, nslots=24, device=DEV,
+                         state_dtype=state_dtype, io="bf16", pad_fraction=0.2,
+                         dst_mode="distinct")
+    else:
+        w = wl.packed("short", 112, nseq=7, max_len=12, H=8, P=72, N=N, G=2, nslots=90,
+                      device=DEV, state_dtype=state_dtype, lengths=[3, 1, 12, 0, 9, 4, 1],
+                      pad_fraction=0.15)
+    o1, s1, before = hz.gpu_run(w, heads_per_block=1, loads_per_lane=2, tile_order=2)
+    compare_full(f"short-{mode}-{state_dtype}-{N}", w, o1, s1, before, hz.oracle_full(w))
+    hpbs = (1, 2) if mode == "packed" else (1, 2, 4)
+    for lpl, hpb, order in itertools.product((2, 4), hpbs, (1, 2, 3)):
+        o2, s2, _ = hz.gpu_run(w, heads_per_block=hpb, loads_per_lane=lpl, tile_order=order)
+        assert torch.equal(hz.bits(o1), hz.bits(o2)), (lpl, hpb, order)
+        assert torch.equal(hz.bits(s1), hz.bits(s2)), (lpl, hpb, order)
+
+
 # ---------------------------------------------------------------- small grid
 
 def _small_cases():
@@ -394,17 +419,24 @@ def test_tied_parameter_views_bit_identical(form):
                                                       ("f16", "one_token", 10),
                                                       ("bf16", "packed", 7),
                                                       ("f16", "packed", 10),
-                                                      ("bf16", "packed_long", 10)])
+                                                      ("bf16", "packed_long", 10),
+                                                      ("bf16", "one_token_d16", 10),
+                                                      ("f16", "one_token_d16", 10),
+                                                      ("bf16", "packed_d32", 10),
+                                                      ("f16", "packed_d32", 10)])
 def test_stochastic_rounding(state_dtype, mode, rounds):
     """Stored 16-bit states equal the oracle's stochastic rounding with the same
     Philox words (up to rare threshold flips between the fp32 and fp64 states);
-    out and placement are those of the round-to-nearest call."""
-    if mode == "one_token":
-        w = wl.one_token("sr", 1001, batch=9, H=8, P=64, N=128, G=2, nslots=24, device=DEV,
+    out and placement are those of the round-to-nearest call. dstate 16 and 32
+    run the short-row geometry (two or four rows per lane)."""
+    if mode in ("one_token", "one_token_d16"):
+        N = 16 if mode == "one_token_d16" else 128
+        w = wl.one_token("sr", 1001, batch=9, H=8, P=64, N=N, G=2, nslots=24, device=DEV,
                          state_dtype=state_dtype, io="bf16", pad_fraction=0.2,
                          dst_mode="distinct")
-    elif mode == "packed":
-        w = wl.packed("sr", 1002, nseq=7, max_len=4, H=4, P=64, N=64, G=1, nslots=40,
+    elif mode in ("packed", "packed_d32"):
+        N = 32 if mode == "packed_d32" else 64
+        w = wl.packed("sr", 1002, nseq=7, max_len=4, H=4, P=64, N=N, G=1, nslots=40,
                       device=DEV, state_dtype=state_dtype, lengths=[3, 1, 4, 0, 2, 4, 1],
                       pad_fraction=0.15)
     else:  # sequences past the eight-token operand stage; rows number the draws
