@@ -95,7 +95,8 @@ typedef struct ssu_ssd_args {
 } ssu_ssd_args;
 
 /* Bytes of workspace ssu_ssd_prefill needs for these sizes: each chunk's
- * entering state as high and low io-type parts, the per-chunk C B^T products
+ * entering state as io-type high parts and 8-bit low parts (three bytes per
+ * element), the per-chunk C B^T products
  * (fp32), each chunk's
  * steps, running sums, weights and decay per head, the chunk descriptors, the
  * per-request list of last chunks and the runs of chunks that continue one
@@ -144,8 +145,8 @@ int ssu_ssd_prefill(const ssu_ssd_args *args, void *stream);
  *
  * Returns what ssu_ssd_prefill returns, and SSU_ERR_UNSUPPORTED when the call's
  * workspace (ssu_ssd_workspace_bytes) exceeds SSU_SSD_STATIC_SCRATCH_BYTES
- * (it holds up to 27 chunks of 128 tokens at 128 heads x 64 x 128 with 8 groups,
- * 42 chunks of 256 at 80 heads x 64 x 128 with 1 group), SSU_ERR_LAUNCH when
+ * (it holds up to 34 chunks of 128 tokens at 128 heads x 64 x 128 with 8 groups,
+ * 54 chunks of 256 at 80 heads x 64 x 128 with 1 group), SSU_ERR_LAUNCH when
  * no device is current or the scratch cannot be found on it. Results are those
  * of ssu_ssd_prefill, bit for bit (the same kernels).
  */

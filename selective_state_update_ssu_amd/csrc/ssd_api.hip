@@ -26,8 +26,8 @@ Layout layout(int64_t nchunks, int64_t batch, int64_t nheads, int64_t headdim, i
               int64_t ngroups, int64_t chunk_size) {
     Layout l;
     l.s16 = 0;
-    l.cb = l.s16 + round_up(static_cast<size_t>(nchunks * nheads * headdim * dstate) * 2 *
-                            ssd::kEnterPlanes);
+    l.cb = l.s16 + round_up(static_cast<size_t>(nchunks * nheads * headdim * dstate) *
+                            ssd::kEnterBytes);
     l.cumlast = l.cb + round_up(static_cast<size_t>(nchunks * ngroups * chunk_size * chunk_size) * 4);
     l.head = l.cumlast + round_up(static_cast<size_t>(nchunks * nheads) * 4);
     l.next = l.head + round_up(static_cast<size_t>(nchunks) * 4);

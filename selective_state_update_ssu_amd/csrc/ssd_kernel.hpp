@@ -89,8 +89,9 @@ struct SsdParams {
     const void* init;     // [batch, H, P, N] state type, may be null
     void* out;            // [tokens, H, P] io
     void* states;         // [nchunks or batch, H, P, N] state type
-    void* s16;            // workspace [nchunks, H, 2, P, N] io: each chunk's entering state
-                          // as high and low parts
+    void* s16;            // workspace [nchunks, H] tiles of kEnterBytes * P * N bytes: each
+                          // chunk's entering state as [P, N] io-type high parts, then
+                          // [P, N] low bytes
     float* cb;            // workspace [nchunks, G, Q, Q]
     float* cumlast;       // workspace [nchunks, H]: each chunk's decay exponent
     ChunkDesc* desc;      // workspace [nchunks]
@@ -151,9 +152,35 @@ __device__ __forceinline__ void split16(float v, IT& hi, IT& lo) {
     hi = static_cast<IT>(v);
     lo = static_cast<IT>(v - static_cast<float>(hi));
 }
-// Each chunk's entering state reaches the scan as these two planes, [2][P][N]
-// per (chunk, head).
-constexpr int kEnterPlanes = 2;
+
+// Each chunk's entering state crosses memory from the walk to the scan as, per
+// (chunk, head), the high parts hi = io(v) of its P x N elements, then their
+// low parts as signed bytes q = round((v - hi) / u), u = ulp(hi) / 256, clamped
+// to +-127: three bytes per element instead of the four of two io-type planes.
+// q u is exact in the io type (at most 7 significant bits), so the scan feeds
+// hi and q u to the matrix cores as the pair above; |v - hi - q u| <= u / 2
+// (u with the clamp, when |v - hi| is exactly ulp(hi) / 2), i.e. 2^-16 (bf16)
+// or 2^-19 (fp16) of |hi|. u is taken from hi's fp32 exponent field, the same
+// on both sides.
+constexpr int kEnterBytes = 3;
+template <typename T> struct IoMantissa;
+template <> struct IoMantissa<__bf16> { static constexpr int bits = 7; };
+template <> struct IoMantissa<_Float16> { static constexpr int bits = 10; };
+template <typename IT>
+__device__ __forceinline__ int low_unit_exp(float hi) {
+    return static_cast<int>((__float_as_uint(hi) >> 23) & 0xFFu) - 127 - IoMantissa<IT>::bits - 8;
+}
+// The low byte of v given its high part (as an fp32 value).
+template <typename IT>
+__device__ __forceinline__ unsigned low_byte(float v, float hi) {
+    const float q = __builtin_rintf(__builtin_amdgcn_ldexpf(v - hi, -low_unit_exp<IT>(hi)));
+    return static_cast<unsigned>(static_cast<int>(fminf(fmaxf(q, -127.f), 127.f))) & 0xFFu;
+}
+// The low part q u back from the byte q (sign-extended) and the high part.
+template <typename IT>
+__device__ __forceinline__ float low_value(float hi, int q) {
+    return __builtin_amdgcn_ldexpf(static_cast<float>(q), low_unit_exp<IT>(hi));
+}
 // Headdim columns one walk item or one scan workgroup covers; headdim is a
 // multiple of it.
 constexpr int kHeadBlock = 64;
@@ -566,9 +593,9 @@ __device__ __forceinline__ int swz(int r, int col) {
 // blocks of KB: B^T [N][KB] and the weighted x^T [P][KB] as high and low 16-bit
 // parts; the next block's operands are requested before the current block's
 // products. After each chunk the state leaves as the next chunk's entering
-// state (high and low io-type planes, for the scan) and in the state type where
+// state (high parts and low bytes, for the scan) and in the state type where
 // it is returned. The run's entering state is the request's initial state (also
-// handed to the scan as the two planes) or zeros. Workgroup i takes items i, i + grid, ...; the items come
+// handed to the scan that way) or zeros. Workgroup i takes items i, i + grid, ...; the items come
 // longest run first, so the long walks start at once.
 constexpr int kWalkKB = 128;
 constexpr int kWalkPitch = kWalkKB + 8;
@@ -611,8 +638,8 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
     const uint32_t xrow = static_cast<uint32_t>(H * PF * 2), brow = static_cast<uint32_t>(p.ngroups * NF * 2);
     const int64_t tile = static_cast<int64_t>(H) * PF * NF;
     const bool lists = !p.return_all && p.batch > 0;
-    // First element of chunk c's entering state for head h (both planes).
-    auto enter_tile = [&](int64_t c, int h) { return (c * H + h) * (kEnterPlanes * static_cast<int64_t>(PF) * NF); };
+    // First byte of chunk c's entering state for head h (high parts, then low bytes).
+    auto enter_tile = [&](int64_t c, int h) { return (c * H + h) * (kEnterBytes * static_cast<int64_t>(PF) * NF); };
 
     // Workgroups are dealt to the XCDs round robin, so with a grid of a multiple
     // of the XCD count each XCD always sees the same residue of item % XCDs.
@@ -693,57 +720,68 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
                 for (int qt = 0; qt < 2; ++qt) acc[nt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        // The state as the next chunk's entering state: the high and the low
-        // planes of this item's block (io type; dst = the block's first element of
-        // the high plane, rows NF apart, the low plane PF * NF further), through
-        // the B^T area of LDS so that
-        // every store writes whole 16-byte pieces of whole rows: each wave drops
-        // its part of S^T into LDS (16-byte chunks of row p permuted by p, which
-        // spreads the writes of sixteen rows over the banks), then the workgroup
-        // copies the rows out. The caller makes sure every wave is done with the
-        // B^T area; the next use of LDS is behind a barrier.
-        auto store_enter = [&](IT* dst) {
-            // Both planes' rows of the block, from dst on (the low plane PF * NF further).
-            const Rsrc er = make_rsrc(dst, static_cast<uint32_t>((PF * NF + (P - 1) * NF + N) * 2));
+        // The state as chunk c's entering state: the high parts and the low bytes
+        // of this item's block (rows NF apart in the head's [PF][NF] tile of
+        // each), through the B^T area of LDS so that every store writes whole
+        // 16-byte pieces of whole rows: each wave drops its part of S^T into LDS
+        // (16-byte chunks of row p permuted by p, which spreads the writes of
+        // sixteen rows over the banks), then the workgroup copies the rows out.
+        // The caller makes sure every wave is done with the B^T area; the next
+        // use of LDS is behind a barrier.
+        auto store_enter = [&](int64_t c) {
+            const Rsrc er = make_rsrc(static_cast<unsigned char*>(p.s16) + enter_tile(c, h),
+                                      static_cast<uint32_t>(kEnterBytes * PF * NF));
+            const uint32_t blk = static_cast<uint32_t>(pb * P * NF + nb * N);  // block's first element
             typedef unsigned short t4 __attribute__((ext_vector_type(4)));
-            constexpr int CPR = N * 2 / 16;  // 16-byte chunks per row
-            constexpr unsigned PLANE = P * N * 2;
-            static_assert(kEnterPlanes * PLANE <= 2u * N * XP, "both planes fit the B^T area");
+            constexpr int CPR = N * 2 / 16;  // 16-byte chunks per row: high parts
+            constexpr int CPL = N / 16;      // low bytes
+            constexpr unsigned HI = P * N * 2;  // LDS bytes of the high parts
+            static_assert(HI + P * N <= 2u * N * XP, "both parts fit the B^T area");
             unsigned char* lt = reinterpret_cast<unsigned char*>(bt);
+            // High parts first, then the low bytes (the high part recomputed), which
+            // keeps few values live beside the next block's operands.
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
                     const int pr = q0 + 16 * qt + lane % 16, n = n0 + 16 * nt + 4 * (lane / 16);
                     const int byte = n * 2;
-                    const unsigned o = pr * N * 2 + (((byte / 16) ^ (pr % CPR)) * 16) + byte % 16;
                     t4 v;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = bits_of<IT>(acc[nt][qt][i]);
-                    *reinterpret_cast<t4*>(lt + o) = v;
+                    *reinterpret_cast<t4*>(lt + pr * N * 2 + (((byte / 16) ^ (pr % CPR)) * 16) + byte % 16) = v;
+                }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = bits_of<IT>(acc[nt][qt][i] - f32_of<IT>(v[i]));
-                    *reinterpret_cast<t4*>(lt + PLANE + o) = v;
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    const int pr = q0 + 16 * qt + lane % 16, n = n0 + 16 * nt + 4 * (lane / 16);
+                    unsigned lo = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        lo |= low_byte<IT>(acc[nt][qt][i], f32_of<IT>(bits_of<IT>(acc[nt][qt][i]))) << (8 * i);
+                    *reinterpret_cast<unsigned*>(lt + HI + pr * N + (((n / 16) ^ (pr % CPL)) * 16) + n % 16) = lo;
                 }
             lds_barrier();
-            constexpr int PIECES = P * CPR / NT;  // per plane
-            static_assert(PIECES * NT == P * CPR, "whole pieces");
-            // One plane at a time, which bounds the registers the copy holds.
+            constexpr int HP = P * CPR / NT, LP = P * CPL / NT;  // pieces per thread
+            static_assert(HP * NT == P * CPR && LP * NT == P * CPL, "whole pieces");
+            // One piece at a time, which bounds the registers the copy holds: the
+            // high parts' pieces, then the low bytes'.
 #pragma unroll 1
-            for (int pl = 0; pl < kEnterPlanes; ++pl)
-#pragma unroll
-                for (int i = 0; i < PIECES; ++i) {
-                    const int idx = tid + NT * i, pr = idx / CPR, ch = idx % CPR;
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(lt + pl * PLANE + pr * N * 2 +
-                                                                    ((ch ^ (pr % CPR)) * 16));
-                    __builtin_amdgcn_raw_buffer_store_b128(v, er, static_cast<uint32_t>(pr * NF * 2 + ch * 16),
-                                                           static_cast<uint32_t>(pl * PF * NF * 2), 0);
-                }
+            for (int i = 0; i < HP + LP; ++i) {
+                const bool high = i < HP;
+                const int idx = tid + NT * (high ? i : i - HP);
+                const int cpr = high ? CPR : CPL, pr = idx / cpr, ch = idx % cpr;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(
+                    lt + (high ? pr * N * 2 : HI + pr * N) + ((ch ^ (pr % cpr)) * 16));
+                __builtin_amdgcn_raw_buffer_store_b128(v, er, (blk + pr * NF) * (high ? 2 : 1) + ch * 16,
+                                                       high ? 0u : static_cast<uint32_t>(2 * PF * NF), 0);
+            }
         };
         // The run's initial state is the first chunk's entering state too (LDS
         // is free: the previous item ended with a barrier, and the first block
         // stages behind one).
-        if (init) store_enter(static_cast<IT*>(p.s16) + enter_tile(c0, h) + (hs - static_cast<int64_t>(h) * PF * NF));
+        if (init) store_enter(c0);
 
         // The returned states, written from the accumulators directly (each
         // chunk's with return_intermediate_states, else only the requests'
@@ -843,7 +881,7 @@ __global__ __launch_bounds__(walk_threads(N), N == 128 ? 4 : 2) void ssd_state_w
             // goes on, and the returned states (state type).
             if (more) {
                 lds_barrier();  // every wave is done with this block's operands
-                store_enter(static_cast<IT*>(p.s16) + enter_tile(c + 1, h) + (hs - static_cast<int64_t>(h) * PF * NF));
+                store_enter(c + 1);
             }
             if (p.return_all) {
                 put(c);
@@ -888,8 +926,11 @@ __host__ __device__ constexpr int scan_waves_per_simd(int N, int Q) {
 // Blocks of 32 C B^T columns each tile has in flight: one for chunks of 256
 // (within 128 registers), two for chunks of 128.
 __host__ __device__ constexpr int scan_cb_depth(int Q) { return Q >= 256 ? 1 : 2; }
+// The scan holds the entering state in LDS as two io-type planes: the high
+// parts and the low parts decoded from their bytes.
+constexpr int kScanStatePlanes = 2;
 __host__ __device__ constexpr unsigned scan_lds_bytes(int P, int N, int Q) {
-    return 4u * Q + 4u * Q + 4u * P + 2u * kEnterPlanes * P * state_pitch(N) +
+    return 4u * Q + 4u * Q + 4u * P + 2u * kScanStatePlanes * P * state_pitch(N) +
            (2u * P * scan_pitch(Q) > 4u * 16 * scan_epilogue_pitch(P) * (scan_threads(Q) / 64)
                 ? 2u * P * scan_pitch(Q)
                 : 4u * 16 * scan_epilogue_pitch(P) * (scan_threads(Q) / 64));
@@ -935,7 +976,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(N, Q)) void ss
     static_assert(NT == 2 * Q, "one value per thread");
     float* sd = cum2 + Q;  // [P] skip coefficients
     unsigned short* sS = reinterpret_cast<unsigned short*>(sd + P);  // [2][P][SP]
-    unsigned short* xv = sS + kEnterPlanes * P * SP;
+    unsigned short* xv = sS + kScanStatePlanes * P * SP;
 
     const IT* Cp = static_cast<const IT*>(p.C);
     const uint32_t xrow = static_cast<uint32_t>(H * PF * 2);
@@ -955,17 +996,22 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(N, Q)) void ss
         rx[r][0] = bload_nt(xr, off);
         rx[r][1] = bload_nt(xr, off + xrow);
     }
-    // The entering state's two planes (zeros for a chunk that opens a request
-    // without one).
+    // The entering state (zeros for a chunk that opens a request without one):
+    // this block's rows (contiguous) of the high parts and of the low bytes, the
+    // same eight elements of each per load.
     const bool has_state = d.enter != kEnterZero;
-    // This block's rows of each plane (planes PF * N apart, rows contiguous).
-    const Rsrc sr = make_rsrc(static_cast<const IT*>(p.s16) + (c * H + h) * kEnterPlanes * PF * N + pb * P * N,
-                              has_state ? (PF + P) * N * 2 : 0);
-    u16x8 rs[kEnterPlanes][SPASS];
+    const Rsrc sr = make_rsrc(static_cast<const unsigned char*>(p.s16) + (c * H + h) * kEnterBytes * PF * N,
+                              has_state ? kEnterBytes * PF * N : 0);
+    const uint32_t sblk = pb * P * N;
+    u16x8 rs[SPASS];
+    typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+    u32x2v rq[SPASS];
 #pragma unroll
-    for (int pl = 0; pl < kEnterPlanes; ++pl)
-#pragma unroll
-        for (int r = 0; r < SPASS; ++r) rs[pl][r] = bload(sr, pl * PF * N * 2 + 16 * (tid + NT * r));
+    for (int r = 0; r < SPASS; ++r) {
+        const uint32_t e = sblk + 8 * (tid + NT * r);
+        rs[r] = bload(sr, 2 * e);
+        rq[r] = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(sr, e, 2 * PF * N, 0));
+    }
     // C operands of the entering-state product, first k step.
     // Token tiles of this wave: w and 2 NW - 1 - w, so that every wave's pair
     // covers about the same share of the causal triangle (tile i needs i / 2 + 1
@@ -996,7 +1042,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(N, Q)) void ss
     // after the products inside the chunk.
     const int er = lane / 8, ec = (lane % 8) * (P / 8);
     static_assert(P / 8 == 8, "eight lanes per row, 16 bytes each");
-    constexpr int ZL = NW * TT * 2048 <= 2 * kEnterPlanes * P * SP ? TT : 0;
+    constexpr int ZL = NW * TT * 2048 <= 2 * kScanStatePlanes * P * SP ? TT : 0;
     const Rsrc zr = make_rsrc(p.z ? static_cast<const IT*>(p.z) + xoff : nullptr, p.z ? len * xrow : 0u);
     u16x8 ez[TT][2];
     auto z_load = [&](int k) {
@@ -1022,12 +1068,17 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(N, Q)) void ss
         }
     }
 #pragma unroll
-    for (int pl = 0; pl < kEnterPlanes; ++pl)
+    for (int r = 0; r < SPASS; ++r) {
+        const int ci = tid + NT * r, pr = ci / (N / 8), n8 = 8 * (ci % (N / 8));
+        u16x8 lo;
 #pragma unroll
-        for (int r = 0; r < SPASS; ++r) {
-            const int ci = tid + NT * r, pr = ci / (N / 8), n8 = 8 * (ci % (N / 8));
-            *reinterpret_cast<u16x8*>(sS + pl * P * SP + pr * SP + swz(pr, n8)) = rs[pl][r];
+        for (int e = 0; e < 8; ++e) {
+            const int q = static_cast<int>(rq[r][e / 4] << (24 - 8 * (e % 4))) >> 24;  // sign-extended byte
+            lo[e] = bits_of<IT>(low_value<IT>(f32_of<IT>(rs[r][e]), q));
         }
+        *reinterpret_cast<u16x8*>(sS + pr * SP + swz(pr, n8)) = rs[r];
+        *reinterpret_cast<u16x8*>(sS + P * SP + pr * SP + swz(pr, n8)) = lo;
+    }
     lds_barrier();
 
     f32x4 acc[TT][PT];
@@ -1049,7 +1100,7 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(N, Q)) void ss
                 for (int k = 0; k < TT; ++k) cn[k] = c_frag(k, 32 * (ks + 1));
             }
 #pragma unroll
-            for (int pl = 0; pl < kEnterPlanes; ++pl) {
+            for (int pl = 0; pl < kScanStatePlanes; ++pl) {
                 v8 sf[PT];
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {

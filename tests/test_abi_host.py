@@ -304,11 +304,11 @@ def test_ssd_rejects(lib, kw, code, needle):
 
 def test_ssd_workspace_bytes(lib):
     n = lib.ssu_ssd_workspace_bytes(6, 3, 8, 64, 128, 2, 256)
-    # entering states (high and low io-type parts), C B^T per chunk and group
-    # (fp32), decay exponents, the request list, chunk descriptors (16 bytes),
-    # chunk-state weights (fp32), the scan's steps and running sums (two fp32 per
-    # token and head), the runs.
-    need = (6 * 8 * 64 * 128 * 2 * 2 + 6 * 2 * 256 * 256 * 4 + 6 * 8 * 4 + 6 * 4 + 3 * 4 + 6 * 16
+    # entering states (io-type high parts and low bytes: three bytes per
+    # element), C B^T per chunk and group (fp32), decay exponents, the request
+    # list, chunk descriptors (16 bytes), chunk-state weights (fp32), the scan's
+    # steps and running sums (two fp32 per token and head), the runs.
+    need = (6 * 8 * 64 * 128 * 3 + 6 * 2 * 256 * 256 * 4 + 6 * 8 * 4 + 6 * 4 + 3 * 4 + 6 * 16
             + 6 * 8 * 256 * 4 + 6 * 8 * 256 * 8 + 3 * 6 * 4 + 4)
     assert need <= n <= need + 12 * 256 and n % 256 == 0
     assert lib.ssu_ssd_workspace_bytes(-1, 3, 8, 64, 128, 2, 256) == 0
@@ -413,4 +413,4 @@ def test_ssd_noalloc_host_checks(lib):
     assert lib.ssu_ssd_prefill_noalloc(ctypes.byref(a), None) == UNS
     msg = lib.ssu_last_error().decode()
     assert "static scratch holds" in msg and str(cap) in msg, msg
-    assert n == 27, n
+    assert n == 34, n

@@ -71,7 +71,7 @@ def test_static_scratch_allocates_only_the_states():
 def test_static_scratch_too_small_raises():
     """A call whose workspace exceeds the static scratch is refused on the host."""
     import selective_state_update_ssu_amd as ssu
-    w = wl.ssd("noalloc_big", 74, lengths=[28 * 128], H=128, P=64, N=128, G=8, chunk=128,
+    w = wl.ssd("noalloc_big", 74, lengths=[35 * 128], H=128, P=64, N=128, G=8, chunk=128,
                device=DEV, with_z=False)
     with pytest.raises(NotImplementedError, match="static scratch holds"):
         ssu.ssd_combined_fwd_varlen(*w.args(), static_scratch=True, **w.kwargs())
