@@ -936,14 +936,22 @@ __host__ __device__ constexpr unsigned scan_lds_bytes(int P, int N, int Q) {
                 : 4u * 16 * scan_epilogue_pitch(P) * (scan_threads(Q) / 64));
 }
 
+// Heads one scan workgroup takes in turn, the next head's operands loading
+// while the current head finishes its epilogue: two for chunks of 128 at dstate
+// up to 128 (LDS allows three workgroups per CU there, which leaves registers
+// for the loads in flight), else one.
+__host__ __device__ constexpr int scan_heads(int N, int Q) { return Q < 256 && N <= 128 ? 2 : 1; }
+
 // x^T and the entering state are stored permuted by swz().
 
-// One workgroup per (chunk, head, block of kHeadBlock headdim columns); wave w
-// owns token tiles w and 2 NW - 1 - w. The outputs of different headdim columns
-// share nothing but the decayed C B^T entries, which each block recomputes.
-// Every load the workgroup needs before its first product -- steps, the x
-// tile, the entering state, the first C operands, D -- is issued at the start,
-// each product's next operands before its current matrix-core work.
+// One workgroup per (chunk, scan_heads consecutive heads, block of kHeadBlock
+// headdim columns), the heads one after the other; wave w owns token tiles w
+// and 2 NW - 1 - w. The outputs of different headdim columns share nothing but
+// the decayed C B^T entries, which each block recomputes. Every load a head
+// needs before its first product -- steps, the x tile, the entering state, the
+// first C operands, D -- is issued before anything waits (the next head's
+// during this head's epilogue), each product's next operands before its
+// current matrix-core work.
 template <typename IT, typename ST, int N, int Q>
 __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(N, Q)) void ssd_scan_kernel(const SsdParams p) {
     constexpr int P = kHeadBlock;
@@ -956,19 +964,19 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(N, Q)) void ss
     static_assert(XPASS * NT == (Q / 2) * (P / 8) && SPASS * NT == P * (N / 8), "passes");
     static_assert((SP * 2) % 16 == 0 && (XP * 2) % 16 == 0, "16-byte rows");
 
+    constexpr int HL = scan_heads(N, Q);
     const int PF = p.headdim, PBK = PF / P;
+    const int H = p.nheads, HQ = (H + HL - 1) / HL;
     const int64_t wg = xcd_order(blockIdx.x, gridDim.x);
-    const int64_t c = wg / (static_cast<int64_t>(p.nheads) * PBK);
-    const int h = static_cast<int>((wg / PBK) % p.nheads);
+    const int64_t c = wg / (static_cast<int64_t>(HQ) * PBK);
+    const int h0 = static_cast<int>((wg / PBK) % HQ) * HL;
     const int pb = static_cast<int>(wg % PBK);
     const ChunkDesc d = load_desc(p, c);
     if (d.len == 0) return;
     const int len = d.len;
-    const int g = h / p.heads_per_group;
-    const int H = p.nheads;
-    const int tid = threadIdx.x;
+    int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int lane = tid % 64;
+    int lane = tid % 64;
 
     extern __shared__ __align__(16) unsigned char smem[];
     float* sl = reinterpret_cast<float*>(smem);  // [Q] cum_s log2(e) - log2(v_s)
@@ -981,302 +989,321 @@ __global__ __launch_bounds__(scan_threads(Q), scan_waves_per_simd(N, Q)) void ss
     const IT* Cp = static_cast<const IT*>(p.C);
     const uint32_t xrow = static_cast<uint32_t>(H * PF * 2);
     // The chunk's first x / z / out row of head h, at this block's columns.
-    const int64_t xoff = (d.lo * H + h) * PF + pb * P;
+    auto xoff_of = [&](int h) { return (d.lo * H + h) * PF + pb * P; };
 
-    // ---- loads issued up front.
-    // cum_s log2(e) - log2(v_s) (tid < Q), then cum_s log2(e).
-    const float step = p.cv[(c * H + h) * 2 * Q + tid];
-    // x: thread handles row octet q of token pair s (eight threads per token row).
-    const Rsrc xr = make_rsrc(static_cast<const IT*>(p.x) + xoff, len * xrow);
-    u16x8 rx[XPASS][2];
-#pragma unroll
-    for (int r = 0; r < XPASS; ++r) {
-        const int idx = tid + NT * r, q = idx % (P / 8), s = 2 * (idx / (P / 8));
-        const uint32_t off = s * xrow + 16 * q;
-        rx[r][0] = bload_nt(xr, off);
-        rx[r][1] = bload_nt(xr, off + xrow);
-    }
-    // The entering state (zeros for a chunk that opens a request without one):
-    // this block's rows (contiguous) of the high parts and of the low bytes, the
-    // same eight elements of each per load.
+    // ---- a head's loads, issued before anything waits: for the first head at
+    // the start, for the next one while this one finishes its epilogue.
     const bool has_state = d.enter != kEnterZero;
-    const Rsrc sr = make_rsrc(static_cast<const unsigned char*>(p.s16) + (c * H + h) * kEnterBytes * PF * N,
-                              has_state ? kEnterBytes * PF * N : 0);
     const uint32_t sblk = pb * P * N;
-    u16x8 rs[SPASS];
     typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
-    u32x2v rq[SPASS];
+    float step;             // cum_s log2(e) - log2(v_s) (tid < Q), then cum_s log2(e)
+    u16x8 rx[XPASS][2];     // x: thread handles row octet q of token pair s
+    u16x8 rs[SPASS];        // entering state: high parts of eight elements
+    u32x2v rq[SPASS];       // ... and their low bytes
+    float dcoef;            // the skip coefficient of headdim row tid (zero without D)
+    auto issue = [&](int h) {
+        step = p.cv[(c * H + h) * 2 * Q + tid];
+        const Rsrc xr = make_rsrc(static_cast<const IT*>(p.x) + xoff_of(h), len * xrow);
 #pragma unroll
-    for (int r = 0; r < SPASS; ++r) {
-        const uint32_t e = sblk + 8 * (tid + NT * r);
-        rs[r] = bload(sr, 2 * e);
-        rq[r] = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(sr, e, 2 * PF * N, 0));
-    }
-    // C operands of the entering-state product, first k step.
-    // Token tiles of this wave: w and 2 NW - 1 - w, so that every wave's pair
-    // covers about the same share of the causal triangle (tile i needs i / 2 + 1
-    // blocks of C B^T).
-    static_assert(TT == 2, "tile pairs");
-    int t0_of[TT];
-    t0_of[0] = 16 * wave;
-    t0_of[1] = 16 * (2 * NW - 1 - wave);
-    int trow[TT];
+        for (int r = 0; r < XPASS; ++r) {
+            const int idx = tid + NT * r, q = idx % (P / 8), s = 2 * (idx / (P / 8));
+            const uint32_t off = s * xrow + 16 * q;
+            rx[r][0] = bload_nt(xr, off);
+            rx[r][1] = bload_nt(xr, off + xrow);
+        }
+        // The entering state (zeros for a chunk that opens a request without
+        // one): this block's rows (contiguous) of the high parts and of the low
+        // bytes, the same eight elements of each per load.
+        const Rsrc sr = make_rsrc(static_cast<const unsigned char*>(p.s16) + (c * H + h) * kEnterBytes * PF * N,
+                                  has_state ? kEnterBytes * PF * N : 0);
 #pragma unroll
-    for (int k = 0; k < TT; ++k) trow[k] = min(t0_of[k] + lane % 16, len - 1);
-    const int kcol = 8 * (lane / 16);
-    auto c_frag = [&](int k, int kk) {
-        return *reinterpret_cast<const v8*>(Cp + ((d.lo + trow[k]) * p.ngroups + g) * N + kk + kcol);
+        for (int r = 0; r < SPASS; ++r) {
+            const uint32_t e = sblk + 8 * (tid + NT * r);
+            rs[r] = bload(sr, 2 * e);
+            rq[r] = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(sr, e, 2 * PF * N, 0));
+        }
+        const Rsrc dr = make_rsrc(p.D, p.D ? static_cast<uint32_t>((p.D_per_dim ? H * PF : H) * 4) : 0u);
+        dcoef = bload_f32(dr, 4u * (p.D_per_dim ? h * PF + pb * P + min(tid, P - 1) : h));
     };
-    v8 cf[TT];
+    issue(h0);
+    // Unrolled, so that which copy prefetches is known when compiling: each
+    // copy's operand registers are then the only live ones.
 #pragma unroll
-    for (int k = 0; k < TT; ++k) cf[k] = c_frag(k, 0);
-    // The skip coefficient of headdim row tid (zero without D).
-    const Rsrc dr = make_rsrc(p.D, p.D ? static_cast<uint32_t>((p.D_per_dim ? H * PF : H) * 4) : 0u);
-    const float dcoef = bload_f32(dr, 4u * (p.D_per_dim ? h * PF + pb * P + min(tid, P - 1) : h));
+    for (int j = 0; j < HL; ++j) {
+        const int h = h0 + j;
+        if (h >= H) break;
+        // Each head recomputes its per-lane offsets rather than holding them
+        // across the loop (an empty asm makes the lane numbers opaque here).
+        asm volatile("" : "+v"(tid), "+v"(lane));
+        // C operands of the entering-state product, first k step.
+        // Token tiles of this wave: w and 2 NW - 1 - w, so that every wave's pair
+        // covers about the same share of the causal triangle (tile i needs i / 2 + 1
+        // blocks of C B^T).
+        static_assert(TT == 2, "tile pairs");
+        int t0_of[TT];
+        t0_of[0] = 16 * wave;
+        t0_of[1] = 16 * (2 * NW - 1 - wave);
+        int trow[TT];
+#pragma unroll
+        for (int k = 0; k < TT; ++k) trow[k] = min(t0_of[k] + lane % 16, len - 1);
+        const int kcol = 8 * (lane / 16);
+        bool live[TT];
+#pragma unroll
+        for (int k = 0; k < TT; ++k) live[k] = t0_of[k] < len;
+        const int er = lane / 8, ec = (lane % 8) * (P / 8);
+        static_assert(P / 8 == 8, "eight lanes per row, 16 bytes each");
+        constexpr int ZL = NW * TT * 2048 <= 2 * kScanStatePlanes * P * SP ? TT : 0;
+        u16x8* const zslot = reinterpret_cast<u16x8*>(sS) + 2 * (wave * 64 + lane);  // + 2 * 64 * NW * k
 
-    // z rows of the epilogue (zeros without z): lane l finishes 8 consecutive
-    // columns of rows l / 8 and l / 8 + 8 of each of its tiles, so every store
-    // instruction writes eight whole rows. Where every wave's tiles fit the
-    // entering-state area they are requested now and parked there once the
-    // entering-state product is done with it; otherwise they are requested
-    // after the products inside the chunk.
-    const int er = lane / 8, ec = (lane % 8) * (P / 8);
-    static_assert(P / 8 == 8, "eight lanes per row, 16 bytes each");
-    constexpr int ZL = NW * TT * 2048 <= 2 * kScanStatePlanes * P * SP ? TT : 0;
-    const Rsrc zr = make_rsrc(p.z ? static_cast<const IT*>(p.z) + xoff : nullptr, p.z ? len * xrow : 0u);
-    u16x8 ez[TT][2];
-    auto z_load = [&](int k) {
-        const uint32_t off = (t0_of[k] + er) * xrow + 2 * ec;
-        ez[k][0] = bload_nt(zr, off);
-        ez[k][1] = bload_nt(zr, off + 8 * xrow);
-    };
+        const int g = h / p.heads_per_group;
+        const int64_t xoff = xoff_of(h);
+        auto c_frag = [&](int k, int kk) {
+            return *reinterpret_cast<const v8*>(Cp + ((d.lo + trow[k]) * p.ngroups + g) * N + kk + kcol);
+        };
+        v8 cf[TT];
 #pragma unroll
-    for (int k = 0; k < ZL; ++k) z_load(k);
-    u16x8* const zslot = reinterpret_cast<u16x8*>(sS) + 2 * (wave * 64 + lane);  // + 2 * 64 * NW * k
+        for (int k = 0; k < TT; ++k) cf[k] = c_frag(k, 0);
 
-    // Steps, x^T (exact) and the entering state into LDS.
-    sl[tid] = step;  // cum2 follows sl
-    if (tid < P) sd[tid] = dcoef;
+        // z rows of the epilogue (zeros without z): lane l finishes 8 consecutive
+        // columns of rows l / 8 and l / 8 + 8 of each of its tiles, so every store
+        // instruction writes eight whole rows. Where every wave's tiles fit the
+        // entering-state area they are requested now and parked there once the
+        // entering-state product is done with it; otherwise they are requested
+        // after the products inside the chunk.
+        const Rsrc zr = make_rsrc(p.z ? static_cast<const IT*>(p.z) + xoff : nullptr, p.z ? len * xrow : 0u);
+        u16x8 ez[TT][2];
+        auto z_load = [&](int k) {
+            const uint32_t off = (t0_of[k] + er) * xrow + 2 * ec;
+            ez[k][0] = bload_nt(zr, off);
+            ez[k][1] = bload_nt(zr, off + 8 * xrow);
+        };
 #pragma unroll
-    for (int r = 0; r < XPASS; ++r) {
-        const int idx = tid + NT * r, q = idx % (P / 8), s = 2 * (idx / (P / 8));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int pr = 8 * q + e;
-            *reinterpret_cast<unsigned*>(xv + pr * XP + swz(pr, s)) =
-                rx[r][0][e] | (static_cast<unsigned>(rx[r][1][e]) << 16);
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < SPASS; ++r) {
-        const int ci = tid + NT * r, pr = ci / (N / 8), n8 = 8 * (ci % (N / 8));
-        u16x8 lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int q = static_cast<int>(rq[r][e / 4] << (24 - 8 * (e % 4))) >> 24;  // sign-extended byte
-            lo[e] = bits_of<IT>(low_value<IT>(f32_of<IT>(rs[r][e]), q));
-        }
-        *reinterpret_cast<u16x8*>(sS + pr * SP + swz(pr, n8)) = rs[r];
-        *reinterpret_cast<u16x8*>(sS + P * SP + pr * SP + swz(pr, n8)) = lo;
-    }
-    lds_barrier();
+        for (int k = 0; k < ZL; ++k) z_load(k);
 
-    f32x4 acc[TT][PT];
+        // Steps, x^T (exact) and the entering state into LDS (after the previous
+        // head's epilogue is done with it).
+        if (j > 0) lds_barrier();
+        sl[tid] = step;  // cum2 follows sl
+        if (tid < P) sd[tid] = dcoef;
 #pragma unroll
-    for (int k = 0; k < TT; ++k)
+        for (int r = 0; r < XPASS; ++r) {
+            const int idx = tid + NT * r, q = idx % (P / 8), s = 2 * (idx / (P / 8));
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool live[TT];
-#pragma unroll
-    for (int k = 0; k < TT; ++k) live[k] = t0_of[k] < len;
-
-    // ---- the entering state: C_t . (S_hi + S_lo), then scaled by exp(cum_t)
-    if (has_state) {
-#pragma unroll
-        for (int ks = 0; ks < KN; ++ks) {
-            v8 cn[TT];
-            if (ks + 1 < KN) {
-#pragma unroll
-                for (int k = 0; k < TT; ++k) cn[k] = c_frag(k, 32 * (ks + 1));
-            }
-#pragma unroll
-            for (int pl = 0; pl < kScanStatePlanes; ++pl) {
-                v8 sf[PT];
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const int pr = 16 * pt + lane % 16;
-                    sf[pt] = *reinterpret_cast<const v8*>(sS + pl * P * SP + pr * SP + swz(pr, 32 * ks + kcol));
-                }
-#pragma unroll
-                for (int k = 0; k < TT; ++k)
-                    if (live[k])
-#pragma unroll
-                        for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(cf[k], sf[pt], acc[k][pt]);
-            }
-            if (ks + 1 < KN) {
-#pragma unroll
-                for (int k = 0; k < TT; ++k) cf[k] = cn[k];
+            for (int e = 0; e < 8; ++e) {
+                const int pr = 8 * q + e;
+                *reinterpret_cast<unsigned*>(xv + pr * XP + swz(pr, s)) =
+                    rx[r][0][e] | (static_cast<unsigned>(rx[r][1][e]) << 16);
             }
         }
+#pragma unroll
+        for (int r = 0; r < SPASS; ++r) {
+            const int ci = tid + NT * r, pr = ci / (N / 8), n8 = 8 * (ci % (N / 8));
+            u16x8 lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int q = static_cast<int>(rq[r][e / 4] << (24 - 8 * (e % 4))) >> 24;  // sign-extended byte
+                lo[e] = bits_of<IT>(low_value<IT>(f32_of<IT>(rs[r][e]), q));
+            }
+            *reinterpret_cast<u16x8*>(sS + pr * SP + swz(pr, n8)) = rs[r];
+            *reinterpret_cast<u16x8*>(sS + P * SP + pr * SP + swz(pr, n8)) = lo;
+        }
+        lds_barrier();
+
+        f32x4 acc[TT][PT];
 #pragma unroll
         for (int k = 0; k < TT; ++k)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = min(t0_of[k] + 4 * (lane / 16) + i, Q - 1);
-                const float f = __builtin_amdgcn_exp2f(cum2[t]);
+            for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // ---- the entering state: C_t . (S_hi + S_lo), then scaled by exp(cum_t)
+        if (has_state) {
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) acc[k][pt][i] *= f;
+            for (int ks = 0; ks < KN; ++ks) {
+                v8 cn[TT];
+                if (ks + 1 < KN) {
+#pragma unroll
+                    for (int k = 0; k < TT; ++k) cn[k] = c_frag(k, 32 * (ks + 1));
+                }
+#pragma unroll
+                for (int pl = 0; pl < kScanStatePlanes; ++pl) {
+                    v8 sf[PT];
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const int pr = 16 * pt + lane % 16;
+                        sf[pt] = *reinterpret_cast<const v8*>(sS + pl * P * SP + pr * SP + swz(pr, 32 * ks + kcol));
+                    }
+#pragma unroll
+                    for (int k = 0; k < TT; ++k)
+                        if (live[k])
+#pragma unroll
+                            for (int pt = 0; pt < PT; ++pt) acc[k][pt] = Mfma<IT>::mma16(cf[k], sf[pt], acc[k][pt]);
+                }
+                if (ks + 1 < KN) {
+#pragma unroll
+                    for (int k = 0; k < TT; ++k) cf[k] = cn[k];
+                }
             }
-    }
-
-    if constexpr (ZL > 0) {
-        lds_barrier();  // every wave is done with the entering state
 #pragma unroll
-        for (int k = 0; k < ZL; ++k) {
-            zslot[2 * 64 * NW * k] = ez[k][0];
-            zslot[2 * 64 * NW * k + 1] = ez[k][1];
+            for (int k = 0; k < TT; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = min(t0_of[k] + 4 * (lane / 16) + i, Q - 1);
+                    const float f = __builtin_amdgcn_exp2f(cum2[t]);
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) acc[k][pt][i] *= f;
+                }
         }
-    }
 
-    // ---- inside the chunk: (C B^T masked, times the decays and the steps v_s)
-    // times x. Tile k needs the s blocks kk <= its last row; its C B^T entries
-    // are requested two blocks ahead of their products (clamped to the chunk's
-    // tile, so a block the tile turns out not to need is a harmless read).
-    const float* cbp = p.cb + (c * p.ngroups + g) * Q * Q;
-    // Eight fp32 C B^T entries of one row: two 16-byte loads.
-    constexpr int CW = 2;
-    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-    constexpr int DEPTH = scan_cb_depth(Q);  // s blocks of C B^T in flight per tile
-    u32x4v cb[TT][DEPTH][CW];
-    const Rsrc cbr = make_rsrc(cbp, Q * Q * sizeof(float));
-    auto cb_load = [&](int k, int kk, int dd) {
-        const int t0 = t0_of[k];
-        // A block past the tile's last row is never used: its load stays in the
-        // instruction stream (the waits count loads) but reads nothing.
-        const uint32_t off = kk > t0 + 15 ? kOutOfRange
-                                           : ((t0 + lane % 16) * Q + min(kk, Q - 32) + kcol) * sizeof(float);
+        if constexpr (ZL > 0) {
+            lds_barrier();  // every wave is done with the entering state
 #pragma unroll
-        for (int w = 0; w < CW; ++w)
-            cb[k][dd][w] = __builtin_amdgcn_raw_buffer_load_b128(cbr, off + 16 * w, 0, 0);
-    };
-    auto cb_value = [&](int k, int dd, int j) -> float { return __uint_as_float(cb[k][dd][j / 4][j % 4]); };
-    // Every step issues one load per (tile, slot) in the same order, whether or
-    // not the tile needs the block (an unneeded block's load reads nothing), so
-    // the wait before each use stays a count of the loads issued after it.
+            for (int k = 0; k < ZL; ++k) {
+                zslot[2 * 64 * NW * k] = ez[k][0];
+                zslot[2 * 64 * NW * k + 1] = ez[k][1];
+            }
+        }
+
+        // ---- inside the chunk: (C B^T masked, times the decays and the steps v_s)
+        // times x. Tile k needs the s blocks kk <= its last row; its C B^T entries
+        // are requested two blocks ahead of their products (clamped to the chunk's
+        // tile, so a block the tile turns out not to need is a harmless read).
+        const float* cbp = p.cb + (c * p.ngroups + g) * Q * Q;
+        // Eight fp32 C B^T entries of one row: two 16-byte loads.
+        constexpr int CW = 2;
+        typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+        constexpr int DEPTH = scan_cb_depth(Q);  // s blocks of C B^T in flight per tile
+        u32x4v cb[TT][DEPTH][CW];
+        const Rsrc cbr = make_rsrc(cbp, Q * Q * sizeof(float));
+        auto cb_load = [&](int k, int kk, int dd) {
+            const int t0 = t0_of[k];
+            // A block past the tile's last row is never used: its load stays in the
+            // instruction stream (the waits count loads) but reads nothing.
+            const uint32_t off = kk > t0 + 15 ? kOutOfRange
+                                               : ((t0 + lane % 16) * Q + min(kk, Q - 32) + kcol) * sizeof(float);
 #pragma unroll
-    for (int dd = 0; dd < DEPTH; ++dd)
+            for (int w = 0; w < CW; ++w)
+                cb[k][dd][w] = __builtin_amdgcn_raw_buffer_load_b128(cbr, off + 16 * w, 0, 0);
+        };
+        auto cb_value = [&](int k, int dd, int j) -> float { return __uint_as_float(cb[k][dd][j / 4][j % 4]); };
+        // Every step issues one load per (tile, slot) in the same order, whether or
+        // not the tile needs the block (an unneeded block's load reads nothing), so
+        // the wait before each use stays a count of the loads issued after it.
 #pragma unroll
-        for (int k = 0; k < TT; ++k) cb_load(k, 32 * dd, dd);
-    // The loop runs DEPTH s blocks per iteration so that slot indices stay static,
-    // up to the last block this wave's later live tile needs.
-    const int kend = min(len, (live[1] ? t0_of[1] : t0_of[0]) + 16);
-    for (int kb = 0; kb < kend; kb += 32 * DEPTH) {
+        for (int dd = 0; dd < DEPTH; ++dd)
 #pragma unroll
-        for (int dd = 0; dd < DEPTH; ++dd) {
-            const int kk = kb + 32 * dd;
-            if (kk >= kend) break;
-            const int col = kk + kcol;
-            v8 xf[PT];
+            for (int k = 0; k < TT; ++k) cb_load(k, 32 * dd, dd);
+        // The loop runs DEPTH s blocks per iteration so that slot indices stay static,
+        // up to the last block this wave's later live tile needs.
+        const int kend = min(len, (live[1] ? t0_of[1] : t0_of[0]) + 16);
+        for (int kb = 0; kb < kend; kb += 32 * DEPTH) {
+#pragma unroll
+            for (int dd = 0; dd < DEPTH; ++dd) {
+                const int kk = kb + 32 * dd;
+                if (kk >= kend) break;
+                const int col = kk + kcol;
+                v8 xf[PT];
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const int pr = 16 * pt + lane % 16;
+                    xf[pt] = *reinterpret_cast<const v8*>(xv + pr * XP + swz(pr, col));
+                }
+                // v_s exp2(ct - cs) = exp2(ct - (cs - log2 v_s)).
+                float ls[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) ls[j] = sl[col + j];
+#pragma unroll
+                for (int k = 0; k < TT; ++k) {
+                    const int t0 = t0_of[k];
+                    if (live[k] && t0 + 15 >= kk) {
+                        const int t = t0 + lane % 16;
+                        const float ct = cum2[t];
+                        v8 ah, al;  // the decayed entries' high and low parts
+                        // Only the block that reaches the tile's rows needs the causal
+                        // mask (s <= t); masked entries take exp2(-inf) = 0, a select.
+                        // Rows past the chunk are computed from finite values and
+                        // never stored.
+                        if (kk + 31 > t0) {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) {
+                                const float ex = col + j <= t ? ct - ls[j] : -__builtin_huge_valf();
+                                IT hi, lo;
+                                split16(cb_value(k, dd, j) * __builtin_amdgcn_exp2f(ex), hi, lo);
+                                ah[j] = hi;
+                                al[j] = lo;
+                            }
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) {
+                                IT hi, lo;
+                                split16(cb_value(k, dd, j) * __builtin_amdgcn_exp2f(ct - ls[j]), hi, lo);
+                                ah[j] = hi;
+                                al[j] = lo;
+                            }
+                        }
+#pragma unroll
+                        for (int pt = 0; pt < PT; ++pt) {
+                            acc[k][pt] = Mfma<IT>::mma16(ah, xf[pt], acc[k][pt]);
+                            acc[k][pt] = Mfma<IT>::mma16(al, xf[pt], acc[k][pt]);
+                        }
+                    }
+                    cb_load(k, kk + 32 * DEPTH, dd);  // in flight during the next blocks
+                }
+            }
+        }
+
+        if (j + 1 < HL) issue(min(h + 1, H - 1));  // (a repeat of h past the last head is unused)
+#pragma unroll
+        for (int k = ZL; k < TT; ++k) z_load(k);
+
+        // ---- skip term from the exact x^T in LDS (row t's four consecutive tokens
+        // are one 8-byte read), then gate and store: each tile goes through a
+        // wave-private LDS scratch spanning the entering-state and x^T areas (free
+        // once every wave is past this point) so that z and out move as whole rows.
+#pragma unroll
+        for (int k = 0; k < TT; ++k)
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const int pr = 16 * pt + lane % 16;
-                xf[pt] = *reinterpret_cast<const v8*>(xv + pr * XP + swz(pr, col));
+                const int t = t0_of[k] + 4 * (lane / 16);
+                typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+                const u16x4 xr4 = *reinterpret_cast<const u16x4*>(xv + pr * XP + swz(pr, t));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[k][pt][i] += sd[pr] * f32_of<IT>(xr4[i]);
             }
-            // v_s exp2(ct - cs) = exp2(ct - (cs - log2 v_s)).
-            float ls[8];
+        constexpr int EP = scan_epilogue_pitch(P);
+        IT* op = static_cast<IT*>(p.out);
+        const bool gate = p.z != nullptr;
+        lds_barrier();  // every wave is done with x^T
+        float* scratch = reinterpret_cast<float*>(xv) + wave * 16 * EP;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ls[j] = sl[col + j];
+        for (int k = 0; k < TT; ++k) {
+            if (!live[k]) break;
 #pragma unroll
-            for (int k = 0; k < TT; ++k) {
-                const int t0 = t0_of[k];
-                if (live[k] && t0 + 15 >= kk) {
-                    const int t = t0 + lane % 16;
-                    const float ct = cum2[t];
-                    v8 ah, al;  // the decayed entries' high and low parts
-                    // Only the block that reaches the tile's rows needs the causal
-                    // mask (s <= t); masked entries take exp2(-inf) = 0, a select.
-                    // Rows past the chunk are computed from finite values and
-                    // never stored.
-                    if (kk + 31 > t0) {
+            for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float ex = col + j <= t ? ct - ls[j] : -__builtin_huge_valf();
-                            IT hi, lo;
-                            split16(cb_value(k, dd, j) * __builtin_amdgcn_exp2f(ex), hi, lo);
-                            ah[j] = hi;
-                            al[j] = lo;
-                        }
-                    } else {
+                for (int i = 0; i < 4; ++i) scratch[(4 * (lane / 16) + i) * EP + 16 * pt + lane % 16] = acc[k][pt][i];
+            ssu::wave_lds_sync();
+            const u16x8 zz[2] = {k < ZL ? zslot[2 * 64 * NW * k] : ez[k][0],
+                                 k < ZL ? zslot[2 * 64 * NW * k + 1] : ez[k][1]};
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            IT hi, lo;
-                            split16(cb_value(k, dd, j) * __builtin_amdgcn_exp2f(ct - ls[j]), hi, lo);
-                            ah[j] = hi;
-                            al[j] = lo;
-                        }
+            for (int half = 0; half < 2; ++half) {
+                const int row = er + 8 * half, t = t0_of[k] + row;
+                if (t < len) {
+                    const f32x4* srow = reinterpret_cast<const f32x4*>(scratch + row * EP + ec);
+                    u16x8 o;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float y = srow[e / 4][e % 4];
+                        if (gate) y *= gate_f32(f32_of<IT>(zz[half][e]));
+                        o[e] = bits_of<IT>(y);
                     }
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) {
-                        acc[k][pt] = Mfma<IT>::mma16(ah, xf[pt], acc[k][pt]);
-                        acc[k][pt] = Mfma<IT>::mma16(al, xf[pt], acc[k][pt]);
-                    }
+                    __builtin_nontemporal_store(
+                        o, reinterpret_cast<u16x8*>(op + xoff + static_cast<int64_t>(t) * H * PF + ec));
                 }
-                cb_load(k, kk + 32 * DEPTH, dd);  // in flight during the next blocks
             }
+            ssu::wave_lds_sync();  // the next tile reuses the scratch
         }
-    }
-
-#pragma unroll
-    for (int k = ZL; k < TT; ++k) z_load(k);
-
-    // ---- skip term from the exact x^T in LDS (row t's four consecutive tokens
-    // are one 8-byte read), then gate and store: each tile goes through a
-    // wave-private LDS scratch spanning the entering-state and x^T areas (free
-    // once every wave is past this point) so that z and out move as whole rows.
-#pragma unroll
-    for (int k = 0; k < TT; ++k)
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const int pr = 16 * pt + lane % 16;
-            const int t = t0_of[k] + 4 * (lane / 16);
-            typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
-            const u16x4 xr4 = *reinterpret_cast<const u16x4*>(xv + pr * XP + swz(pr, t));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[k][pt][i] += sd[pr] * f32_of<IT>(xr4[i]);
-        }
-    constexpr int EP = scan_epilogue_pitch(P);
-    IT* op = static_cast<IT*>(p.out);
-    const bool gate = p.z != nullptr;
-    lds_barrier();  // every wave is done with x^T
-    float* scratch = reinterpret_cast<float*>(xv) + wave * 16 * EP;
-#pragma unroll
-    for (int k = 0; k < TT; ++k) {
-        if (!live[k]) break;
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) scratch[(4 * (lane / 16) + i) * EP + 16 * pt + lane % 16] = acc[k][pt][i];
-        ssu::wave_lds_sync();
-        const u16x8 zz[2] = {k < ZL ? zslot[2 * 64 * NW * k] : ez[k][0],
-                             k < ZL ? zslot[2 * 64 * NW * k + 1] : ez[k][1]};
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int row = er + 8 * half, t = t0_of[k] + row;
-            if (t < len) {
-                const f32x4* srow = reinterpret_cast<const f32x4*>(scratch + row * EP + ec);
-                u16x8 o;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float y = srow[e / 4][e % 4];
-                    if (gate) y *= gate_f32(f32_of<IT>(zz[half][e]));
-                    o[e] = bits_of<IT>(y);
-                }
-                __builtin_nontemporal_store(
-                    o, reinterpret_cast<u16x8*>(op + xoff + static_cast<int64_t>(t) * H * PF + ec));
-            }
-        }
-        ssu::wave_lds_sync();  // the next tile reuses the scratch
-    }
+    }  // heads
 }
 
 }  // namespace ssd
@@ -1314,8 +1341,10 @@ hipError_t launch_instance(const SsdParams& p, hipStream_t stream) {
     const int64_t walkers = std::min<int64_t>(fit, p.nchunks * p.nheads * blocks);
     hipLaunchKernelGGL((ssd_state_walk_kernel<IT, ST, NB, Q>), dim3(static_cast<unsigned>(walkers)),
                        dim3(walk_threads(NB)), walk_lds_bytes(kHeadBlock, NB), stream, p);
+    constexpr int HL = scan_heads(N, Q);
     hipLaunchKernelGGL((ssd_scan_kernel<IT, ST, N, Q>),
-                       dim3(static_cast<unsigned>(p.nchunks * p.nheads * (p.headdim / kHeadBlock))),
+                       dim3(static_cast<unsigned>(p.nchunks * ((p.nheads + HL - 1) / HL) *
+                                                  (p.headdim / kHeadBlock))),
                        dim3(scan_threads(Q)), scan_lds_bytes(kHeadBlock, N, Q), stream, p);
     return hipGetLastError();
 }

@@ -66,6 +66,11 @@ CASES = {
     "headdim192": dict(lengths=[200, 333], H=2, P=192, N=128, G=1, chunk=256, with_init=True),
     "headdim256_f16": dict(lengths=[150, 260], H=2, P=256, N=64, G=2, chunk=128, io="f16",
                            with_init=True, D_per_dim=True),
+    # chunks of 128 take two heads per scan workgroup: an odd head count leaves
+    # the last workgroup of each chunk one head, and one group per head puts
+    # the two heads of a workgroup in different groups; two column blocks.
+    "odd_heads_q128": dict(lengths=[200, 129, 7], H=5, P=128, N=128, G=5, chunk=128,
+                           with_init=True, D_per_dim=True),
 }
 
 
