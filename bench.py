@@ -638,35 +638,58 @@ def run_ssd_workload(name, steps, warmup):
 
 
 def ssd_cpu_baseline(seconds):
-    """The fp64 oracle, single-threaded, on the first request of the
-    Mamba2-2.7B-shaped prefill (all heads), repeated for about `seconds`."""
+    """The fp64 oracle on the first request of the Mamba2-2.7B-shaped prefill,
+    repeated for about `seconds`: half of the time one thread on all heads
+    (`single_thread_value`), half one thread per available core, each task an
+    oracle call on a block of heads (the shape has one group, so every block
+    reads the same B and C; a head's recurrence needs nothing from another)."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     from selective_state_update_ssu_amd import workloads as wl
 
     w = wl.ssd_mamba2_2p7b("cpu")
+    H = w.x.shape[1]
+    assert w.B.shape[1] == 1, "head blocks share the single group"
     cc = w.cu_chunk_seqlens.numpy().astype(np.int64)
     si = w.seq_idx.numpy().astype(np.int64)
     chunks = np.nonzero(si == 0)[0]
     hi = int(cc[chunks[-1] + 1])
-    f = lambda t: t[:hi].double().numpy()
-    args = (f(w.x), f(w.dt), w.A.double().numpy(), f(w.B), f(w.C), w.chunk_size,
-            cc[:chunks[-1] + 2], np.zeros(len(chunks), dtype=np.int64),
+    meta = (w.chunk_size, cc[:chunks[-1] + 2], np.zeros(len(chunks), dtype=np.int64),
             np.array([len(chunks) - 1]))
-    kw = dict(D=w.D.double().numpy(), z=f(w.z), dt_bias=w.dt_bias.double().numpy(),
-              dt_softplus=True)
+
+    def task(h0, h1):
+        f = lambda t: np.ascontiguousarray(t[:hi, h0:h1].double().numpy())
+        g = lambda t: np.ascontiguousarray(t[h0:h1].double().numpy())
+        args = (f(w.x), f(w.dt), g(w.A), w.B[:hi].double().numpy(), w.C[:hi].double().numpy(),
+                *meta)
+        kw = dict(D=g(w.D), z=f(w.z), dt_bias=g(w.dt_bias), dt_softplus=True)
+        return args, kw
+
     orc = oracle.default()
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        orc.ssd_prefill(*args, **kw)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": hi * calls / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"request 0 of ssd_mamba2_2p7b ({hi} tokens, all 80 heads), fp64, "
-                      f"{calls} calls in {el:.1f} s, one thread"}
+
+    def run(tasks, threads, budget):
+        """(sequence, head) units per second: every task repeatedly, `threads` at a time."""
+        done = 0
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            while time.perf_counter() - t0 < budget:
+                heads = list(ex.map(lambda t: (orc.ssd_prefill(*t[1][0], **t[1][1]), t[0])[1],
+                                    tasks))
+                done += sum(heads)
+        return done / (time.perf_counter() - t0)
+
+    whole = [(H, task(0, H))]
+    one = run(whole, 1, seconds / 2) * hi / H
+    threads = cpu_threads()
+    per = -(-H // threads)
+    blocks = [(min(h0 + per, H) - h0, task(h0, min(h0 + per, H))) for h0 in range(0, H, per)]
+    many = run(blocks, threads, seconds / 2) * hi / H
+    return {"value": many, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": one, "cpu_model": cpu_model(),
+            "sample": f"request 0 of ssd_mamba2_2p7b ({hi} tokens, {H} heads), fp64: one "
+                      f"thread on all heads for {seconds / 2:.1f} s, then {threads} threads "
+                      f"on {len(blocks)} blocks of up to {per} heads for {seconds / 2:.1f} s"}
 
 
 def summarize_ssd(prof_dir, workload, cmd):
