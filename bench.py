@@ -962,7 +962,10 @@ def main():
                   f"{rec['tokens_per_s'] / 1e6:.2f} M tokens/s, {rec['hbm_gbps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
         if not args.no_cpu_baseline:
-            extra["ssd_cpu_baseline"] = ssd_cpu_baseline(min(5.0, args.cpu_seconds))
+            try:  # an extra figure: its failure is reported, not fatal to the line
+                extra["ssd_cpu_baseline"] = ssd_cpu_baseline(min(5.0, args.cpu_seconds))
+            except Exception as e:  # noqa: BLE001
+                extra["ssd_cpu_baseline"] = {"error": f"{type(e).__name__}: {e}"}
     ceil = ceilings()
     copy_gbps = ceil["copy"]
     rings = ring_tracker_times()
