@@ -595,3 +595,38 @@ def test_prepared_calls_match_the_regular_calls():
         assert o_prep.shape == o_reg.shape
         assert torch.equal(hz.bits(o_reg), hz.bits(o_prep)), dense
         assert torch.equal(hz.bits(s_reg), hz.bits(s_prep)), dense
+
+
+# ------------------------------------------------------- every compiled instance
+
+@pytest.mark.parametrize("mode", ["one_token", "packed"])
+@pytest.mark.parametrize("state_dtype", ["f32", "f16", "bf16"])
+def test_every_compiled_instance(state_dtype, mode):
+    """Every (io dtype, dstate, loads per lane) instance of this state dtype and
+    entry point -- 30 kernels -- against the oracle on a small ragged shape
+    (headdim 72: a partial second row block at every geometry), with pads and
+    distinct destinations; and, for a 16-bit state, the stochastically rounding
+    instances (bf16 io, every dstate and load depth) against the oracle's
+    rounding."""
+    n = 0
+    for io, N, lpl in itertools.product(["f32", "f16", "bf16"], [16, 32, 64, 128, 256], [2, 4]):
+        if mode == "one_token":
+            w = wl.one_token("inst", 31, batch=5, H=4, P=72, N=N, G=2, nslots=12, device=DEV,
+                             state_dtype=state_dtype, io=io, pad_fraction=0.2,
+                             dst_mode="distinct")
+        else:
+            w = wl.packed("inst", 32, nseq=4, max_len=10, H=4, P=72, N=N, G=2, nslots=48,
+                          device=DEV, state_dtype=state_dtype, io=io,
+                          lengths=[3, 0, 10, 1], pad_fraction=0.25)
+        name = f"{mode}-{state_dtype}-{io}-N{N}-l{lpl}"
+        out, after, before = hz.gpu_run(w, loads_per_lane=lpl)
+        compare_full(name, w, out, after, before, hz.oracle_full(w))
+        n += 1
+        if state_dtype != "f32" and io == "bf16":
+            w.rand_seed = torch.tensor([0x5EED + N], dtype=torch.int64, device=DEV)
+            out, after, before = hz.gpu_run(w, loads_per_lane=lpl)
+            hz.check_placement(name + "-sr", w, out, after, before)
+            hz.check_slots_sr(name + "-sr state", after, before, list(range(w.state.shape[0])),
+                              hz.oracle_full(w).state, hz.oracle_full(w, rounding=False).state)
+            n += 1
+    _say(f"[parity] every instance, {mode} {state_dtype}: {n} kernels checked")
