@@ -1,6 +1,7 @@
 """SSD chunked prefill on the GPU against the fp64 oracle, element by element:
 16-bit results within 1e-2 + 2e-2 |ref|, fp32 states within 1e-5 of their scale
 (ssd_harness.py)."""
+import itertools
 import os
 
 import numpy as np
@@ -238,3 +239,25 @@ def test_explicit_stream():
     assert torch.equal(states, ref_states) and torch.equal(out2, out)
     keys = {k[1] for k in ssu._ssd_workspaces}
     assert side.cuda_stream in keys
+
+
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_every_compiled_instance(io):
+    """Every compiled prefill instance of this io type -- state dtype x dstate
+    64/128/256 x chunk 128/256, 18 kernel sets -- against the oracle at the
+    bars on a small case: two requests (one of a single chunk, one of three with
+    a ragged tail), headdim 128, two groups, initial states, gate."""
+    worst = [0.0, 0.0]
+    n = 0
+    for st, N, Q in itertools.product(["f32", "f16", "bf16"], [64, 128, 256], [128, 256]):
+        w = wl.ssd(f"inst_{io}_{st}_{N}_{Q}", 41, device=DEV, lengths=[Q - 3, 2 * Q + 37], H=4,
+                   P=128, N=N, G=2, chunk=Q, io=io, state_dtype=st, with_init=True)
+        out = torch.full_like(w.x, float("nan"))
+        _, states = sh.run_gpu(w, out)
+        torch.cuda.synchronize()
+        ref, mag = sh.oracle_ref(w)
+        (r_out, _), (r_st, _) = sh.check_all(w, out, states, ref, mag)
+        worst = [max(worst[0], r_out), max(worst[1], r_st)]
+        n += 1
+    print(f"[ssd] every instance, {io} io: {n} kernel sets, worst err/bar out {worst[0]:.3f}, "
+          f"states {worst[1]:.3f}", flush=True)
