@@ -14,6 +14,10 @@
  * state; every stored value must equal that result except where the GPU's fp32
  * state sits next to a rounding threshold (at most 0.5 % of the elements, each
  * one bf16 step away).
+ * A fourth call runs the SSD prefill (include/ssd.h) with a workspace of its
+ * own, checked against the oracle's prefill at the same bars as the Python
+ * tests (bf16 out within 1e-2 + 2e-2 |ref|, fp32 states within 1e-5 of their
+ * scale).
  * Prints "c client ok" and exits 0 on success, 1 on a mismatch, 2 on a HIP or
  * library error.
  */
@@ -24,6 +28,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include "ssd.h"
 #include "ssu.h"
 #include "ssu_oracle.h"
 
@@ -405,6 +410,139 @@ int main(void) {
                "%ld threshold flips, %ld mismatches: %s\n", written - flips - bad, written,
                flips, bad, ok ? "matches" : "MISMATCH");
         failures += !ok;
+    }
+
+    /* ---- the SSD prefill (include/ssd.h): two requests of 150 and 40 tokens in
+       chunks of 128 (three chunks), bf16 io, fp32 states, initial states, gate,
+       D and dt_bias, and a workspace from hipMalloc of ssu_ssd_workspace_bytes.
+       out and the per-request final states against the oracle at the bars:
+       |err| <= 1e-2 + 2e-2 |ref| for bf16 out, max |err| <= 1e-5 max(1, max |ref|)
+       for the fp32 states. */
+    {
+        enum { SH = 2, SP = 64, SN = 64, SG = 1, Q = 128, TOK = 190, NCH = 3, NB = 2 };
+        const int32_t cu[NCH + 1] = {0, 128, 150, 190};
+        const int32_t sidx[NCH] = {0, 0, 1};
+        const int32_t last[NB] = {1, 2};
+        const size_t nx = (size_t)TOK * SH * SP, nb = (size_t)TOK * SG * SN,
+                     ns = (size_t)NB * SH * SP * SN;
+        uint16_t *x16 = malloc(nx * 2), *z16 = malloc(nx * 2), *b16 = malloc(nb * 2),
+                 *c16 = malloc(nb * 2), *o16 = malloc(nx * 2);
+        double *x64 = malloc(nx * 8), *z64 = malloc(nx * 8), *b64 = malloc(nb * 8),
+               *c64 = malloc(nb * 8);
+        for (size_t i = 0; i < nx; ++i) {
+            x16[i] = bf16_bits(uniform(-1.5f, 1.5f));
+            x64[i] = bf16_value(x16[i]);
+            z16[i] = bf16_bits(uniform(-2.f, 2.f));
+            z64[i] = bf16_value(z16[i]);
+        }
+        for (size_t i = 0; i < nb; ++i) {
+            b16[i] = bf16_bits(uniform(-1.5f, 1.5f));
+            b64[i] = bf16_value(b16[i]);
+            c16[i] = bf16_bits(uniform(-1.5f, 1.5f));
+            c64[i] = bf16_value(c16[i]);
+        }
+        float dt[TOK * SH], a2[SH], d2[SH], bias2[SH];
+        fill(dt, TOK * SH, -3.f, 0.f);
+        for (int h = 0; h < SH; ++h) {
+            a2[h] = -expf(uniform(0.f, 2.f));
+            d2[h] = uniform(-1.f, 1.f);
+            bias2[h] = uniform(-1.f, 1.f);
+        }
+        float* init = malloc(ns * sizeof(float));
+        fill(init, ns, -1.f, 1.f);
+
+        void *dx = to_device(x16, nx * 2), *dz = to_device(z16, nx * 2), *dB = to_device(b16, nb * 2),
+             *dC = to_device(c16, nb * 2), *ddt = to_device(dt, sizeof dt),
+             *dA2 = to_device(a2, sizeof a2), *dD2 = to_device(d2, sizeof d2),
+             *dbias2 = to_device(bias2, sizeof bias2), *dinit = to_device(init, ns * sizeof(float)),
+             *dcu = to_device(cu, sizeof cu), *dsidx = to_device(sidx, sizeof sidx),
+             *dlast = to_device(last, sizeof last);
+        void *dout = NULL, *dstates = NULL, *dwork = NULL;
+        CHECK_HIP(hipMalloc(&dout, nx * 2));
+        CHECK_HIP(hipMalloc(&dstates, ns * sizeof(float)));
+        const size_t wbytes = ssu_ssd_workspace_bytes(NCH, NB, SH, SP, SN, SG, Q);
+        CHECK_HIP(hipMalloc(&dwork, wbytes));
+
+        ssu_ssd_args a;
+        memset(&a, 0, sizeof a);
+        a.struct_size = sizeof a;
+        a.tokens = TOK;
+        a.nheads = SH;
+        a.headdim = SP;
+        a.dstate = SN;
+        a.ngroups = SG;
+        a.chunk_size = Q;
+        a.nchunks = NCH;
+        a.batch = NB;
+        a.x = dx;
+        a.dt = ddt;
+        a.A = dA2;
+        a.B = dB;
+        a.C = dC;
+        a.D = dD2;
+        a.z = dz;
+        a.dt_bias = dbias2;
+        a.io_dtype = SSU_BF16;
+        a.dt_dtype = SSU_F32;
+        a.dt_softplus = 1;
+        a.dt_min = 0.0;
+        a.dt_max = INFINITY;
+        a.cu_chunk_seqlens = dcu;
+        a.seq_idx = dsidx;
+        a.last_chunk_indices = dlast;
+        a.meta_dtype = SSU_I32;
+        a.state_dtype = SSU_F32;
+        a.initial_states = dinit;
+        a.out = dout;
+        a.states = dstates;
+        a.workspace = dwork;
+        a.workspace_bytes = wbytes;
+        if (ssu_ssd_prefill(&a, stream) != SSU_OK) {
+            fprintf(stderr, "ssu_ssd_prefill: %s\n", ssu_last_error());
+            return 2;
+        }
+        CHECK_HIP(hipStreamSynchronize(stream));
+        float* states_gpu = malloc(ns * sizeof(float));
+        CHECK_HIP(hipMemcpy(o16, dout, nx * 2, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(states_gpu, dstates, ns * sizeof(float), hipMemcpyDeviceToHost));
+
+        int64_t cu64[NCH + 1], sidx64[NCH], last64[NB];
+        for (int c = 0; c <= NCH; ++c) cu64[c] = cu[c];
+        for (int c = 0; c < NCH; ++c) sidx64[c] = sidx[c];
+        for (int b = 0; b < NB; ++b) last64[b] = last[b];
+        double *dt64 = widen(dt, TOK * SH), *a64 = widen(a2, SH), *d64 = widen(d2, SH),
+               *bias64b = widen(bias2, SH), *init64 = widen(init, ns);
+        double* out_ref = malloc(nx * 8);
+        double* chunk_ref = malloc((size_t)NCH * SH * SP * SN * 8);
+        double* final_ref = malloc(ns * 8);
+        if (oracle_ssd_prefill(TOK, SH, SP, SN, SG, x64, dt64, a64, b64, c64, d64, 0, z64, bias64b,
+                               1, 0.0, INFINITY, Q, NCH, cu64, sidx64, NB, last64, init64, out_ref,
+                               chunk_ref, final_ref) != 0) {
+            fprintf(stderr, "oracle_ssd_prefill refused its arguments\n");
+            return 2;
+        }
+        long bad_out = 0;
+        double worst_out = 0.0;
+        for (size_t i = 0; i < nx; ++i) {
+            const double err = fabs((double)bf16_value(o16[i]) - out_ref[i]);
+            const double bar = 1e-2 + 2e-2 * fabs(out_ref[i]);
+            if (!(err <= bar)) ++bad_out;
+            if (err / bar > worst_out) worst_out = err / bar;
+        }
+        double scale = 1.0, worst_st = 0.0;
+        for (size_t i = 0; i < ns; ++i) scale = fmax(scale, fabs(final_ref[i]));
+        for (size_t i = 0; i < ns; ++i) worst_st = fmax(worst_st, fabs(states_gpu[i] - final_ref[i]));
+        const int ok = bad_out == 0 && worst_st <= 1e-5 * scale;
+        printf("ssd prefill: out worst err/bar %.3f (%ld outside), final states max err %.2e "
+               "(bar %.2e): %s\n", worst_out, bad_out, worst_st, 1e-5 * scale,
+               ok ? "matches the oracle" : "MISMATCH");
+        failures += !ok;
+        void* bufs[] = {dx, dz, dB, dC, ddt, dA2, dD2, dbias2, dinit, dcu, dsidx, dlast,
+                        dout, dstates, dwork};
+        for (size_t i = 0; i < sizeof bufs / sizeof bufs[0]; ++i) CHECK_HIP(hipFree(bufs[i]));
+        free(x16); free(z16); free(b16); free(c16); free(o16); free(x64); free(z64); free(b64);
+        free(c64); free(init); free(states_gpu); free(dt64); free(a64); free(d64); free(bias64b);
+        free(init64); free(out_ref); free(chunk_ref); free(final_ref);
     }
 
     CHECK_HIP(hipStreamDestroy(stream));
