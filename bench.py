@@ -346,8 +346,8 @@ def cpu_model():
 
 def cpu_threads():
     """Host threads for the CPU leg: every CPU this process may run on, capped by
-    OMP_NUM_THREADS when the environment sets it (a GPU machine grants each GPU's
-    jobs a share of its host, and says so there)."""
+    OMP_NUM_THREADS when the environment sets it (a host shared by several GPUs
+    may grant each GPU's jobs a share of its CPUs, and say so there)."""
     try:
         n = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
