@@ -99,7 +99,7 @@ typedef enum ssu_index_dtype {
 typedef enum ssu_status {
     SSU_OK = 0,
     SSU_ERR_INVALID_ARGUMENT = 1, /* inconsistent sizes, null required pointer, ... */
-    SSU_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+    SSU_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement */
     SSU_ERR_LAUNCH = 3            /* the HIP runtime refused the launch */
 } ssu_status;
 
