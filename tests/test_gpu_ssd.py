@@ -241,6 +241,45 @@ def test_explicit_stream():
     assert side.cuda_stream in keys
 
 
+def test_two_threads_on_two_streams():
+    """Two host threads, each with a stream of its own, repeat prefills of
+    different shapes at once: every result equals the single-threaded one bit
+    for bit (each stream gets its own cached workspace)."""
+    import threading
+    import selective_state_update_ssu_amd as ssu
+    ws = [_make("bf16_f32_ragged"), _make("ids_out_of_order")]
+    refs = []
+    for w in ws:
+        out = torch.empty_like(w.x)
+        refs.append((out, ssu.ssd_combined_fwd_varlen(*w.args(), out=out, **w.kwargs())))
+    torch.cuda.synchronize()
+    results = [[], []]
+    errors = []
+
+    def worker(i):
+        try:
+            side = torch.cuda.Stream()
+            with torch.cuda.stream(side):
+                for _ in range(6):
+                    out = torch.empty_like(ws[i].x)
+                    st = ssu.ssd_combined_fwd_varlen(*ws[i].args(), out=out, **ws[i].kwargs())
+                    results[i].append((out, st))
+            side.synchronize()
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(2):
+        assert len(results[i]) == 6
+        for out, st in results[i]:
+            assert torch.equal(out, refs[i][0]) and torch.equal(st, refs[i][1]), i
+
+
 @pytest.mark.parametrize("io", ["bf16", "f16"])
 def test_every_compiled_instance(io):
     """Every compiled prefill instance of this io type -- state dtype x dstate
