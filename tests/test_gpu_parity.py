@@ -125,6 +125,10 @@ def _small_cases():
             cases.append(dict(state_dtype=st, io="bf16", N=N, P=64, H=4, G=1))
     for P in (80, 40, 128, 1):
         cases.append(dict(state_dtype="f32", io="bf16", N=64, P=P, H=4, G=2))
+    # headdim 256 (several row blocks per head at every geometry); one head
+    cases.append(dict(state_dtype="bf16", io="bf16", N=128, P=256, H=2, G=1))
+    cases.append(dict(state_dtype="f16", io="f16", N=16, P=256, H=2, G=2))
+    cases.append(dict(state_dtype="f32", io="bf16", N=128, P=64, H=1, G=1))
     cases.append(dict(state_dtype="f16", io="f16", N=16, P=72, H=6, G=3))
     # launch shapes, optional operands and index dtypes
     cases.append(dict(state_dtype="f32", io="bf16", N=128, P=64, H=8, G=1, hpb=4))
@@ -176,6 +180,8 @@ def test_one_token_small(case):
     dict(state_dtype="f32", io="bf16", N=128, P=64, H=4, G=1, accepted=False),
     dict(state_dtype="f32", io="bf16", N=64, P=64, H=4, G=1, with_z=False, dt_per_dim=True),
     dict(state_dtype="f32", io="bf16", N=128, P=64, H=4, G=1, disable=True),
+    dict(state_dtype="bf16", io="bf16", N=64, P=256, H=2, G=1),
+    dict(state_dtype="f32", io="f32", N=32, P=64, H=1, G=1),
 ], ids=_case_id)
 def test_packed_small(case):
     c = dict(case)
